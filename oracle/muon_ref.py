@@ -1,0 +1,156 @@
+"""CPU oracle for the shape-fused Muon optimizer step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product package
+(``muon_newton_schulz_05_amd``) imports, links or calls this module; only the
+tests, the smoke check and the CPU-baseline leg of the benchmark do.  It shares
+no code with the HIP path: it reads plain numpy arrays and computes every step
+in float64 with plain numpy operations, one matrix at a time, in the order the
+method states.  It is slow on purpose: a reader should be able to check it
+against the sources by eye.
+
+Sources (cited by page title and section):
+
+* [Notes] "关于分布式Muon的想法整合及讨论" (notes on distributed Muon):
+  - §1 Introduction: Muon acts on 2-D weight matrices; per matrix it keeps a
+    momentum of the gradient, orthogonalises that momentum approximately and
+    uses the result as the update direction.
+  - §2 Muon执行过程 (how a Muon step runs): the first formula normalises the
+    momentum, which needs the whole matrix; the rest of the step is a Gram
+    matrix and a chain of matrix products.  (The formulas themselves did not
+    survive extraction.)
+  - §6 与TP的结合 (combining with tensor parallelism): when the matrix is split,
+    the normalisation only needs the parts' sums of squares added up, i.e. the
+    normaliser is the Frobenius norm; and the Gram matrix changes every
+    Newton-Schulz round because X does.
+* [Blog] "MindSpore HyperParallel X 盘古,Muon优化器实现6倍性能跃升":
+  - 三大性能挑战 (three challenges), third item: the orthogonalisation is a
+    Newton-Schulz iteration of typically 5 to 10 rounds of matrix products and
+    additions.
+  - FSDP域分布式Muon更新原方案 (original FSDP scheme, Fig. 1): the momentum M_t
+    is orthogonalised into O_t, which then updates the parameter.
+  - Muon亲和的专家切分 (expert split, Fig. 4): for a 3-D expert tensor
+    [E, M, N] only the last two dimensions take part; the E slices are
+    mathematically independent.
+
+Readings taken where the pages are silent (each is also listed in the design doc):
+
+* Newton-Schulz round: ``A = X X^T``, ``B = b A + c A^2``, ``X <- a X + B X``
+  with (a, b, c) given by the caller; the standard quintic Muon form.
+* Orientation: if a slice has more rows than columns it is transposed before
+  the iteration and transposed back after (strictly more: square slices are
+  not transposed).  In exact arithmetic this changes nothing (the iteration
+  commutes with transposition); it only fixes which Gram matrix is formed.
+* Momentum: heavy-ball ``M <- beta M + G``, stored rounded to float32.
+* Normaliser: ``X / (||X||_F + eps)``, eps = 1e-7 by default.
+* Update: ``W <- W - lr O``; no shape-dependent factor, no weight decay.
+* Scalars (lr, beta, a, b, c) are float32 values; they enter the float64
+  arithmetic as the float32-rounded numbers.
+
+Array conventions: a float32 array is float32 data; a uint16 array holds
+bfloat16 bit patterns (the upper half of an IEEE binary32 word).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+DEFAULT_EPS = 1e-7
+
+
+def decode(x: np.ndarray) -> np.ndarray:
+    """Return ``x`` as float64.
+
+    float32/float64 convert exactly.  uint16 is read as bfloat16 bit patterns:
+    bfloat16 is binary32 with the low 16 mantissa bits dropped, so placing the
+    pattern in the upper half of a 32-bit word gives the exact value.
+    """
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if x.dtype in (np.float32, np.float64):
+        return x.astype(np.float64)
+    raise TypeError(f"unsupported dtype {x.dtype}")
+
+
+def f32(v: float) -> float:
+    """The float32-rounded value of a scalar, as a Python float."""
+    return float(np.float32(v))
+
+
+def momentum_update(m: np.ndarray, g: np.ndarray, beta: float) -> np.ndarray:
+    """Heavy-ball momentum of the gradient, [Notes] §1; stored as float32.
+
+    The product beta*M of two float32 numbers is exact in float64, so the only
+    roundings are the float64 add and the final float32 store.
+    """
+    return (f32(beta) * decode(m) + decode(g)).astype(np.float32)
+
+
+def orient(x: np.ndarray) -> tuple[np.ndarray, bool]:
+    """Transpose a slice with more rows than columns; return (X, transposed)."""
+    rows, cols = x.shape
+    if rows > cols:
+        return x.T, True
+    return x, False
+
+
+def frobenius_normalize(x: np.ndarray, eps: float = DEFAULT_EPS) -> np.ndarray:
+    """X / (||X||_F + eps): the whole-matrix normalisation of [Notes] §2, whose
+    split form in §6 adds up per-part sums of squares."""
+    return x / (np.sqrt(np.sum(x * x)) + eps)
+
+
+def newton_schulz(x: np.ndarray, steps: int, a: float, b: float, c: float) -> np.ndarray:
+    """``steps`` rounds of X <- a X + (b A + c A^2) X with the Gram matrix
+    A = X X^T recomputed every round ([Notes] §2 and §6; [Blog], three
+    challenges, third item)."""
+    a, b, c = f32(a), f32(b), f32(c)
+    for _ in range(steps):
+        gram = x @ x.T
+        poly = b * gram + c * (gram @ gram)
+        x = a * x + poly @ x
+    return x
+
+
+def orthogonalize(m: np.ndarray, steps: int, a: float, b: float, c: float,
+                  eps: float = DEFAULT_EPS) -> np.ndarray:
+    """O for one 2-D momentum slice: orient, normalise, iterate, un-orient."""
+    x, transposed = orient(decode(m))
+    x = frobenius_normalize(x, eps)
+    x = newton_schulz(x, steps, a, b, c)
+    return x.T if transposed else x
+
+
+def _slices(shape: tuple[int, ...]):
+    """Index tuples of the independent 2-D slices of a 2-D or 3-D tensor
+    ([Blog], expert split: only the last two dimensions take part)."""
+    if len(shape) == 2:
+        yield (Ellipsis,)
+    elif len(shape) == 3:
+        for e in range(shape[0]):
+            yield (e, Ellipsis)
+    else:
+        raise ValueError(f"Muon acts on 2-D matrices or 3-D stacks of them, got shape {shape}")
+
+
+def muon_step(params, grads, momenta, *, lr: float, beta: float, ns_steps: int,
+              a: float, b: float, c: float, eps: float = DEFAULT_EPS):
+    """One Muon step over a list of parameters.
+
+    Each parameter is 2-D [R, C] or 3-D [E, R, C]; every 2-D slice is handled
+    on its own.  Returns ``(new_params, new_momenta, updates)``: new parameters
+    as float64 arrays (not rounded to the parameter's storage type), new
+    momenta as float32 arrays and the orthogonalised directions O as float64.
+    """
+    new_params, new_momenta, updates = [], [], []
+    lr = f32(lr)
+    for w, g, m in zip(params, grads, momenta):
+        w64 = decode(w)
+        m_new = momentum_update(m, g, beta)
+        o = np.zeros(m_new.shape, dtype=np.float64)
+        for sl in _slices(m_new.shape):
+            o[sl] = orthogonalize(m_new[sl], ns_steps, a, b, c, eps)
+        new_params.append(w64 - lr * o)
+        new_momenta.append(m_new)
+        updates.append(o)
+    return new_params, new_momenta, updates
