@@ -1,0 +1,233 @@
+"""Benchmark of the fused Muon step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode bf16|fp32]
+
+Prints ONE JSON line.  A step is one full Muon update of every parameter of
+the workload (momentum, normalisation, k Newton-Schulz rounds, weight update)
+with inputs already resident in HBM.  ``value`` is matrices (2-D slices) per
+second; the line also carries the effective TFLOP/s, the roofline of the
+dominant kernel (timed with HIP events on the launch stream) and the CPU
+oracle's throughput on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
+DEFAULT_WORKLOAD = "fused_74x24x10240"
+
+
+def elem_bytes(dt: str) -> int:
+    return 2 if dt == "bf16" else 4
+
+
+def compulsory_bytes(wl: workloads.Workload) -> float:
+    """Bytes a step must move: read G, read+write M (f32), read+write W."""
+    tot = 0.0
+    for p in wl.params:
+        e = 1
+        for d in p.shape:
+            e *= d
+        tot += e * (elem_bytes(p.grad_dtype) + 8 + 2 * elem_bytes(p.param_dtype))
+    return tot
+
+
+def make_gpu_inputs(wl: workloads.Workload, dev):
+    """Seeded synthetic inputs generated on the device (same recipe as the
+    host generator: Gaussian gradients of the workload's std, stored in the
+    workload's types; momentum from a prior step; weights N(0, 0.02^2))."""
+    import torch
+    gen = torch.Generator(device=dev)
+    params, grads, moms = [], [], []
+    for i, p in enumerate(wl.params):
+        gen.manual_seed(workloads.seed(wl, i))
+        g = torch.randn(p.shape, generator=gen, device=dev, dtype=torch.float32) * wl.grad_std
+        grads.append(g.to(torch.bfloat16) if p.grad_dtype == "bf16" else g)
+        m = torch.randn(p.shape, generator=gen, device=dev, dtype=torch.float32) * wl.grad_std
+        moms.append(m)
+        w = torch.randn(p.shape, generator=gen, device=dev, dtype=torch.float32) * 0.02
+        params.append(w.to(torch.bfloat16) if p.param_dtype == "bf16" else w)
+    return params, grads, moms
+
+
+def cpu_baseline(wl: workloads.Workload, budget_s: float):
+    """The oracle, as it stands, timed on the host on a bounded sample of the
+    workload: whole parameters in workload order until the budget is spent."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    mats = 0
+    t_total = 0.0
+    sampled = []
+    idx = 0
+    reps = 0
+    while t_total < budget_s:
+        i = idx % len(wl.params)
+        spec = wl.params[i]
+        g = workloads.gradient(wl, i)
+        w = np.zeros(spec.shape, np.float32)
+        m = np.zeros(spec.shape, np.float32)
+        t0 = time.perf_counter()
+        oracle.muon_step([w], [g], [m], lr=wl.lr, beta=wl.beta, ns_steps=wl.ns_steps,
+                         a=wl.coeffs[0], b=wl.coeffs[1], c=wl.coeffs[2])
+        t_total += time.perf_counter() - t0
+        mats += spec.shape[0] if len(spec.shape) == 3 else 1
+        sampled.append(i)
+        idx += 1
+        if idx % len(wl.params) == 0:
+            reps += 1
+    desc = (f"{reps} full pass(es) + {idx % len(wl.params)} of {len(wl.params)} parameters"
+            if reps else f"first {idx} of {len(wl.params)} parameters")
+    return {"value": mats / t_total, "unit": "matrices/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{desc} ({mats} matrices, {t_total:.1f} s, float64 numpy)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(workloads.WORKLOADS))
+    ap.add_argument("--mode", default=None, choices=["bf16", "fp32"])
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--graph", action="store_true", help="replay streamed launches from a HIP graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    from muon_newton_schulz_05_amd import MuonPlan
+
+    wl = workloads.WORKLOADS[args.workload]
+    mode = args.mode or wl.mode
+    big = wl.flops() > 1e13
+    steps = args.steps if args.steps is not None else (10 if big else 200)
+    warmup = args.warmup if args.warmup is not None else (2 if big else 10)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    params, grads, moms = make_gpu_inputs(wl, dev)
+    torch.cuda.synchronize()
+    plan = MuonPlan(params, grad_dtypes=[g.dtype for g in grads], mode=mode, use_graph=args.graph)
+    info = plan.info()
+    stream = torch.cuda.current_stream(dev)
+    kw = dict(lr=wl.lr, beta=wl.beta, ns_steps=wl.ns_steps, coeffs=wl.coeffs)
+
+    for _ in range(warmup):
+        plan.step(grads, moms, **kw)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        plan.step(grads, moms, **kw)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    status = plan.status()
+    plan.close()
+
+    # Per-kernel timing: the same steps again on a plan that brackets every
+    # launch with HIP events on the launch stream.
+    tplan = MuonPlan(params, grad_dtypes=[g.dtype for g in grads], mode=mode, timing=True)
+    tsteps = max(1, min(steps, 20))
+    for _ in range(tsteps):
+        tplan.step(grads, moms, **kw)
+    torch.cuda.synchronize()
+    tplan.timings()  # discard the first pass (warm caches)
+    for _ in range(tsteps):
+        tplan.step(grads, moms, **kw)
+    tim = tplan.timings()
+    tplan.close()
+
+    n_mat = wl.n_matrices
+    flops = wl.flops() if mode else 0.0
+    kernel_ms = {k: (v[0] / tsteps, v[1] // tsteps) for k, v in tim.items() if v[1]}
+    dominant = max(kernel_ms, key=lambda k: kernel_ms[k][0])
+    dom_ms_per_launch = kernel_ms[dominant][0] / max(1, kernel_ms[dominant][1])
+
+    if dominant == "resident":
+        # Compulsory bytes of the resident buckets; X never leaves the chip.
+        res_bytes = 0.0
+        for p in wl.params:
+            r, c = p.shape[-2:]
+            if min(r, c) <= 32:
+                e = 1
+                for d in p.shape:
+                    e *= d
+                res_bytes += e * (elem_bytes(p.grad_dtype) + 8 + 2 * elem_bytes(p.param_dtype))
+        per_launch = res_bytes / max(1, kernel_ms[dominant][1])
+        achieved = per_launch / (dom_ms_per_launch * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "k_resident", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "algorithmic_bytes_per_launch": per_launch,
+                "avg_launch_ms": round(dom_ms_per_launch, 5)}
+    else:
+        # Flops of the dominant matrix-core kernel class per launch.
+        per = {"gram": lambda m, n: 2.0 * m * m * n, "poly": lambda m, n: 2.0 * m ** 3,
+               "apply": lambda m, n: 2.0 * m * m * n}.get(dominant)
+        fl = 0.0
+        if per:
+            for m, n in wl.oriented_matrices():
+                if m > 32:
+                    fl += wl.ns_steps * per(m, n)
+        per_launch = fl / max(1, kernel_ms[dominant][1])
+        achieved = per_launch / (dom_ms_per_launch * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[mode]
+        roof = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "algorithmic_flops_per_launch": per_launch, "avg_launch_ms": round(dom_ms_per_launch, 5)}
+
+    out = {
+        "metric": "Muon step matrices/s + effective TFLOP/s (frac of MFMA/HBM roofline), 1 GPU",
+        "value": round(n_mat * steps / (ms * steps * 1e-3), 3),
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "wall_ms_per_step": round(wall * 1e3 / steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if mode == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "matrices": n_mat, "ns_steps": wl.ns_steps, "mode": mode,
+                   "shapes": sorted({tuple(p.shape) for p in wl.params}), "graph": bool(args.graph)},
+        "effective_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+        "effective_tflops_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[mode], 4),
+        "compulsory_gbs": round(compulsory_bytes(wl) / (ms * 1e-3) / 1e9, 1),
+        "roofline": roof,
+        "kernels_ms_per_step": {k: round(v[0], 5) for k, v in kernel_ms.items()},
+        "launches_per_step": info["launches_fixed"] + info["launches_per_ns"] * wl.ns_steps,
+        "device_error": status,
+    }
+    if args.cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 3)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * muon.h -- C ABI of the shape-fused Muon optimizer step for AMD MI355X (gfx950).
+ *
+ * One Muon step, per 2-D weight slice W of shape [R, C]:
+ *   1. M <- beta * M + G                       (momentum of the gradient)
+ *   2. X <- M, transposed when R > C            (so X is [m, n], m = min(R, C))
+ *   3. X <- X / (||X||_F + eps)                 (whole-matrix Frobenius normalisation)
+ *   4. k times: A = X X^T;  X <- a X + (b A + c A^2) X      (Newton-Schulz)
+ *   5. O <- X, transposed back when R > C
+ *   6. W <- W - lr * O
+ *
+ * Sources, by page and section:
+ *  - "关于分布式Muon的想法整合及讨论" (notes on distributed Muon), §1 Introduction:
+ *    Muon keeps a momentum of the gradient, orthogonalises it approximately
+ *    and steps along the result; it acts on 2-D matrices.  §2 (how a Muon
+ *    step runs): the momentum is first normalised, which needs the whole
+ *    matrix; the rest is a Gram matrix and a chain of matrix products.  §6
+ *    (combining with tensor parallelism): the normaliser is a sum of squares
+ *    over all parts, and the Gram matrix is recomputed every round.
+ *  - "MindSpore HyperParallel X 盘古,Muon优化器实现6倍性能跃升", section
+ *    三大性能挑战 (three challenges): the iteration takes 5 to 10 rounds of
+ *    matrix products and additions, and small matrices make a per-matrix
+ *    launch stream host-bound; section 专家切分 (expert split): a 3-D
+ *    [E, M, N] tensor is E independent slices; section 矩阵融合优化 (matrix
+ *    fusion, Fig. 6-7): parameters whose last two dimensions agree are run as
+ *    one batched problem, which is what a plan does here.
+ *  The Newton-Schulz form in step 4 and the transpose rule in step 2 are not
+ *  printed on the pages; they are the standard quintic Muon iteration, with
+ *  (a, b, c) supplied by the caller.
+ *
+ * Memory and ownership
+ *  - params, grads and momentum are DEVICE pointers owned by the caller, on the
+ *    device the plan was created on; each is a contiguous row-major tensor of
+ *    the shape given at plan creation, 16-byte aligned.  params and momentum
+ *    are updated in place, grads is only read.  Momentum is always float32.
+ *  - The arrays of pointers passed to muon_step are HOST arrays of n_params
+ *    entries, read during the call only.
+ *  - A plan owns its device workspace (allocated once in muon_plan_create,
+ *    never during muon_step), its device tables and, if enabled, its graph.
+ *  - A plan is bound to the device that was current when it was created and
+ *    is not thread-safe: one muon_step on a plan at a time.  Different plans
+ *    are independent.
+ *
+ * Errors
+ *  - Every function returns a muon_status_t; muon_last_error() gives a
+ *    message for the last failure on the calling thread.  No C++ exception
+ *    crosses this interface.
+ *  - Shape and dtype problems are reported by muon_plan_create/describe.
+ *    muon_step checks its pointers and scalars before it enqueues anything;
+ *    on error nothing is enqueued and no memory is modified.
+ *  - muon_step is asynchronous on `stream`: device faults surface at the
+ *    caller's next synchronisation.  muon_plan_status() reports the plan's
+ *    device-side error word (it synchronises).
+ */
+#ifndef MUON_H
+#define MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad shape, non-finite scalar ... */
+  MUON_ERR_UNSUPPORTED = 2,      /* valid request this build does not support            */
+  MUON_ERR_HIP = 3,              /* a HIP runtime call failed                             */
+  MUON_ERR_OOM = 4,              /* workspace allocation failed or exceeds workspace_limit */
+  MUON_ERR_DEVICE_MISMATCH = 5,  /* current device differs from the plan's device         */
+  MUON_ERR_DEVICE = 6            /* the device reported an error (muon_plan_status)        */
+} muon_status_t;
+
+typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype_t;
+
+/* Arithmetic of the Newton-Schulz iteration.
+ *  MUON_MODE_FP32:      float32 storage and float32 products (matrix cores in fp32).
+ *  MUON_MODE_BF16_MFMA: bfloat16 operands on the matrix cores with float32
+ *                       accumulation; Gram matrices and polynomial in float32. */
+typedef enum { MUON_MODE_FP32 = 0, MUON_MODE_BF16_MFMA = 1 } muon_mode_t;
+
+/* Descriptor of one parameter.  ndim 2: shape = [R, C];  ndim 3: shape = [E, R, C]
+ * holding E independent slices.  Momentum is always float32. */
+typedef struct {
+  int32_t ndim;
+  int32_t param_dtype; /* muon_dtype_t of W */
+  int32_t grad_dtype;  /* muon_dtype_t of G */
+  int32_t reserved;
+  int64_t shape[3];
+} muon_param_desc_t;
+
+typedef struct {
+  int32_t mode;            /* muon_mode_t; default MUON_MODE_BF16_MFMA                        */
+  int32_t use_graph;       /* 1: capture the step's launches in a HIP graph and replay it     */
+  float eps;               /* normaliser offset, default 1e-7                                 */
+  int32_t max_ns_steps;    /* muon_step rejects ns_steps > this; default 16                   */
+  uint64_t workspace_limit;/* bytes; 0 = no limit.  Plans needing more fail with MUON_ERR_OOM */
+  int32_t resident_max_m;  /* slices with m <= this (<= 32) run the single-kernel resident
+                              path; 0 = default 32, -1 = never (every slice streams)          */
+  int32_t timing;          /* 1: time each kernel class with HIP events (muon_plan_timings)   */
+  int32_t n_cu;            /* compute units to plan for; 0 = the device's (describe: 256)     */
+  int32_t reserved[3];
+} muon_plan_opts_t;
+
+/* How a bucket of same-shape slices is executed. */
+typedef enum { MUON_PATH_RESIDENT = 0, MUON_PATH_STREAM = 1 } muon_path_t;
+
+#define MUON_MAX_BUCKETS 64
+
+typedef struct {
+  int64_t m, n;            /* oriented slice shape, m <= n                         */
+  int32_t count;           /* slices in the bucket                                 */
+  int32_t n_transposed;    /* of which stored as [n, m] (R > C)                    */
+  int32_t path;            /* muon_path_t                                          */
+  int32_t cluster;         /* resident: workgroups cooperating on one slice        */
+  int32_t groups;          /* resident: cooperative launches the bucket needs      */
+  int32_t reserved;
+  uint64_t workspace_bytes;/* this bucket's share of the workspace                 */
+} muon_bucket_info_t;
+
+typedef struct {
+  int32_t n_params;
+  int32_t n_matrices;      /* 2-D slices after expanding 3-D parameters            */
+  int32_t n_buckets;
+  int32_t mode;
+  uint64_t workspace_bytes;
+  int32_t launches_fixed;  /* launches per step independent of ns_steps           */
+  int32_t launches_per_ns; /* plus this many per Newton-Schulz round              */
+  muon_bucket_info_t buckets[MUON_MAX_BUCKETS];
+} muon_plan_info_t;
+
+typedef struct muon_plan* muon_plan_t;
+
+/* Fill *opts with the defaults listed above. */
+void muon_default_opts(muon_plan_opts_t* opts);
+
+/* Plan a step over n_params parameters (descs[0..n_params-1], in the order
+ * muon_step will receive their pointers).  Slices are oriented, grouped by
+ * oriented shape (m, n) and given a kernel path; the workspace is allocated
+ * once on the current device.  opts may be NULL (defaults).
+ * Errors: INVALID_ARGUMENT (null pointers, n_params <= 0, ndim not 2 or 3, a
+ * dimension <= 0 or >= 2^31, unknown dtype or mode, bad eps/max_ns_steps),
+ * UNSUPPORTED (more than MUON_MAX_BUCKETS shapes), OOM, HIP. */
+int muon_plan_create(const muon_param_desc_t* descs, int32_t n_params,
+                     const muon_plan_opts_t* opts, muon_plan_t* out_plan);
+
+/* The same planning as muon_plan_create without touching any device: fills
+ * *info as the plan would report it (opts->n_cu, or 256 compute units). */
+int muon_plan_describe(const muon_param_desc_t* descs, int32_t n_params,
+                       const muon_plan_opts_t* opts, muon_plan_info_t* info);
+
+/* Report an existing plan's layout. */
+int muon_plan_query(muon_plan_t plan, muon_plan_info_t* info);
+
+/* Enqueue one Muon step on `stream` (a hipStream_t; NULL = the null stream).
+ * params/grads/momentum: host arrays of n_params device pointers (see above).
+ * ns_steps in [0, max_ns_steps]; lr, beta, a, b, c finite.  ns_steps = 0 steps
+ * along the normalised momentum.  Does not synchronise the host. */
+int muon_step(muon_plan_t plan, void* const* params, const void* const* grads,
+              void* const* momentum, float lr, float beta, int32_t ns_steps,
+              float a, float b, float c, void* stream);
+
+/* Synchronise the plan's device and read its device-side error word
+ * (nonzero: a cooperative wait in the resident kernel gave up).  Clears it.
+ * Returns MUON_ERR_DEVICE when the word was nonzero. */
+int muon_plan_status(muon_plan_t plan, uint32_t* device_error);
+
+/* Kernel-class timings collected since the last call (opts.timing = 1):
+ * out_ms[i] = total milliseconds, out_count[i] = launches, for i < n_out and
+ * the classes 0 resident, 1 momentum, 2 norm, 3 gram, 4 poly, 5 apply,
+ * 6 update.  Synchronises.  Returns the number of classes. */
+int muon_plan_timings(muon_plan_t plan, double* out_ms, int64_t* out_count, int32_t n_out);
+
+/* Release the plan and its device memory.  NULL is a no-op. */
+int muon_plan_destroy(muon_plan_t plan);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* muon_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MUON_H */

@@ -1,0 +1,486 @@
+// api.cpp -- the C ABI (include/muon.h): plan lifecycle and the launch sequence.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "kernels.h"
+#include "planner.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MUON_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr uint32_t kPlanMagic = 0x4d554f4eu;  // "MUON"
+// Polls of a resident-kernel wait before it gives up (about 0.2 s).
+constexpr uint32_t kSpinLimit = 4u << 20;
+
+struct TimedLaunch {
+  int cls;
+  hipEvent_t start, stop;
+};
+
+}  // namespace
+
+struct muon_plan {
+  uint32_t magic = kPlanMagic;
+  muon::Plan p;
+  int device = 0;
+  char* ws = nullptr;
+  std::vector<muon::PtrEntry> ptrs;  // last table uploaded
+  bool ptrs_valid = false;
+  muon::PtrEntry* pinned = nullptr;  // staging for the upload
+  hipEvent_t upload_done = nullptr;
+  bool upload_pending = false;
+  // graph of the streamed launches, keyed by ns_steps and stream
+  hipGraphExec_t gexec = nullptr;
+  int graph_ns = -1;
+  hipStream_t graph_stream = nullptr;
+  // timing
+  std::vector<TimedLaunch> timed;
+  std::vector<hipEvent_t> event_pool;
+  double acc_ms[muon::kNumClasses] = {};
+  int64_t acc_cnt[muon::kNumClasses] = {};
+};
+
+namespace {
+
+bool plan_ok(muon_plan_t plan) { return plan != nullptr && plan->magic == kPlanMagic; }
+
+template <typename T>
+T* at(muon_plan_t plan, uint64_t off) {
+  return reinterpret_cast<T*>(plan->ws + off);
+}
+
+hipEvent_t take_event(muon_plan_t plan) {
+  if (!plan->event_pool.empty()) {
+    hipEvent_t e = plan->event_pool.back();
+    plan->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Run one launch, bracketed by events when timing is on.
+template <class F>
+hipError_t timed(muon_plan_t plan, int cls, hipStream_t s, bool timing, F&& launch) {
+  if (!timing) return launch();
+  hipEvent_t a = take_event(plan), b = take_event(plan);
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipEventRecord(a, s);
+  hipError_t e = launch();
+  hipEventRecord(b, s);
+  plan->timed.push_back({cls, a, b});
+  return e;
+}
+
+hipError_t enqueue_resident(muon_plan_t plan, const muon::BucketPlan& bp, int ns, hipStream_t s,
+                            bool timing) {
+  const muon::Plan& p = plan->p;
+  for (int g = 0; g < bp.groups; ++g) {
+    muon::ResidentLaunch L;
+    L.mats = at<muon::DevMat>(plan, bp.off_mats);
+    L.ptrs = at<muon::PtrEntry>(plan, p.off_ptrs);
+    L.sc = at<muon::DevScalars>(plan, p.off_scalars);
+    L.gram_parts = at<float>(plan, bp.off_gram);
+    L.sq_parts = at<double>(plan, bp.off_sqp);
+    L.ctrs = at<uint32_t>(plan, bp.off_ctr);
+    L.err = at<uint32_t>(plan, p.off_err);
+    L.m = (int)bp.m;
+    L.n = (int)bp.n;
+    L.cluster = bp.cluster;
+    L.tiles_per_wg = bp.tiles_per_wg;
+    L.tpw = bp.tpw;
+    L.count = (int)bp.slices.size();
+    L.mat_base = g * bp.mats_per_group;
+    const int left = (int)bp.slices.size() - L.mat_base;
+    L.n_mats = left < bp.mats_per_group ? left : bp.mats_per_group;
+    L.ns_steps = ns;
+    L.spin_limit = kSpinLimit;
+    L.bf16 = p.mode == MUON_MODE_BF16_MFMA;
+    hipError_t e = timed(plan, muon::kClsResident, s, timing, [&] { return muon::launch_resident(L, s); });
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, hipStream_t s,
+                          bool timing) {
+  const muon::Plan& p = plan->p;
+  const int cnt = (int)bp.slices.size();
+  const muon::DevMat* mats = at<muon::DevMat>(plan, bp.off_mats);
+  const muon::PtrEntry* ptrs = at<muon::PtrEntry>(plan, p.off_ptrs);
+  const muon::DevScalars* sc = at<muon::DevScalars>(plan, p.off_scalars);
+  float* scale = at<float>(plan, bp.off_scale);
+  hipError_t e;
+
+  muon::MomentumLaunch mo{mats, ptrs, sc, plan->ws + bp.off_x[0], plan->ws + bp.off_xt[0],
+                          at<float>(plan, bp.off_sq), bp.m, bp.n, bp.mp, bp.np, cnt, bp.km_tiles,
+                          bp.x_bytes};
+  if ((e = timed(plan, muon::kClsMomentum, s, timing, [&] { return muon::launch_momentum(mo, s); })) != hipSuccess)
+    return e;
+  muon::NormLaunch no{at<float>(plan, bp.off_sq), scale, sc, cnt, bp.km_tiles};
+  if ((e = timed(plan, muon::kClsNorm, s, timing, [&] { return muon::launch_norm(no, s); })) != hipSuccess)
+    return e;
+  if (ns == 0) {
+    muon::Update0Launch u{mats, ptrs, sc, scale, bp.m, bp.n, cnt};
+    return timed(plan, muon::kClsUpdate, s, timing, [&] { return muon::launch_update0(u, s); });
+  }
+  for (int it = 0; it < ns; ++it) {
+    const int src = it & 1, dst = src ^ 1;
+    const float* sfirst = it == 0 ? scale : nullptr;
+    muon::GramLaunch gl{plan->ws + bp.off_x[src], at<float>(plan, bp.off_a32),
+                        bp.off_a16 ? at<uint16_t>(plan, bp.off_a16) : nullptr, sfirst, bp.mp, bp.np,
+                        cnt, bp.x_bytes};
+    if ((e = timed(plan, muon::kClsGram, s, timing, [&] { return muon::launch_gram(gl, s); })) != hipSuccess)
+      return e;
+    muon::PolyLaunch pl;
+    pl.op = bp.poly_f32 ? (const void*)at<float>(plan, bp.off_a32) : (const void*)at<uint16_t>(plan, bp.off_a16);
+    pl.op_bytes = bp.poly_f32 ? 4 : 2;
+    pl.a32 = at<float>(plan, bp.off_a32);
+    pl.phi = plan->ws + bp.off_phi;
+    pl.plo = bp.p_hilo ? at<uint16_t>(plan, bp.off_plo) : nullptr;
+    pl.p_bytes = p.mode == MUON_MODE_FP32 ? 4 : 2;
+    pl.sc = sc;
+    pl.mp = bp.mp;
+    pl.count = cnt;
+    if ((e = timed(plan, muon::kClsPoly, s, timing, [&] { return muon::launch_poly(pl, s); })) != hipSuccess)
+      return e;
+    muon::ApplyLaunch al;
+    al.phi = plan->ws + bp.off_phi;
+    al.plo = bp.p_hilo ? (const void*)(plan->ws + bp.off_plo) : nullptr;
+    al.p_bytes = pl.p_bytes;
+    al.xt_old = plan->ws + bp.off_xt[src];
+    al.x_old = plan->ws + bp.off_x[src];
+    al.x_new = plan->ws + bp.off_x[dst];
+    al.xt_new = plan->ws + bp.off_xt[dst];
+    al.scale = sfirst;
+    al.sc = sc;
+    al.mp = bp.mp;
+    al.np = bp.np;
+    al.m = bp.m;
+    al.n = bp.n;
+    al.count = cnt;
+    al.x_bytes = bp.x_bytes;
+    al.final_round = it == ns - 1;
+    al.mats = mats;
+    al.ptrs = ptrs;
+    if ((e = timed(plan, muon::kClsApply, s, timing, [&] { return muon::launch_apply(al, s); })) != hipSuccess)
+      return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t enqueue_streamed_buckets(muon_plan_t plan, int ns, hipStream_t s, bool timing) {
+  for (const muon::BucketPlan& bp : plan->p.buckets) {
+    if (bp.path != MUON_PATH_STREAM) continue;
+    hipError_t e = enqueue_stream(plan, bp, ns, s, timing);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+bool has_streamed(const muon::Plan& p) {
+  for (const auto& b : p.buckets)
+    if (b.path == MUON_PATH_STREAM) return true;
+  return false;
+}
+
+void drop_graph(muon_plan_t plan) {
+  if (plan->gexec) hipGraphExecDestroy(plan->gexec);
+  plan->gexec = nullptr;
+  plan->graph_ns = -1;
+  plan->graph_stream = nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+void muon_default_opts(muon_plan_opts_t* opts) {
+  if (opts) muon::default_opts(opts);
+}
+
+const char* muon_last_error(void) { return g_last_error.c_str(); }
+
+int muon_plan_describe(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_opts_t* opts,
+                       muon_plan_info_t* info) {
+  if (info == nullptr) return fail(MUON_ERR_INVALID_ARGUMENT, "info is null");
+  const int n_cu = (opts && opts->n_cu > 0) ? opts->n_cu : 256;
+  muon::Plan p;
+  std::string err;
+  const int rc = muon::make_plan(descs, n_params, opts, n_cu, 1, &p, &err);
+  if (rc != MUON_OK) return fail(rc, "%s", err.c_str());
+  muon::fill_info(p, info);
+  g_last_error.clear();
+  return MUON_OK;
+}
+
+int muon_plan_create(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_opts_t* opts,
+                     muon_plan_t* out_plan) {
+  if (out_plan == nullptr) return fail(MUON_ERR_INVALID_ARGUMENT, "out_plan is null");
+  *out_plan = nullptr;
+  // Validate the request before touching the device.
+  {
+    muon::Plan probe;
+    std::string err;
+    const int rc = muon::make_plan(descs, n_params, opts, 256, 1, &probe, &err);
+    if (rc != MUON_OK && rc != MUON_ERR_OOM) return fail(rc, "%s", err.c_str());
+  }
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  if (opts && opts->n_cu > 0 && opts->n_cu < n_cu) n_cu = opts->n_cu;
+
+  muon_plan* plan = new (std::nothrow) muon_plan;
+  if (!plan) return fail(MUON_ERR_OOM, "host allocation failed");
+  plan->device = dev;
+  std::string err;
+  int rc = muon::make_plan(descs, n_params, opts, n_cu, 1, &plan->p, &err);
+  if (rc != MUON_OK) {
+    delete plan;
+    return fail(rc, "%s", err.c_str());
+  }
+  // Every resident variant in use must fit at least one workgroup per CU,
+  // which is what the cooperative launches were sized for.
+  for (const auto& bp : plan->p.buckets) {
+    if (bp.path != MUON_PATH_RESIDENT) continue;
+    if (muon::resident_occupancy(bp.tpw, plan->p.mode == MUON_MODE_BF16_MFMA) < 1) {
+      delete plan;
+      return fail(MUON_ERR_UNSUPPORTED, "resident kernel (%d tiles per wave) does not fit a CU", bp.tpw);
+    }
+  }
+  const muon::Plan& p = plan->p;
+  e = hipMalloc(&plan->ws, p.ws_total);
+  if (e != hipSuccess) {
+    hipGetLastError();
+    delete plan;
+    return fail(MUON_ERR_OOM, "workspace of %llu bytes: %s", (unsigned long long)p.ws_total,
+                hipGetErrorString(e));
+  }
+  // Zero once: padding of the streamed workspace must stay exactly zero.
+  e = hipMemset(plan->ws, 0, p.ws_total);
+  std::vector<muon::DevMat> table;
+  for (const auto& bp : p.buckets) {
+    if (e != hipSuccess) break;
+    table.clear();
+    for (int si : bp.slices) {
+      const muon::Slice& s = p.slices[si];
+      muon::DevMat d;
+      d.param = s.param;
+      d.transposed = s.transposed;
+      d.pdtype = s.pdtype;
+      d.gdtype = s.gdtype;
+      d.slice_off = s.slice_off;
+      table.push_back(d);
+    }
+    e = hipMemcpy(plan->ws + bp.off_mats, table.data(), sizeof(muon::DevMat) * table.size(),
+                  hipMemcpyHostToDevice);
+  }
+  if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&plan->pinned),
+                                         sizeof(muon::PtrEntry) * p.n_params, hipHostMallocDefault);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->upload_done, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    muon_plan_destroy(plan);
+    return hip_fail(e, "plan setup");
+  }
+  *out_plan = plan;
+  g_last_error.clear();
+  return MUON_OK;
+}
+
+int muon_plan_query(muon_plan_t plan, muon_plan_info_t* info) {
+  if (!plan_ok(plan)) return fail(MUON_ERR_INVALID_ARGUMENT, "invalid plan handle");
+  if (!info) return fail(MUON_ERR_INVALID_ARGUMENT, "info is null");
+  muon::fill_info(plan->p, info);
+  return MUON_OK;
+}
+
+int muon_step(muon_plan_t plan, void* const* params, const void* const* grads, void* const* momentum,
+              float lr, float beta, int32_t ns_steps, float a, float b, float c, void* stream) {
+  if (!plan_ok(plan)) return fail(MUON_ERR_INVALID_ARGUMENT, "invalid plan handle");
+  const muon::Plan& p = plan->p;
+  if (!params || !grads || !momentum) return fail(MUON_ERR_INVALID_ARGUMENT, "null pointer array");
+  for (int i = 0; i < p.n_params; ++i) {
+    const void* ptr3[3] = {params[i], grads[i], momentum[i]};
+    const char* names[3] = {"params", "grads", "momentum"};
+    for (int k = 0; k < 3; ++k) {
+      if (ptr3[k] == nullptr) return fail(MUON_ERR_INVALID_ARGUMENT, "%s[%d] is null", names[k], i);
+      if ((reinterpret_cast<uintptr_t>(ptr3[k]) & 15) != 0)
+        return fail(MUON_ERR_INVALID_ARGUMENT, "%s[%d] is not 16-byte aligned", names[k], i);
+    }
+  }
+  if (ns_steps < 0 || ns_steps > p.max_ns_steps)
+    return fail(MUON_ERR_INVALID_ARGUMENT, "ns_steps %d outside [0, %d]", ns_steps, p.max_ns_steps);
+  const float sc5[5] = {lr, beta, a, b, c};
+  const char* sn[5] = {"lr", "beta", "a", "b", "c"};
+  for (int k = 0; k < 5; ++k)
+    if (!std::isfinite(sc5[k])) return fail(MUON_ERR_INVALID_ARGUMENT, "%s is not finite", sn[k]);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->device)
+    return fail(MUON_ERR_DEVICE_MISMATCH, "plan lives on device %d, current device is %d", plan->device, dev);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // Pointer table: upload only when it changed.
+  std::vector<muon::PtrEntry> now(p.n_params);
+  for (int i = 0; i < p.n_params; ++i) {
+    now[i].w = params[i];
+    now[i].g = grads[i];
+    now[i].m = static_cast<float*>(momentum[i]);
+  }
+  const bool same = plan->ptrs_valid &&
+                    std::memcmp(now.data(), plan->ptrs.data(), sizeof(muon::PtrEntry) * p.n_params) == 0;
+  if (!same) {
+    if (plan->upload_pending) {
+      e = hipEventSynchronize(plan->upload_done);  // the staging buffer is still being read
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    }
+    std::memcpy(plan->pinned, now.data(), sizeof(muon::PtrEntry) * p.n_params);
+    e = hipMemcpyAsync(plan->ws + p.off_ptrs, plan->pinned, sizeof(muon::PtrEntry) * p.n_params,
+                       hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "pointer table upload");
+    e = hipEventRecord(plan->upload_done, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    plan->upload_pending = true;
+    plan->ptrs = now;
+    plan->ptrs_valid = true;
+  }
+
+  muon::DevScalars v;
+  v.lr = lr;
+  v.beta = beta;
+  v.a = a;
+  v.b = b;
+  v.c = c;
+  v.eps = p.eps;
+  v.ns_steps = ns_steps;
+  v.pad = 0;
+  e = muon::launch_prologue(at<muon::DevScalars>(plan, p.off_scalars), v,
+                            at<uint32_t>(plan, p.off_ctrs), p.n_resident_slices, s);
+  if (e != hipSuccess) return hip_fail(e, "prologue launch");
+
+  const bool timing = p.timing != 0;
+  for (const auto& bp : p.buckets) {
+    if (bp.path != MUON_PATH_RESIDENT) continue;
+    e = enqueue_resident(plan, bp, ns_steps, s, timing);
+    if (e != hipSuccess) return hip_fail(e, "resident launch");
+  }
+  if (!has_streamed(p)) return MUON_OK;
+
+  const bool graph = p.use_graph && !timing && s != nullptr;
+  if (!graph) {
+    e = enqueue_streamed_buckets(plan, ns_steps, s, timing);
+    if (e != hipSuccess) return hip_fail(e, "streamed launch");
+    return MUON_OK;
+  }
+  if (plan->gexec == nullptr || plan->graph_ns != ns_steps || plan->graph_stream != s) {
+    drop_graph(plan);
+    e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+    hipError_t le = enqueue_streamed_buckets(plan, ns_steps, s, false);
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(s, &g);
+    if (le != hipSuccess) {
+      if (g) hipGraphDestroy(g);
+      return hip_fail(le, "launch during capture");
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+    e = hipGraphInstantiate(&plan->gexec, g, nullptr, nullptr, 0);
+    hipGraphDestroy(g);
+    if (e != hipSuccess) {
+      plan->gexec = nullptr;
+      return hip_fail(e, "hipGraphInstantiate");
+    }
+    plan->graph_ns = ns_steps;
+    plan->graph_stream = s;
+  }
+  e = hipGraphLaunch(plan->gexec, s);
+  if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  return MUON_OK;
+}
+
+int muon_plan_status(muon_plan_t plan, uint32_t* device_error) {
+  if (!plan_ok(plan)) return fail(MUON_ERR_INVALID_ARGUMENT, "invalid plan handle");
+  hipError_t e = hipSetDevice(plan->device);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  uint32_t word = 0;
+  e = hipMemcpy(&word, plan->ws + plan->p.off_err, sizeof word, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && word != 0) e = hipMemset(plan->ws + plan->p.off_err, 0, sizeof word);
+  if (e != hipSuccess) return hip_fail(e, "reading the device error word");
+  if (device_error) *device_error = word;
+  if (word != 0) return fail(MUON_ERR_DEVICE, "device error word 0x%x (a resident-kernel wait gave up)", word);
+  return MUON_OK;
+}
+
+int muon_plan_timings(muon_plan_t plan, double* out_ms, int64_t* out_count, int32_t n_out) {
+  if (!plan_ok(plan)) return fail(MUON_ERR_INVALID_ARGUMENT, "invalid plan handle");
+  for (TimedLaunch& t : plan->timed) {
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    hipEventElapsedTime(&ms, t.start, t.stop);
+    plan->acc_ms[t.cls] += ms;
+    plan->acc_cnt[t.cls] += 1;
+    plan->event_pool.push_back(t.start);
+    plan->event_pool.push_back(t.stop);
+  }
+  plan->timed.clear();
+  for (int i = 0; i < n_out && i < muon::kNumClasses; ++i) {
+    if (out_ms) out_ms[i] = plan->acc_ms[i];
+    if (out_count) out_count[i] = plan->acc_cnt[i];
+    plan->acc_ms[i] = 0.0;
+    plan->acc_cnt[i] = 0;
+  }
+  return muon::kNumClasses;
+}
+
+int muon_plan_destroy(muon_plan_t plan) {
+  if (plan == nullptr) return MUON_OK;
+  if (!plan_ok(plan)) return fail(MUON_ERR_INVALID_ARGUMENT, "invalid plan handle");
+  int cur = -1;
+  hipGetDevice(&cur);
+  if (cur != plan->device) hipSetDevice(plan->device);
+  hipDeviceSynchronize();
+  drop_graph(plan);
+  for (TimedLaunch& t : plan->timed) {
+    hipEventDestroy(t.start);
+    hipEventDestroy(t.stop);
+  }
+  for (hipEvent_t ev : plan->event_pool) hipEventDestroy(ev);
+  if (plan->upload_done) hipEventDestroy(plan->upload_done);
+  if (plan->pinned) hipHostFree(plan->pinned);
+  if (plan->ws) hipFree(plan->ws);
+  if (cur >= 0 && cur != plan->device) hipSetDevice(cur);
+  plan->magic = 0;
+  delete plan;
+  return MUON_OK;
+}
+
+}  // extern "C"

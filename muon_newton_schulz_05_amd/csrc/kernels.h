@@ -1,0 +1,111 @@
+// kernels.h -- host-side launchers of the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace muon {
+
+// Writes the step's scalars and clears the resident arrival counters.
+hipError_t launch_prologue(DevScalars* dst, const DevScalars& v, uint32_t* ctrs, int n_ctrs,
+                           hipStream_t s);
+
+// ---------------------------------------------------------------- resident
+struct ResidentLaunch {
+  const DevMat* mats;     // bucket's slice table
+  const PtrEntry* ptrs;
+  const DevScalars* sc;
+  float* gram_parts;      // [2][count][cluster][32*32] (round parity)
+  double* sq_parts;       // [count][cluster]
+  uint32_t* ctrs;         // [count]
+  uint32_t* err;
+  int m, n;
+  int cluster, tiles_per_wg, tpw;
+  int count;              // slices in the bucket
+  int mat_base, n_mats;   // slices of this cooperative launch
+  int ns_steps;
+  uint32_t spin_limit;
+  int bf16;               // 1: bf16 matrix-core mode, 0: fp32 mode
+};
+hipError_t launch_resident(const ResidentLaunch& a, hipStream_t s);
+// Co-resident workgroups per CU of the resident kernel variant (0 on error).
+int resident_occupancy(int tpw, int bf16);
+
+// ---------------------------------------------------------------- streamed
+struct MomentumLaunch {
+  const DevMat* mats;
+  const PtrEntry* ptrs;
+  const DevScalars* sc;
+  void* x;                // [count][mp][np]
+  void* xt;               // [count][np][mp]
+  float* sq;              // [count][km_tiles]
+  int64_t m, n, mp, np;
+  int count, km_tiles, x_bytes;
+};
+hipError_t launch_momentum(const MomentumLaunch& a, hipStream_t s);
+
+struct NormLaunch {
+  const float* sq;
+  float* scale;           // [count][2] = {s, s*s}
+  const DevScalars* sc;
+  int count, km_tiles;
+};
+hipError_t launch_norm(const NormLaunch& a, hipStream_t s);
+
+// A = scale2 * X X^T  (scale2 = s^2 on the first round, else 1)
+struct GramLaunch {
+  const void* x;
+  float* a32;
+  uint16_t* a16;          // bf16 copy of A (or null)
+  const float* scale;     // null after the first round
+  int64_t mp, np;
+  int count, x_bytes;
+};
+hipError_t launch_gram(const GramLaunch& a, hipStream_t s);
+
+// P = b A + c A A  (A symmetric, so A A = A A^T)
+struct PolyLaunch {
+  const void* op;         // A as the product's operand: a32 (float) or a16 (bf16)
+  int op_bytes;
+  const float* a32;
+  void* phi;              // P (float) or its bf16 high part
+  uint16_t* plo;          // bf16 low part (or null)
+  int p_bytes;
+  const DevScalars* sc;
+  int64_t mp;
+  int count;
+};
+hipError_t launch_poly(const PolyLaunch& a, hipStream_t s);
+
+// X' = scale * (a X + P X); the final round subtracts lr * X' from W instead.
+struct ApplyLaunch {
+  const void* phi;
+  const void* plo;        // or null
+  int p_bytes;
+  const void* xt_old;
+  const void* x_old;
+  void* x_new;
+  void* xt_new;
+  const float* scale;     // null after the first round
+  const DevScalars* sc;
+  int64_t mp, np, m, n;
+  int count, x_bytes;
+  int final_round;
+  const DevMat* mats;
+  const PtrEntry* ptrs;
+};
+hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
+
+// ns_steps == 0: W -= lr * s * M.
+struct Update0Launch {
+  const DevMat* mats;
+  const PtrEntry* ptrs;
+  const DevScalars* sc;
+  const float* scale;
+  int64_t m, n;
+  int count;
+};
+hipError_t launch_update0(const Update0Launch& a, hipStream_t s);
+
+}  // namespace muon

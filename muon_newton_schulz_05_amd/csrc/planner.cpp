@@ -1,0 +1,278 @@
+// planner.cpp -- validation, orientation, shape buckets and workspace layout.
+#include "planner.h"
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <utility>
+
+namespace muon {
+
+namespace {
+
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Tiles-per-wave values the resident kernel is compiled for.
+const int kTpwBf16[] = {1, 2, 4, 8, 14};
+const int kTpwF32[] = {1, 2, 4, 8};
+
+struct Alloc {
+  uint64_t top = 0;
+  uint64_t take(uint64_t bytes) {
+    uint64_t off = align_up(top, 256);
+    top = off + bytes;
+    return off;
+  }
+};
+
+}  // namespace
+
+int resident_tpw_max(int mode) { return mode == MUON_MODE_FP32 ? 8 : 14; }
+
+int resident_tpw_pick(int mode, int need) {
+  if (mode == MUON_MODE_FP32) {
+    for (int t : kTpwF32)
+      if (t >= need) return t;
+  } else {
+    for (int t : kTpwBf16)
+      if (t >= need) return t;
+  }
+  return 0;
+}
+
+void default_opts(muon_plan_opts_t* o) {
+  std::memset(o, 0, sizeof(*o));
+  o->mode = MUON_MODE_BF16_MFMA;
+  o->use_graph = 0;
+  o->eps = 1e-7f;
+  o->max_ns_steps = 16;
+  o->workspace_limit = 0;
+  o->resident_max_m = 0;
+  o->timing = 0;
+  o->n_cu = 0;
+}
+
+int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_opts_t* opts_in,
+              int n_cu, int occupancy, Plan* out, std::string* err) {
+  char buf[256];
+  if (descs == nullptr || out == nullptr) {
+    *err = "null descriptor array or output";
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  if (n_params <= 0) {
+    *err = "n_params must be positive";
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  muon_plan_opts_t opts;
+  if (opts_in) opts = *opts_in;
+  else default_opts(&opts);
+  if (opts.mode != MUON_MODE_FP32 && opts.mode != MUON_MODE_BF16_MFMA) {
+    *err = "unknown mode";
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  if (!std::isfinite(opts.eps) || opts.eps < 0.f) {
+    *err = "eps must be finite and >= 0";
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  if (opts.max_ns_steps < 0 || opts.max_ns_steps > 1000) {
+    *err = "max_ns_steps must be in [0, 1000]";
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  if (opts.resident_max_m < -1 || opts.resident_max_m > kMaxResidentM) {
+    std::snprintf(buf, sizeof buf, "resident_max_m must be -1, 0 or in [1, %d]", kMaxResidentM);
+    *err = buf;
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  if (n_cu <= 0 || occupancy <= 0) {
+    *err = "device description has no compute units";
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+
+  Plan p;
+  p.mode = opts.mode;
+  p.eps = opts.eps;
+  p.max_ns_steps = opts.max_ns_steps;
+  p.workspace_limit = opts.workspace_limit;
+  p.resident_max_m = opts.resident_max_m == 0 ? kMaxResidentM
+                     : opts.resident_max_m < 0 ? 0 : opts.resident_max_m;
+  p.timing = opts.timing ? 1 : 0;
+  p.use_graph = opts.use_graph ? 1 : 0;
+  p.n_cu = n_cu;
+  p.resident_occupancy = occupancy;
+  p.n_params = n_params;
+  p.descs.assign(descs, descs + n_params);
+
+  // Expand parameters into 2-D slices and orient each one.
+  for (int i = 0; i < n_params; ++i) {
+    const muon_param_desc_t& d = descs[i];
+    if (d.ndim != 2 && d.ndim != 3) {
+      std::snprintf(buf, sizeof buf, "parameter %d: ndim %d (Muon takes 2-D matrices or 3-D stacks)",
+                    i, d.ndim);
+      *err = buf;
+      return MUON_ERR_INVALID_ARGUMENT;
+    }
+    for (int k = 0; k < d.ndim; ++k) {
+      if (d.shape[k] <= 0 || d.shape[k] >= (int64_t(1) << 31)) {
+        std::snprintf(buf, sizeof buf, "parameter %d: dimension %d is %lld", i, k,
+                      (long long)d.shape[k]);
+        *err = buf;
+        return MUON_ERR_INVALID_ARGUMENT;
+      }
+    }
+    if ((d.param_dtype != MUON_F32 && d.param_dtype != MUON_BF16) ||
+        (d.grad_dtype != MUON_F32 && d.grad_dtype != MUON_BF16)) {
+      std::snprintf(buf, sizeof buf, "parameter %d: unknown dtype", i);
+      *err = buf;
+      return MUON_ERR_INVALID_ARGUMENT;
+    }
+    const int64_t E = d.ndim == 3 ? d.shape[0] : 1;
+    const int64_t R = d.shape[d.ndim - 2], C = d.shape[d.ndim - 1];
+    if (E * R * C >= (int64_t(1) << 40)) {
+      std::snprintf(buf, sizeof buf, "parameter %d: too many elements", i);
+      *err = buf;
+      return MUON_ERR_INVALID_ARGUMENT;
+    }
+    for (int64_t e = 0; e < E; ++e) {
+      Slice s;
+      s.param = i;
+      s.e = (int)e;
+      s.rows = R;
+      s.cols = C;
+      s.transposed = R > C ? 1 : 0;
+      s.m = s.transposed ? C : R;
+      s.n = s.transposed ? R : C;
+      s.slice_off = e * R * C;
+      s.pdtype = d.param_dtype;
+      s.gdtype = d.grad_dtype;
+      p.slices.push_back(s);
+    }
+  }
+
+  // Bucket by oriented shape, in order of first appearance.
+  std::map<std::pair<int64_t, int64_t>, int> index;
+  for (int si = 0; si < (int)p.slices.size(); ++si) {
+    Slice& s = p.slices[si];
+    auto key = std::make_pair(s.m, s.n);
+    auto it = index.find(key);
+    int b;
+    if (it == index.end()) {
+      if ((int)p.buckets.size() >= MUON_MAX_BUCKETS) {
+        std::snprintf(buf, sizeof buf, "more than %d distinct oriented shapes", MUON_MAX_BUCKETS);
+        *err = buf;
+        return MUON_ERR_UNSUPPORTED;
+      }
+      b = (int)p.buckets.size();
+      index[key] = b;
+      BucketPlan bp;
+      bp.m = s.m;
+      bp.n = s.n;
+      bp.path = s.m <= p.resident_max_m ? MUON_PATH_RESIDENT : MUON_PATH_STREAM;
+      p.buckets.push_back(bp);
+    } else {
+      b = it->second;
+    }
+    s.bucket = b;
+    p.buckets[b].slices.push_back(si);
+    p.buckets[b].n_transposed += s.transposed;
+  }
+
+  // Geometry and workspace.
+  Alloc ws;
+  p.off_scalars = ws.take(sizeof(DevScalars));
+  p.off_err = ws.take(sizeof(uint32_t));
+  p.off_ptrs = ws.take(sizeof(PtrEntry) * (uint64_t)n_params);
+  p.launches_fixed = 1;  // prologue
+  p.launches_per_ns = 0;
+  for (BucketPlan& bp : p.buckets) {
+    const uint64_t cnt = bp.slices.size();
+    bp.ws_begin = ws.take(0);
+    bp.off_mats = ws.take(sizeof(DevMat) * cnt);
+    if (bp.path == MUON_PATH_RESIDENT) {
+      const int ntiles = (int)((bp.n + 31) / 32);
+      const int per_wg_max = kResidentWaves * resident_tpw_max(p.mode);
+      bp.cluster = (ntiles + per_wg_max - 1) / per_wg_max;
+      bp.tiles_per_wg = (ntiles + bp.cluster - 1) / bp.cluster;
+      bp.tpw = resident_tpw_pick(p.mode, (bp.tiles_per_wg + kResidentWaves - 1) / kResidentWaves);
+      const int capacity = p.n_cu * p.resident_occupancy;
+      if (bp.cluster > capacity) {
+        std::snprintf(buf, sizeof buf, "slice [%lld,%lld] needs %d co-resident workgroups, device has %d",
+                      (long long)bp.m, (long long)bp.n, bp.cluster, capacity);
+        *err = buf;
+        return MUON_ERR_UNSUPPORTED;
+      }
+      bp.mats_per_group = capacity / bp.cluster;
+      bp.groups = (int)((cnt + bp.mats_per_group - 1) / bp.mats_per_group);
+      bp.off_gram = ws.take(2 * cnt * bp.cluster * 1024 * sizeof(float));
+      bp.off_sqp = ws.take(cnt * bp.cluster * sizeof(double));
+      p.n_resident_slices += (int)cnt;
+      p.launches_fixed += bp.groups;
+    } else {
+      bp.mp = round_up(bp.m, kStreamPad);
+      bp.np = round_up(bp.n, kStreamPad);
+      bp.x_bytes = p.mode == MUON_MODE_FP32 ? 4 : 2;
+      bp.poly_f32 = p.mode == MUON_MODE_FP32 || bp.m <= 512;
+      bp.p_hilo = p.mode == MUON_MODE_BF16_MFMA && bp.m <= 512;
+      bp.km_tiles = (int)(((bp.m + kMomTile - 1) / kMomTile) * ((bp.n + kMomTile - 1) / kMomTile));
+      const uint64_t xsz = cnt * bp.mp * bp.np * bp.x_bytes;
+      const uint64_t msz = cnt * bp.mp * bp.mp;
+      for (int i = 0; i < 2; ++i) bp.off_x[i] = ws.take(xsz);
+      for (int i = 0; i < 2; ++i) bp.off_xt[i] = ws.take(xsz);
+      bp.off_a32 = ws.take(msz * 4);
+      bp.off_a16 = (p.mode == MUON_MODE_BF16_MFMA && !bp.poly_f32) ? ws.take(msz * 2) : 0;
+      bp.off_phi = ws.take(msz * (p.mode == MUON_MODE_FP32 ? 4 : 2));
+      bp.off_plo = bp.p_hilo ? ws.take(msz * 2) : 0;
+      bp.off_sq = ws.take(cnt * bp.km_tiles * sizeof(float));
+      bp.off_scale = ws.take(cnt * 2 * sizeof(float));
+      p.launches_fixed += 2;   // momentum, norm
+      p.launches_per_ns += 3;  // gram, poly, apply (the last apply also updates W)
+    }
+    bp.ws_bytes = ws.take(0) - bp.ws_begin;
+  }
+  // Arrival counters of all resident slices sit in one block so that the
+  // prologue clears them with a single store pass.
+  p.off_ctrs = ws.take(sizeof(uint32_t) * (uint64_t)(p.n_resident_slices > 0 ? p.n_resident_slices : 1));
+  {
+    uint64_t pos = p.off_ctrs;
+    for (BucketPlan& bp : p.buckets) {
+      if (bp.path != MUON_PATH_RESIDENT) continue;
+      bp.off_ctr = pos;
+      pos += sizeof(uint32_t) * bp.slices.size();
+    }
+  }
+  p.ws_total = align_up(ws.top, 256);
+  if (p.workspace_limit != 0 && p.ws_total > p.workspace_limit) {
+    std::snprintf(buf, sizeof buf, "workspace needs %llu bytes, limit is %llu",
+                  (unsigned long long)p.ws_total, (unsigned long long)p.workspace_limit);
+    *err = buf;
+    return MUON_ERR_OOM;
+  }
+  *out = std::move(p);
+  return MUON_OK;
+}
+
+void fill_info(const Plan& p, muon_plan_info_t* info) {
+  std::memset(info, 0, sizeof(*info));
+  info->n_params = p.n_params;
+  info->n_matrices = (int)p.slices.size();
+  info->n_buckets = (int)p.buckets.size();
+  info->mode = p.mode;
+  info->workspace_bytes = p.ws_total;
+  info->launches_fixed = p.launches_fixed;
+  info->launches_per_ns = p.launches_per_ns;
+  for (int i = 0; i < (int)p.buckets.size() && i < MUON_MAX_BUCKETS; ++i) {
+    const BucketPlan& b = p.buckets[i];
+    muon_bucket_info_t& o = info->buckets[i];
+    o.m = b.m;
+    o.n = b.n;
+    o.count = (int)b.slices.size();
+    o.n_transposed = b.n_transposed;
+    o.path = b.path;
+    o.cluster = b.cluster;
+    o.groups = b.groups;
+    o.workspace_bytes = b.ws_bytes;
+  }
+}
+
+}  // namespace muon

@@ -1,0 +1,87 @@
+// planner.h -- host-side planning of a fused Muon step (no HIP calls).
+//
+// Groups 2-D slices by oriented shape so that each group runs as one batched
+// problem ("MindSpore HyperParallel X 盘古,Muon优化器实现6倍性能跃升", section
+// 矩阵融合优化 / matrix fusion: parameters whose last two dimensions agree are
+// stacked into one [B, M, N] problem; section 专家切分 / expert split: each
+// slice of a 3-D expert tensor is independent), picks a kernel path per group
+// and lays out the device workspace.
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "layout.h"
+
+namespace muon {
+
+struct Slice {
+  int param = 0, e = 0, transposed = 0, pdtype = 0, gdtype = 0;
+  int64_t rows = 0, cols = 0, m = 0, n = 0, slice_off = 0;
+  int bucket = -1;
+};
+
+struct BucketPlan {
+  int64_t m = 0, n = 0;
+  int path = MUON_PATH_STREAM;
+  std::vector<int> slices;  // indices into Plan::slices, in plan order
+  int n_transposed = 0;
+
+  // resident path
+  int cluster = 0;          // workgroups per slice
+  int tiles_per_wg = 0;     // 32-column tiles per workgroup
+  int tpw = 0;              // tiles per wave (kernel instantiation)
+  int mats_per_group = 0;   // slices per cooperative launch
+  int groups = 0;
+  uint64_t off_gram = 0, off_sqp = 0, off_ctr = 0;
+
+  // streamed path
+  int64_t mp = 0, np = 0;   // padded dims
+  int x_bytes = 0;          // X element size (2: bf16, 4: fp32)
+  bool poly_f32 = false;    // A^2 from float32 A (else bf16 copy of A)
+  bool p_hilo = false;      // B fed to the matrix cores as a bf16 hi/lo pair
+  int km_tiles = 0;         // momentum-kernel tiles per slice
+  uint64_t off_x[2] = {0, 0}, off_xt[2] = {0, 0};
+  uint64_t off_a32 = 0, off_a16 = 0, off_phi = 0, off_plo = 0, off_sq = 0, off_scale = 0;
+
+  uint64_t off_mats = 0;    // this bucket's DevMat table
+  uint64_t ws_begin = 0, ws_bytes = 0;
+};
+
+struct Plan {
+  int mode = MUON_MODE_BF16_MFMA;
+  float eps = 1e-7f;
+  int max_ns_steps = 16;
+  uint64_t workspace_limit = 0;
+  int resident_max_m = kMaxResidentM;
+  int timing = 0, use_graph = 0;
+  int n_cu = 256;
+  int resident_occupancy = 1;  // co-resident resident-kernel workgroups per CU
+
+  int n_params = 0;
+  std::vector<muon_param_desc_t> descs;
+  std::vector<Slice> slices;
+  std::vector<BucketPlan> buckets;
+  uint64_t off_scalars = 0, off_err = 0, off_ptrs = 0, off_ctrs = 0;
+  int n_resident_slices = 0;
+  uint64_t ws_total = 0;
+  int launches_fixed = 0, launches_per_ns = 0;
+};
+
+// Largest tiles-per-wave instantiation of the resident kernel for a mode.
+int resident_tpw_max(int mode);
+// Smallest instantiated tiles-per-wave >= need (0 if none).
+int resident_tpw_pick(int mode, int need);
+
+void default_opts(muon_plan_opts_t* o);
+
+// Validate and plan.  n_cu / occupancy describe the device (create) or the
+// assumed device (describe).  Returns a muon_status_t; *err gets a message.
+int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_opts_t* opts,
+              int n_cu, int resident_occupancy, Plan* out, std::string* err);
+
+void fill_info(const Plan& p, muon_plan_info_t* info);
+
+}  // namespace muon

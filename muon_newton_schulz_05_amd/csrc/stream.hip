@@ -1,0 +1,442 @@
+// stream.hip -- kernels of the streamed path (slices with m > 32).
+//
+// Per step and shape bucket:
+//   momentum  M <- beta M + G, per-tile sums of squares, X0 = M (oriented) and
+//             its transpose into the workspace          ("关于分布式Muon的想法整合及讨论"
+//                                                        §1, §2, §6)
+//   norm      s = 1 / (||M||_F + eps) from the tile sums, fixed order
+//   k rounds  gram   A = X X^T          (s^2 folded in on the first round)
+//             poly   P = b A + c A A
+//             apply  X' = a X + P X     (s folded in on the first round;
+//                                         the last round updates W instead)
+// ("MindSpore HyperParallel X 盘古,Muon优化器实现6倍性能跃升", 三大性能挑战: the
+// iteration is rounds of matrix products and additions.)
+//
+// Every product is C[i][j] = sum_k A[i][k] B[j][k] with both operands
+// contiguous along k: X X^T reads X twice, A A reads the symmetric A twice,
+// P X reads P and the transposed copy X^T that the previous round wrote.
+// Workspace matrices are zero-padded to multiples of 128, so the products run
+// on whole tiles and the padding stays exactly zero.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace muon {
+namespace {
+
+// ------------------------------------------------------------------ prologue
+__global__ void k_prologue(DevScalars* dst, DevScalars v, uint32_t* ctrs, int n) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *dst = v;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) ctrs[i] = 0;
+}
+
+// ------------------------------------------------------------------ momentum
+template <typename XT>
+__global__ __launch_bounds__(256) void k_momentum(MomentumLaunch a) {
+  __shared__ float tile[kMomTile][kMomTile + 1];
+  __shared__ float wsum[4];
+  const int z = blockIdx.y;
+  const int tiles_n = (int)((a.n + kMomTile - 1) / kMomTile);
+  const int ti = blockIdx.x / tiles_n, tj = blockIdx.x % tiles_n;
+  const int64_t i0 = (int64_t)ti * kMomTile, j0 = (int64_t)tj * kMomTile;
+  const DevMat d = a.mats[z];
+  const PtrEntry pe = a.ptrs[d.param];
+  const float beta = a.sc->beta;
+  const int tid = threadIdx.x;
+
+  // Load along the stored rows (coalesced), keep M_new in LDS in oriented order.
+  for (int q = 0; q < 16; ++q) {
+    const int fast = tid & 63, slow = (tid >> 6) + 4 * q;
+    const int ii = d.transposed ? fast : slow;
+    const int jj = d.transposed ? slow : fast;
+    const int64_t i = i0 + ii, j = j0 + jj;
+    float v = 0.f;
+    if (i < a.m && j < a.n) {
+      const int64_t idx = d.slice_off + (d.transposed ? j * a.m + i : i * a.n + j);
+      v = fmaf(beta, pe.m[idx], load_as_f32(pe.g, idx, d.gdtype));
+      pe.m[idx] = v;
+    }
+    tile[ii][jj] = v;
+  }
+  __syncthreads();
+
+  XT* x = static_cast<XT*>(a.x) + (int64_t)z * a.mp * a.np;
+  XT* xt = static_cast<XT*>(a.xt) + (int64_t)z * a.mp * a.np;
+  float sq = 0.f;
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q;
+    const int ii = e >> 6, jj = e & 63;
+    const float v = tile[ii][jj];
+    sq = fmaf(v, v, sq);
+    if (i0 + ii < a.m && j0 + jj < a.n) x[(i0 + ii) * a.np + j0 + jj] = cvt_x<XT>(v);
+  }
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q;
+    const int jj = e >> 6, ii = e & 63;
+    if (i0 + ii < a.m && j0 + jj < a.n) xt[(j0 + jj) * a.mp + i0 + ii] = cvt_x<XT>(tile[ii][jj]);
+  }
+  sq = wave_sum(sq);
+  if ((tid & 63) == 0) wsum[tid >> 6] = sq;
+  __syncthreads();
+  if (tid == 0) a.sq[(int64_t)z * a.km_tiles + blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
+// ------------------------------------------------------------------ norm
+__global__ __launch_bounds__(256) void k_norm(NormLaunch a) {
+  __shared__ double red[256];
+  const int z = blockIdx.x;
+  double s = 0.0;
+  for (int t = threadIdx.x; t < a.km_tiles; t += 256) s += (double)a.sq[(int64_t)z * a.km_tiles + t];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double sc = 1.0 / (sqrt(red[0]) + (double)a.sc->eps);
+    a.scale[2 * z] = (float)sc;
+    a.scale[2 * z + 1] = (float)(sc * sc);
+  }
+}
+
+// ------------------------------------------------------------------ GEMM core
+// 128 x 128 output tile per 256-thread workgroup; 4 waves in a 2 x 2 grid,
+// each computing 64 x 64 with 32x32 matrix-core instructions.  k-slices of
+// 64 bytes per row are staged through LDS, double buffered.
+constexpr int kBM = 128, kBN = 128;
+constexpr int kRowBytes = 64;       // bytes of k per operand row per stage
+constexpr int kLdsRow = kRowBytes + 16;
+
+struct GemmCore {
+  const char* a;   // A operand base (matrix 0)
+  const char* a2;  // second A operand (hi/lo split) or null
+  const char* b;
+  int64_t lda, ldb;          // row strides in elements
+  int64_t sa, sb;            // matrix strides in elements
+  int64_t K;                 // contraction length (multiple of the k-slice)
+  int tiles_n;               // output tiles along j
+};
+
+__device__ __forceinline__ f32x16_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <typename T, class Epi>
+__global__ __launch_bounds__(256) void k_gemm(GemmCore c, Epi epi) {
+  constexpr int BK = kRowBytes / (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) char lds[2][2][kBM * kLdsRow];
+  const int z = blockIdx.z;
+  const int tm = blockIdx.x / c.tiles_n, tn = blockIdx.x % c.tiles_n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const char* A = c.a + ((int64_t)z * c.sa + (int64_t)tm * kBM * c.lda) * (int64_t)sizeof(T);
+  const char* A2 = c.a2 ? c.a2 + ((int64_t)z * c.sa + (int64_t)tm * kBM * c.lda) * (int64_t)sizeof(T)
+                        : nullptr;
+  const char* B = c.b + ((int64_t)z * c.sb + (int64_t)tn * kBN * c.ldb) * (int64_t)sizeof(T);
+
+  int row[2], c16[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int idx = tid + 256 * h;
+    row[h] = idx >> 2;
+    c16[h] = idx & 3;
+  }
+  uint4 ra[2], rb[2];
+  const int nk = (int)(c.K / BK);
+  const int total = A2 ? 2 * nk : nk;
+
+  auto gload = [&](int it) {
+    const int kt = it % nk;
+    const char* Ab = it >= nk ? A2 : A;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra[h] = *reinterpret_cast<const uint4*>(Ab + ((int64_t)row[h] * c.lda + (int64_t)kt * BK) * (int64_t)sizeof(T) + c16[h] * 16);
+      rb[h] = *reinterpret_cast<const uint4*>(B + ((int64_t)row[h] * c.ldb + (int64_t)kt * BK) * (int64_t)sizeof(T) + c16[h] * 16);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<uint4*>(&lds[buf][0][row[h] * kLdsRow + c16[h] * 16]) = ra[h];
+      *reinterpret_cast<uint4*>(&lds[buf][1][row[h] * kLdsRow + c16[h] * 16]) = rb[h];
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16_t{};
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int it = 0; it < total; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < total) gload(it + 1);
+    const char* As = lds[cur][0];
+    const char* Bs = lds[cur][1];
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8_t af[2], bf[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          af[x] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + x * 32 + (lane & 31)) * kLdsRow + s * 32 + (lane >> 5) * 16);
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+          bf[y] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 64 + y * 32 + (lane & 31)) * kLdsRow + s * 32 + (lane >> 5) * 16);
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int y = 0; y < 2; ++y) acc[x][y] = mfma_bf16(af[x], bf[y], acc[x][y]);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        float af[2], bf[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          af[x] = *reinterpret_cast<const float*>(As + (wm * 64 + x * 32 + (lane & 31)) * kLdsRow + (s * 2 + (lane >> 5)) * 4);
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+          bf[y] = *reinterpret_cast<const float*>(Bs + (wn * 64 + y * 32 + (lane & 31)) * kLdsRow + (s * 2 + (lane >> 5)) * 4);
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int y = 0; y < 2; ++y) acc[x][y] = mfma_f32(af[x], bf[y], acc[x][y]);
+      }
+    }
+    if (it + 1 < total) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Output layout of a 32x32 block: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32.
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int i0 = tm * kBM + wm * 64 + x * 32 + 8 * g + 4 * (lane >> 5);
+        const int j = tn * kBN + wn * 64 + y * 32 + (lane & 31);
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = acc[x][y][4 * g + u];
+        epi(z, i0, j, v);
+      }
+}
+
+// ------------------------------------------------------------------ epilogues
+struct GramEpi {
+  float* a32;
+  uint16_t* a16;
+  const float* scale;
+  int64_t mp;
+  __device__ void operator()(int z, int i0, int j, const float v[4]) const {
+    const float s = scale ? scale[2 * z + 1] : 1.f;
+    const int64_t base = (int64_t)z * mp * mp + j;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float val = s * v[u];
+      a32[base + (int64_t)(i0 + u) * mp] = val;
+      if (a16) a16[base + (int64_t)(i0 + u) * mp] = to_bf16(val);
+    }
+  }
+};
+
+struct PolyEpi {
+  const float* a32;
+  void* phi;
+  uint16_t* plo;
+  int p_f32;
+  const DevScalars* sc;
+  int64_t mp;
+  __device__ void operator()(int z, int i0, int j, const float v[4]) const {
+    const float b = sc->b, c = sc->c;
+    const int64_t base = (int64_t)z * mp * mp + j;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t idx = base + (int64_t)(i0 + u) * mp;
+      const float val = b * a32[idx] + c * v[u];
+      if (p_f32) {
+        static_cast<float*>(phi)[idx] = val;
+      } else {
+        const uint16_t hi = to_bf16(val);
+        static_cast<uint16_t*>(phi)[idx] = hi;
+        if (plo) plo[idx] = to_bf16(val - from_bf16(hi));
+      }
+    }
+  }
+};
+
+template <typename XT>
+struct ApplyEpi {
+  const XT* x_old;
+  XT* x_new;
+  XT* xt_new;
+  const float* scale;
+  const DevScalars* sc;
+  int64_t mp, np;
+  __device__ void operator()(int z, int i0, int j, const float v[4]) const {
+    const float s = scale ? scale[2 * z] : 1.f;
+    const float a = sc->a;
+    const int64_t zo = (int64_t)z * mp * np;
+    XT out[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t idx = zo + (int64_t)(i0 + u) * np + j;
+      const float val = s * fmaf(a, x_to_f32(x_old[idx]), v[u]);
+      out[u] = cvt_x<XT>(val);
+      x_new[idx] = out[u];
+    }
+    XT* t = xt_new + zo + (int64_t)j * mp + i0;
+    if constexpr (sizeof(XT) == 2) {
+      uint2 p;
+      p.x = (uint32_t)out[0] | ((uint32_t)out[1] << 16);
+      p.y = (uint32_t)out[2] | ((uint32_t)out[3] << 16);
+      *reinterpret_cast<uint2*>(t) = p;
+    } else {
+      *reinterpret_cast<float4*>(t) = make_float4(out[0], out[1], out[2], out[3]);
+    }
+  }
+};
+
+template <typename XT>
+struct FinalEpi {
+  const XT* x_old;
+  const float* scale;
+  const DevScalars* sc;
+  const DevMat* mats;
+  const PtrEntry* ptrs;
+  int64_t mp, np, m, n;
+  __device__ void operator()(int z, int i0, int j, const float v[4]) const {
+    if (j >= n) return;
+    const float s = scale ? scale[2 * z] : 1.f;
+    const float a = sc->a, lr = sc->lr;
+    const DevMat d = mats[z];
+    const PtrEntry pe = ptrs[d.param];
+    const int64_t zo = (int64_t)z * mp * np;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u;
+      if (i >= m) break;
+      const float val = s * fmaf(a, x_to_f32(x_old[zo + i * np + j]), v[u]);
+      const int64_t idx = d.slice_off + (d.transposed ? (int64_t)j * m + i : i * n + j);
+      const float w = load_as_f32(pe.w, idx, d.pdtype);
+      store_from_f32(pe.w, idx, d.pdtype, w - lr * val);
+    }
+  }
+};
+
+// ------------------------------------------------------------------ ns_steps = 0
+__global__ __launch_bounds__(256) void k_update0(Update0Launch a) {
+  const int z = blockIdx.y;
+  const DevMat d = a.mats[z];
+  const PtrEntry pe = a.ptrs[d.param];
+  const float k = a.sc->lr * a.scale[2 * z];
+  const int64_t total = a.m * a.n;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t idx = d.slice_off + e;  // stored order; O and W share the layout
+    const float w = load_as_f32(pe.w, idx, d.pdtype);
+    store_from_f32(pe.w, idx, d.pdtype, w - k * pe.m[idx]);
+  }
+}
+
+template <typename T, class Epi>
+hipError_t run_gemm(const GemmCore& c, const Epi& e, int64_t rows, int count, hipStream_t s) {
+  const int tiles = (int)(rows / kBM) * c.tiles_n;
+  hipLaunchKernelGGL((k_gemm<T, Epi>), dim3(tiles, 1, count), dim3(256), 0, s, c, e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prologue(DevScalars* dst, const DevScalars& v, uint32_t* ctrs, int n_ctrs,
+                           hipStream_t s) {
+  const int blocks = n_ctrs > 0 ? (n_ctrs + 255) / 256 : 1;
+  hipLaunchKernelGGL(k_prologue, dim3(blocks < 64 ? blocks : 64), dim3(256), 0, s, dst, v, ctrs, n_ctrs);
+  return hipGetLastError();
+}
+
+hipError_t launch_momentum(const MomentumLaunch& a, hipStream_t s) {
+  if (a.x_bytes == 2) hipLaunchKernelGGL(k_momentum<uint16_t>, dim3(a.km_tiles, a.count), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_momentum<float>, dim3(a.km_tiles, a.count), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(const NormLaunch& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_norm, dim3(a.count), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gram(const GramLaunch& a, hipStream_t s) {
+  GemmCore c;
+  c.a = static_cast<const char*>(a.x);
+  c.a2 = nullptr;
+  c.b = c.a;
+  c.lda = c.ldb = a.np;
+  c.sa = c.sb = a.mp * a.np;
+  c.K = a.np;
+  c.tiles_n = (int)(a.mp / kBN);
+  GramEpi e{a.a32, a.a16, a.scale, a.mp};
+  return a.x_bytes == 2 ? run_gemm<uint16_t>(c, e, a.mp, a.count, s)
+                        : run_gemm<float>(c, e, a.mp, a.count, s);
+}
+
+hipError_t launch_poly(const PolyLaunch& a, hipStream_t s) {
+  GemmCore c;
+  c.a = static_cast<const char*>(a.op);
+  c.a2 = nullptr;
+  c.b = c.a;
+  c.lda = c.ldb = a.mp;
+  c.sa = c.sb = a.mp * a.mp;
+  c.K = a.mp;
+  c.tiles_n = (int)(a.mp / kBN);
+  PolyEpi e{a.a32, a.phi, a.plo, a.p_bytes == 4, a.sc, a.mp};
+  return a.op_bytes == 2 ? run_gemm<uint16_t>(c, e, a.mp, a.count, s)
+                         : run_gemm<float>(c, e, a.mp, a.count, s);
+}
+
+hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
+  GemmCore c;
+  c.a = static_cast<const char*>(a.phi);
+  c.a2 = static_cast<const char*>(a.plo);
+  c.b = static_cast<const char*>(a.xt_old);
+  c.lda = a.mp;
+  c.ldb = a.mp;
+  c.sa = a.mp * a.mp;
+  c.sb = a.np * a.mp;
+  c.K = a.mp;
+  c.tiles_n = (int)(a.np / kBN);
+  if (a.x_bytes == 2) {
+    if (a.final_round) {
+      FinalEpi<uint16_t> e{static_cast<const uint16_t*>(a.x_old), a.scale, a.sc, a.mats, a.ptrs,
+                           a.mp, a.np, a.m, a.n};
+      return run_gemm<uint16_t>(c, e, a.mp, a.count, s);
+    }
+    ApplyEpi<uint16_t> e{static_cast<const uint16_t*>(a.x_old), static_cast<uint16_t*>(a.x_new),
+                         static_cast<uint16_t*>(a.xt_new), a.scale, a.sc, a.mp, a.np};
+    return run_gemm<uint16_t>(c, e, a.mp, a.count, s);
+  }
+  if (a.final_round) {
+    FinalEpi<float> e{static_cast<const float*>(a.x_old), a.scale, a.sc, a.mats, a.ptrs,
+                      a.mp, a.np, a.m, a.n};
+    return run_gemm<float>(c, e, a.mp, a.count, s);
+  }
+  ApplyEpi<float> e{static_cast<const float*>(a.x_old), static_cast<float*>(a.x_new),
+                    static_cast<float*>(a.xt_new), a.scale, a.sc, a.mp, a.np};
+  return run_gemm<float>(c, e, a.mp, a.count, s);
+}
+
+hipError_t launch_update0(const Update0Launch& a, hipStream_t s) {
+  int64_t blocks = (a.m * a.n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_update0, dim3((unsigned)blocks, a.count), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,91 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run one
+plan step through the C ABI, run the oracle on the same bytes, compare."""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import workloads
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def to_device(a: np.ndarray, dev):
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def to_host(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().cpu().numpy()
+
+
+def make_inputs(shapes, grad_dtypes, seed, std=1e-3, param_dtypes=None, w_std=0.0, m_std=0.0):
+    grads, params, moms = [], [], []
+    for i, s in enumerate(shapes):
+        gd = grad_dtypes[i] if isinstance(grad_dtypes, (list, tuple)) else grad_dtypes
+        pd = (param_dtypes[i] if isinstance(param_dtypes, (list, tuple)) else param_dtypes) or "f32"
+        grads.append(workloads.gaussian(s, seed + i, std, gd))
+        w = workloads.gaussian(s, seed + 500 + i, w_std) if w_std else np.zeros(s, np.float32)
+        params.append(workloads.f32_to_bf16_bits(w) if pd == "bf16" else w)
+        moms.append(workloads.gaussian(s, seed + 900 + i, m_std) if m_std else np.zeros(s, np.float32))
+    return params, grads, moms
+
+
+def gpu_step(params, grads, moms, *, mode, lr, beta, ns_steps, coeffs, steps=1, plan_kw=None,
+             dev="cuda:0"):
+    """Run `steps` fused steps on one plan; return (params, momenta) as numpy."""
+    import torch
+
+    from muon_newton_schulz_05_amd import MuonPlan
+    p_dev = [to_device(p, dev) for p in params]
+    g_dev = [to_device(g, dev) for g in grads]
+    m_dev = [to_device(m, dev) for m in moms]
+    plan = MuonPlan(p_dev, grad_dtypes=[g.dtype for g in g_dev], mode=mode, **(plan_kw or {}))
+    for _ in range(steps):
+        plan.step(g_dev, m_dev, lr=lr, beta=beta, ns_steps=ns_steps, coeffs=coeffs)
+    torch.cuda.synchronize()
+    assert plan.status() == 0, "a resident-kernel wait timed out"
+    plan.close()
+    return [to_host(p) for p in p_dev], [to_host(m) for m in m_dev]
+
+
+def oracle_step(params, grads, moms, *, lr, beta, ns_steps, coeffs, steps=1):
+    w, m = list(params), list(moms)
+    o = None
+    for _ in range(steps):
+        w, m, o = oracle.muon_step(w, grads, m, lr=lr, beta=beta, ns_steps=ns_steps,
+                                   a=coeffs[0], b=coeffs[1], c=coeffs[2])
+    return w, m, o
+
+
+def slice_rel_errors(got: np.ndarray, ref: np.ndarray):
+    """Relative Frobenius error of every 2-D slice."""
+    g = oracle.decode(got) if got.dtype == np.uint16 else got.astype(np.float64)
+    r = ref.astype(np.float64)
+    if r.ndim == 2:
+        g, r = g[None], r[None]
+    out = []
+    for gs, rs in zip(g, r):
+        den = np.linalg.norm(rs)
+        out.append(np.linalg.norm(gs - rs) / den if den > 0 else np.linalg.norm(gs))
+    return out
+
+
+def update_errors(w_new_gpu, w_old, lr, o_ref):
+    """Relative Frobenius error of the applied update O = (W_old - W_new) / lr per slice."""
+    w_old64 = oracle.decode(w_old) if w_old.dtype == np.uint16 else w_old.astype(np.float64)
+    w_new64 = oracle.decode(w_new_gpu) if w_new_gpu.dtype == np.uint16 else w_new_gpu.astype(np.float64)
+    o_gpu = (w_old64 - w_new64) / np.float64(np.float32(lr))
+    return slice_rel_errors(o_gpu, o_ref)
+
+
+def max_ulp_diff(a: np.ndarray, b: np.ndarray) -> int:
+    ai = a.astype(np.float32).view(np.int32).astype(np.int64)
+    bi = b.astype(np.float32).view(np.int32).astype(np.int64)
+    return int(np.max(np.abs(ai - bi))) if a.size else 0

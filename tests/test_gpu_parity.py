@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bars: relative Frobenius error of every slice's update O <= 1e-4 in fp32 mode
+and <= 2e-2 in bf16 matrix-core mode; momentum equal to the oracle's float32
+value within 1 ulp (float32 FMA vs float64 then rounded); fused runs bitwise
+equal to per-matrix runs; identical runs bitwise equal.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_helpers import (TOL, gpu_step, make_inputs, max_ulp_diff, oracle_step, slice_rel_errors,
+                         to_device, to_host, update_errors)
+
+pytestmark = pytest.mark.gpu
+
+Q = workloads.QUINTIC
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import muon_newton_schulz_05_amd as m
+    m.load_library()
+
+
+def check(shapes, mode, *, grad_dtype="bf16", ns=5, lr=1.0, beta=0.95, seed=1, std=1e-3,
+          w_std=0.0, m_std=0.0, param_dtype=None, steps=1, plan_kw=None, tol=None):
+    params, grads, moms = make_inputs(shapes, grad_dtype, seed, std, param_dtype, w_std, m_std)
+    w_gpu, m_gpu = gpu_step(params, grads, moms, mode=mode, lr=lr, beta=beta, ns_steps=ns, coeffs=Q,
+                            steps=steps, plan_kw=plan_kw)
+    w_ref, m_ref, o_ref = oracle_step(params, grads, moms, lr=lr, beta=beta, ns_steps=ns, coeffs=Q,
+                                      steps=steps)
+    tol = tol if tol is not None else TOL[mode]
+    worst = 0.0
+    for i in range(len(shapes)):
+        if steps == 1:
+            errs = update_errors(w_gpu[i], params[i], lr, o_ref[i])
+        else:
+            errs = slice_rel_errors(w_gpu[i], w_ref[i])
+        worst = max(worst, max(errs))
+        if steps == 1:
+            assert max_ulp_diff(m_gpu[i], m_ref[i]) <= 1, f"momentum of parameter {i}"
+    print(f"{shapes} {mode}: worst relative error {worst:.3e}")
+    assert worst <= tol, f"{shapes} {mode}: {worst:.3e} > {tol}"
+    return worst
+
+
+def test_single_fp32_128x256():
+    """One float32 [128,256] matrix, N(0,1) gradient, zero momentum, fp32 mode."""
+    check([(128, 256)], "fp32", grad_dtype="f32", std=1.0, lr=0.02)
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+@pytest.mark.parametrize("shape", [(24, 10240), (10240, 24), (24, 1000), (7, 100), (32, 33),
+                                   (1, 64), (16, 5000), (3, 24, 777), (17, 4099)])
+def test_resident_shapes(shape, mode):
+    check([shape], mode)
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+@pytest.mark.parametrize("shape", [(128, 256), (100, 300), (300, 100), (33, 500), (2, 200, 333),
+                                   (256, 256), (600, 700)])
+def test_streamed_shapes(shape, mode):
+    check([shape], mode)
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+def test_mixed_plan(mode):
+    """Several buckets in one plan, both paths, transposed members, f32 and bf16 grads."""
+    shapes = [(24, 3000), (3000, 24), (160, 96), (96, 160), (4, 24, 3000), (64, 64)]
+    params, grads, moms = make_inputs(shapes, ["bf16", "f32", "bf16", "f32", "bf16", "bf16"], 5)
+    w_gpu, _ = gpu_step(params, grads, moms, mode=mode, lr=1.0, beta=0.9, ns_steps=5, coeffs=Q)
+    _, _, o_ref = oracle_step(params, grads, moms, lr=1.0, beta=0.9, ns_steps=5, coeffs=Q)
+    for i in range(len(shapes)):
+        assert max(update_errors(w_gpu[i], params[i], 1.0, o_ref[i])) <= TOL[mode]
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+def test_nonzero_state_and_bf16_params(mode):
+    """Nonzero W and momentum exercise the read-modify-write; bf16 weights are
+    rounded to nearest even, so their check allows one bf16 rounding of W."""
+    check([(24, 2000), (200, 120)], mode, w_std=0.02, m_std=1e-3, lr=0.02)
+    shapes = [(24, 2000), (200, 120)]
+    params, grads, moms = make_inputs(shapes, "bf16", 9, param_dtypes="bf16", w_std=0.02)
+    w_gpu, _ = gpu_step(params, grads, moms, mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    w_ref, _, o_ref = oracle_step(params, grads, moms, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    import oracle
+    for i in range(2):
+        got = oracle.decode(w_gpu[i])
+        err = np.linalg.norm(got - w_ref[i])
+        bound = 2.0 ** -8 * np.linalg.norm(w_ref[i]) + 0.02 * TOL[mode] * np.linalg.norm(o_ref[i])
+        assert err <= bound, (i, err, bound)
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+def test_three_steps(mode):
+    check([(24, 1500), (130, 260)], mode, steps=3, lr=0.02, w_std=0.02, tol=TOL[mode])
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+@pytest.mark.parametrize("ns", [0, 1, 2, 7])
+def test_ns_steps(ns, mode):
+    check([(24, 700), (96, 300)], mode, ns=ns)
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+def test_fusion_is_bitexact(mode):
+    """A fused bucket gives bitwise the same W and M as one plan per matrix."""
+    shapes = [(24, 2500)] * 5 + [(96, 200)] * 3 + [(2500, 24)]
+    params, grads, moms = make_inputs(shapes, "bf16", 21)
+    w_f, m_f = gpu_step(params, grads, moms, mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    for i in range(len(shapes)):
+        w_1, m_1 = gpu_step([params[i]], [grads[i]], [moms[i]], mode=mode, lr=0.02, beta=0.95,
+                            ns_steps=5, coeffs=Q)
+        assert np.array_equal(w_f[i], w_1[0]) and np.array_equal(m_f[i], m_1[0]), f"slice {i}"
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+def test_3d_equals_2d_slices(mode):
+    shapes3 = [(3, 24, 900), (2, 80, 150)]
+    params, grads, moms = make_inputs(shapes3, "bf16", 31)
+    w3, m3 = gpu_step(params, grads, moms, mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    p2 = [p[e] for p in params for e in range(p.shape[0])]
+    g2 = [g[e] for g in grads for e in range(g.shape[0])]
+    mm2 = [m[e] for m in moms for e in range(m.shape[0])]
+    w2, m2 = gpu_step(p2, g2, mm2, mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    k = 0
+    for i, p in enumerate(params):
+        for e in range(p.shape[0]):
+            assert np.array_equal(w3[i][e], w2[k]) and np.array_equal(m3[i][e], m2[k])
+            k += 1
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+@pytest.mark.parametrize("shape", [(24, 1800), (96, 230)])
+def test_transposed_input_gives_transposed_output(shape, mode):
+    params, grads, moms = make_inputs([shape], "bf16", 41)
+    w_a, _ = gpu_step(params, grads, moms, mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    gt = [np.ascontiguousarray(grads[0].T)]
+    w_b, _ = gpu_step([np.ascontiguousarray(params[0].T)], gt, [np.ascontiguousarray(moms[0].T)],
+                      mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    assert np.array_equal(w_a[0].T, w_b[0])
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+def test_deterministic(mode):
+    shapes = [(24, 4000), (256, 384)]
+    params, grads, moms = make_inputs(shapes, "bf16", 51, w_std=0.02, m_std=1e-3)
+    a = gpu_step(params, grads, moms, mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q, steps=2)
+    b = gpu_step(params, grads, moms, mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q, steps=2)
+    for x, y in zip(a[0] + a[1], b[0] + b[1]):
+        assert np.array_equal(x, y)
+
+
+def test_fused_74x24x10240_bf16():
+    """The pages' fusion example: 74 parameters of [24, 10240], bf16 grads."""
+    wl = workloads.WORKLOADS["fused_74x24x10240"]
+    grads = [workloads.gradient(wl, i) for i in range(len(wl.params))]
+    shapes = [p.shape for p in wl.params]
+    params = [np.zeros(s, np.float32) for s in shapes]
+    moms = [np.zeros(s, np.float32) for s in shapes]
+    w_gpu, m_gpu = gpu_step(params, grads, moms, mode="bf16", lr=wl.lr, beta=wl.beta,
+                            ns_steps=wl.ns_steps, coeffs=wl.coeffs)
+    _, m_ref, o_ref = oracle_step(params, grads, moms, lr=wl.lr, beta=wl.beta, ns_steps=wl.ns_steps,
+                                  coeffs=wl.coeffs)
+    worst = max(max(update_errors(w_gpu[i], params[i], wl.lr, o_ref[i])) for i in range(len(shapes)))
+    print(f"74x[24,10240] bf16: worst {worst:.3e}")
+    assert worst <= TOL["bf16"]
+    for i in range(len(shapes)):
+        assert max_ulp_diff(m_gpu[i], m_ref[i]) <= 1
+
+
+def test_fused_74x24x10240_fp32():
+    wl = workloads.WORKLOADS["fused_74x24x10240"]
+    grads = [workloads.gradient(wl, i) for i in range(len(wl.params))]
+    shapes = [p.shape for p in wl.params]
+    params = [np.zeros(s, np.float32) for s in shapes]
+    moms = [np.zeros(s, np.float32) for s in shapes]
+    w_gpu, _ = gpu_step(params, grads, moms, mode="fp32", lr=1.0, beta=wl.beta, ns_steps=5,
+                        coeffs=wl.coeffs)
+    _, _, o_ref = oracle_step(params, grads, moms, lr=1.0, beta=wl.beta, ns_steps=5, coeffs=wl.coeffs)
+    worst = max(max(update_errors(w_gpu[i], params[i], 1.0, o_ref[i])) for i in range(len(shapes)))
+    print(f"74x[24,10240] fp32: worst {worst:.3e}")
+    assert worst <= TOL["fp32"]
+
+
+def test_graph_replay_matches_eager():
+    import torch
+
+    from muon_newton_schulz_05_amd import MuonPlan
+    shapes = [(96, 300), (300, 96), (24, 800)]
+    params, grads, moms = make_inputs(shapes, "bf16", 61, w_std=0.02)
+    dev = "cuda:0"
+    outs = []
+    for use_graph in (False, True):
+        p = [to_device(x, dev) for x in params]
+        g = [to_device(x, dev) for x in grads]
+        m = [to_device(x, dev) for x in moms]
+        plan = MuonPlan(p, grad_dtypes=[x.dtype for x in g], mode="bf16", use_graph=use_graph)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            for k, lr in enumerate([0.02, 0.01, 0.03, 0.03]):
+                plan.step(g, m, lr=lr, beta=0.9, ns_steps=5, coeffs=Q)
+                s.synchronize()  # eager host work between replays
+        torch.cuda.synchronize()
+        outs.append([to_host(x) for x in p + m])
+        plan.close()
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y)
+
+
+def test_step_rejects_bad_arguments_without_side_effects():
+    import torch
+
+    from muon_newton_schulz_05_amd import MuonError, MuonPlan, muon_step
+    p = [torch.zeros(24, 100, device="cuda:0")]
+    g = [torch.ones(24, 100, device="cuda:0")]
+    m = [torch.zeros(24, 100, device="cuda:0")]
+    plan = MuonPlan(p, mode="bf16")
+    s = torch.cuda.current_stream().cuda_stream
+    for bad in [dict(lr=float("nan")), dict(beta=float("inf")), dict(ns_steps=17), dict(ns_steps=-1)]:
+        kw = dict(lr=0.02, beta=0.9, ns_steps=5)
+        kw.update(bad)
+        with pytest.raises(MuonError) as ei:
+            muon_step(plan.handle, [p[0].data_ptr()], [g[0].data_ptr()], [m[0].data_ptr()],
+                      kw["lr"], kw["beta"], kw["ns_steps"], *Q, s)
+        assert ei.value.code == 1
+    with pytest.raises(MuonError):
+        muon_step(plan.handle, [0], [g[0].data_ptr()], [m[0].data_ptr()], 0.02, 0.9, 5, *Q, s)
+    with pytest.raises(MuonError):
+        muon_step(plan.handle, [p[0].data_ptr() + 4], [g[0].data_ptr()], [m[0].data_ptr()], 0.02, 0.9, 5,
+                  *Q, s)
+    torch.cuda.synchronize()
+    assert not p[0].any() and not m[0].any()
+    plan.close()
