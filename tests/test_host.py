@@ -1,0 +1,194 @@
+"""Host-side tests (no GPU): the C-ABI library loads, exports what the header
+declares, its structs match the C layout, the planner groups each workload as
+intended and every argument error is reported with its code."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import muon_newton_schulz_05_amd as pkg
+    if not os.path.exists(pkg.LIB_PATH):
+        pytest.skip("libmuon.so not built (run __graft_entry__.build())")
+    pkg.load_library()
+    return pkg
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(m):
+    declared = header_functions()
+    assert set(declared) == set(m.EXPORTED)
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layout_matches_c(m):
+    src = r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "muon.h"
+int main(void) {
+  printf("%zu %zu %zu %zu\n", sizeof(muon_param_desc_t), sizeof(muon_plan_opts_t),
+         sizeof(muon_bucket_info_t), sizeof(muon_plan_info_t));
+  printf("%zu %zu %zu %zu\n", offsetof(muon_param_desc_t, shape), offsetof(muon_plan_opts_t, workspace_limit),
+         offsetof(muon_plan_opts_t, n_cu), offsetof(muon_plan_info_t, buckets));
+  printf("%zu %zu\n", offsetof(muon_bucket_info_t, workspace_bytes), offsetof(muon_plan_info_t, launches_per_ns));
+  return 0;
+}
+'''
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    from muon_newton_schulz_05_amd import binding as b
+    got = [ctypes.sizeof(b.ParamDesc), ctypes.sizeof(b.PlanOpts), ctypes.sizeof(b.BucketInfo),
+           ctypes.sizeof(b.PlanInfo), b.ParamDesc.shape.offset, b.PlanOpts.workspace_limit.offset,
+           b.PlanOpts.n_cu.offset, b.PlanInfo.buckets.offset, b.BucketInfo.workspace_bytes.offset,
+           b.PlanInfo.launches_per_ns.offset]
+    assert got == vals
+
+
+def describe(m, wl, **opts):
+    d = m.make_descs([p.shape for p in wl.params], [p.param_dtype for p in wl.params],
+                     [p.grad_dtype for p in wl.params])
+    opts.setdefault("mode", wl.mode)
+    return m.info_dict(m.muon_plan_describe(d, m.make_opts(**opts)))
+
+
+def bucket_keys(info):
+    return [(b["m"], b["n"], b["count"], b["n_transposed"], b["path"]) for b in info["buckets"]]
+
+
+def test_plans_of_the_workloads(m):
+    W = workloads.WORKLOADS
+    assert bucket_keys(describe(m, W["single_128x256"])) == [(128, 256, 1, 0, "stream")]
+    info = describe(m, W["fused_74x24x10240"])
+    assert bucket_keys(info) == [(24, 10240, 74, 0, "resident")]
+    assert info["buckets"][0]["cluster"] == 3 and info["buckets"][0]["groups"] == 1
+    assert info["launches_fixed"] == 2 and info["launches_per_ns"] == 0   # prologue + one kernel
+    assert bucket_keys(describe(m, W["moe_experts"])) == [(24, 10240, 32, 0, "resident"),
+                                                          (1408, 2048, 64, 0, "stream")]
+    info = describe(m, W["dense_h4096_l8"])
+    assert bucket_keys(info) == [(4096, 12288, 8, 0, "stream"), (4096, 4096, 8, 0, "stream"),
+                                 (4096, 16384, 16, 8, "stream")]
+    assert info["launches_fixed"] == 1 + 3 * 2 and info["launches_per_ns"] == 3 * 3
+    assert bucket_keys(describe(m, W["large_share"])) == [(8192, 8192, 4, 0, "stream"),
+                                                          (4096, 16384, 4, 4, "stream")]
+    assert describe(m, W["large_share"])["n_matrices"] == 8
+
+
+def test_fp32_mode_uses_smaller_clusters(m):
+    info = describe(m, workloads.WORKLOADS["fused_74x24x10240"], mode="fp32")
+    b = info["buckets"][0]
+    assert b["path"] == "resident" and b["cluster"] * 64 >= 320 and b["groups"] >= 1
+    assert b["count"] == 74
+
+
+def test_cluster_depends_on_shape_not_batch(m):
+    """Per-slice work split must not depend on the batch size (bitwise fusion)."""
+    one = m.info_dict(m.muon_plan_describe(m.make_descs([(24, 10240)], ["f32"], ["bf16"]), m.make_opts()))
+    many = m.info_dict(m.muon_plan_describe(m.make_descs([(24, 10240)] * 200, ["f32"] * 200, ["bf16"] * 200),
+                                            m.make_opts()))
+    assert one["buckets"][0]["cluster"] == many["buckets"][0]["cluster"]
+    assert many["buckets"][0]["groups"] == -(-200 // (256 // many["buckets"][0]["cluster"]))
+
+
+def test_resident_can_be_disabled(m):
+    info = describe(m, workloads.WORKLOADS["fused_74x24x10240"], resident_max_m=-1)
+    assert info["buckets"][0]["path"] == "stream"
+
+
+def test_3d_slices_and_orientation(m):
+    d = m.make_descs([(3, 50, 20), (20, 50), (50, 20)], ["f32"] * 3, ["f32"] * 3)
+    info = m.info_dict(m.muon_plan_describe(d, m.make_opts(resident_max_m=-1)))
+    assert info["n_matrices"] == 5
+    assert bucket_keys(info) == [(20, 50, 5, 4, "stream")]
+
+
+def expect_error(m, code, shapes, pd=None, gd=None, **opts):
+    d = m.make_descs(shapes, pd or ["f32"] * len(shapes), gd or ["f32"] * len(shapes))
+    with pytest.raises(m.MuonError) as ei:
+        m.muon_plan_describe(d, m.make_opts(**opts))
+    assert ei.value.code == code, m.muon_last_error()
+    assert m.muon_last_error()
+
+
+def test_argument_errors(m):
+    INV, UNS, OOM = 1, 2, 4
+    expect_error(m, INV, [(5,)])
+    expect_error(m, INV, [(2, 2, 2, 2)])
+    expect_error(m, INV, [(0, 4)])
+    expect_error(m, INV, [(4, -1)])
+    expect_error(m, INV, [(1 << 31, 2)])
+    expect_error(m, INV, [(4, 4)], pd=[7])
+    expect_error(m, INV, [(4, 4)], gd=[9])
+    expect_error(m, INV, [(4, 4)], mode=5)
+    expect_error(m, INV, [(4, 4)], eps=-1.0)
+    expect_error(m, INV, [(4, 4)], eps=float("nan"))
+    expect_error(m, INV, [(4, 4)], max_ns_steps=-2)
+    expect_error(m, INV, [(4, 4)], resident_max_m=33)
+    expect_error(m, OOM, [(256, 256)], workspace_limit=1024)
+    expect_error(m, UNS, [(40 + i, 100) for i in range(65)])
+    expect_error(m, UNS, [(24, 10_000_000)], n_cu=2)
+
+
+def test_zero_params_and_null_pointers(m):
+    lib = m.load_library()
+    info = m.PlanInfo()
+    assert lib.muon_plan_describe(m.make_descs([(4, 4)]), 0, None, ctypes.byref(info)) == 1
+    assert lib.muon_plan_describe(None, 1, None, ctypes.byref(info)) == 1
+    assert lib.muon_plan_describe(m.make_descs([(4, 4)]), 1, None, None) == 1
+
+
+def test_create_validates_before_touching_the_device(m):
+    lib = m.load_library()
+    h = ctypes.c_void_p()
+    d = m.make_descs([(2, 2, 2, 2)])
+    assert lib.muon_plan_create(d, 1, None, ctypes.byref(h)) == 1
+    assert not h.value
+    assert lib.muon_plan_create(d, 1, None, None) == 1
+
+
+def test_invalid_handles(m):
+    lib = m.load_library()
+    P = ctypes.c_void_p * 1
+    assert lib.muon_plan_destroy(None) == 0
+    assert lib.muon_step(None, P(1), P(1), P(1), 0.1, 0.9, 5, 1.0, 0.0, 0.0, None) == 1
+    assert lib.muon_plan_query(None, ctypes.byref(m.PlanInfo())) == 1
+    bogus = ctypes.create_string_buffer(64)
+    assert lib.muon_step(ctypes.cast(bogus, ctypes.c_void_p), P(1), P(1), P(1), 0.1, 0.9, 5, 1.0, 0.0, 0.0,
+                         None) == 1
+    assert lib.muon_plan_status(None, None) == 1
+
+
+def test_default_opts(m):
+    o = m.muon_default_opts()
+    assert o.mode == m.MUON_MODE_BF16_MFMA and abs(o.eps - 1e-7) < 1e-12 and o.max_ns_steps == 16
+    assert o.use_graph == 0 and o.timing == 0 and o.workspace_limit == 0
+
+
+def test_workspace_grows_with_batch(m):
+    a = m.info_dict(m.muon_plan_describe(m.make_descs([(100, 300)] * 2), None))
+    b = m.info_dict(m.muon_plan_describe(m.make_descs([(100, 300)] * 4), None))
+    assert b["workspace_bytes"] > a["workspace_bytes"]
