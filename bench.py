@@ -167,19 +167,24 @@ def main():
     dominant = max(kernel_ms, key=lambda k: kernel_ms[k][0])
     dom_ms_per_launch = kernel_ms[dominant][0] / max(1, kernel_ms[dominant][1])
 
-    if dominant == "resident":
-        # Compulsory bytes of the resident buckets; X never leaves the chip.
-        res_bytes = 0.0
-        for p in wl.params:
-            r, c = p.shape[-2:]
-            if min(r, c) <= 32:
-                e = 1
-                for d in p.shape:
-                    e *= d
-                res_bytes += e * (elem_bytes(p.grad_dtype) + 8 + 2 * elem_bytes(p.param_dtype))
-        per_launch = res_bytes / max(1, kernel_ms[dominant][1])
+    # Algorithmic bytes of the skinny-path kernels (per element of their slices):
+    # skinny_gram reads G and M and writes M; skinny_apply reads M and W and writes W.
+    skinny_elems = 0.0
+    skinny_gram_b = skinny_apply_b = 0.0
+    for p in wl.params:
+        r, c = p.shape[-2:]
+        if min(r, c) <= 32:
+            e = 1
+            for dd in p.shape:
+                e *= dd
+            skinny_elems += e
+            skinny_gram_b += e * (elem_bytes(p.grad_dtype) + 8)
+            skinny_apply_b += e * (4 + 2 * elem_bytes(p.param_dtype))
+    if dominant in ("skinny_gram", "skinny_apply"):
+        nbytes = skinny_gram_b if dominant == "skinny_gram" else skinny_apply_b
+        per_launch = nbytes / max(1, kernel_ms[dominant][1])
         achieved = per_launch / (dom_ms_per_launch * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "k_resident", "achieved": round(achieved, 1),
+        roof = {"bound": "hbm", "kernel": "k_" + dominant, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None, "algorithmic_bytes_per_launch": per_launch,
                 "avg_launch_ms": round(dom_ms_per_launch, 5)}
@@ -198,6 +203,9 @@ def main():
         roof = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
                 "algorithmic_flops_per_launch": per_launch, "avg_launch_ms": round(dom_ms_per_launch, 5)}
+    if skinny_elems and "skinny_gram" in kernel_ms and "skinny_apply" in kernel_ms:
+        sk_ms = kernel_ms["skinny_gram"][0] + kernel_ms["skinny_apply"][0]
+        roof["skinny_pair_gbs"] = round((skinny_gram_b + skinny_apply_b) / (sk_ms * 1e-3) / 1e9, 1)
 
     out = {
         "metric": "Muon step matrices/s + effective TFLOP/s (frac of MFMA/HBM roofline), 1 GPU",

@@ -96,15 +96,22 @@ typedef struct {
   float eps;               /* normaliser offset, default 1e-7                                 */
   int32_t max_ns_steps;    /* muon_step rejects ns_steps > this; default 16                   */
   uint64_t workspace_limit;/* bytes; 0 = no limit.  Plans needing more fail with MUON_ERR_OOM */
-  int32_t resident_max_m;  /* slices with m <= this (<= 32) run the single-kernel resident
-                              path; 0 = default 32, -1 = never (every slice streams)          */
+  int32_t skinny_max_m;    /* slices with m <= this (<= 32) run the skinny path, which does
+                              the rounds in the m x m Gram space; 0 = default 32,
+                              -1 = never (every slice takes the streamed path)                */
   int32_t timing;          /* 1: time each kernel class with HIP events (muon_plan_timings)   */
   int32_t n_cu;            /* compute units to plan for; 0 = the device's (describe: 256)     */
   int32_t reserved[3];
 } muon_plan_opts_t;
 
-/* How a bucket of same-shape slices is executed. */
-typedef enum { MUON_PATH_RESIDENT = 0, MUON_PATH_STREAM = 1 } muon_path_t;
+/* How a bucket of same-shape slices is executed.
+ *  MUON_PATH_SKINNY: m <= 32.  One pass forms the first Gram matrix (split over
+ *    256-column chunks), the rounds run on m x m matrices (each round's P is a
+ *    polynomial in A, so A' = P^2 A and X_k = P_{k-1}..P_0 X_0), and one pass
+ *    applies X_k = Q X_0 and updates W.  Three launches per bucket.
+ *  MUON_PATH_STREAM: every round forms A = X X^T, P = bA + cA^2 and
+ *    X <- aX + PX with batched matrix-core products over the bucket. */
+typedef enum { MUON_PATH_SKINNY = 0, MUON_PATH_STREAM = 1 } muon_path_t;
 
 #define MUON_MAX_BUCKETS 64
 
@@ -113,9 +120,8 @@ typedef struct {
   int32_t count;           /* slices in the bucket                                 */
   int32_t n_transposed;    /* of which stored as [n, m] (R > C)                    */
   int32_t path;            /* muon_path_t                                          */
-  int32_t cluster;         /* resident: workgroups cooperating on one slice        */
-  int32_t groups;          /* resident: cooperative launches the bucket needs      */
-  int32_t reserved;
+  int32_t chunks;          /* skinny: 256-column chunks per slice (workgroups)     */
+  int32_t reserved[2];
   uint64_t workspace_bytes;/* this bucket's share of the workspace                 */
 } muon_bucket_info_t;
 
@@ -161,15 +167,17 @@ int muon_step(muon_plan_t plan, void* const* params, const void* const* grads,
               void* const* momentum, float lr, float beta, int32_t ns_steps,
               float a, float b, float c, void* stream);
 
-/* Synchronise the plan's device and read its device-side error word
- * (nonzero: a cooperative wait in the resident kernel gave up).  Clears it.
- * Returns MUON_ERR_DEVICE when the word was nonzero. */
+/* Synchronise the plan's device and read its device-side error word, then
+ * clear it.  Bit 0: some slice's momentum had a non-finite norm (its update
+ * is then not finite either).  Returns MUON_ERR_DEVICE when the word was
+ * nonzero. */
 int muon_plan_status(muon_plan_t plan, uint32_t* device_error);
 
 /* Kernel-class timings collected since the last call (opts.timing = 1):
  * out_ms[i] = total milliseconds, out_count[i] = launches, for i < n_out and
- * the classes 0 resident, 1 momentum, 2 norm, 3 gram, 4 poly, 5 apply,
- * 6 update.  Synchronises.  Returns the number of classes. */
+ * the classes 0 skinny_gram, 1 skinny_poly, 2 skinny_apply, 3 momentum,
+ * 4 norm, 5 gram, 6 poly, 7 apply, 8 update.  Synchronises.  Returns the
+ * number of classes. */
 int muon_plan_timings(muon_plan_t plan, double* out_ms, int64_t* out_count, int32_t n_out);
 
 /* Release the plan and its device memory.  NULL is a no-op. */

@@ -26,11 +26,12 @@ MUON_F32 = 0
 MUON_BF16 = 1
 MUON_MODE_FP32 = 0
 MUON_MODE_BF16_MFMA = 1
-MUON_PATH_RESIDENT = 0
+MUON_PATH_SKINNY = 0
 MUON_PATH_STREAM = 1
 MUON_MAX_BUCKETS = 64
 
-KERNEL_CLASSES = ("resident", "momentum", "norm", "gram", "poly", "apply", "update")
+KERNEL_CLASSES = ("skinny_gram", "skinny_poly", "skinny_apply", "momentum", "norm", "gram", "poly", "apply",
+                  "update")
 EXPORTED = ("muon_default_opts", "muon_plan_create", "muon_plan_describe", "muon_plan_query",
             "muon_step", "muon_plan_status", "muon_plan_timings", "muon_plan_destroy",
             "muon_last_error")
@@ -45,15 +46,15 @@ class ParamDesc(ctypes.Structure):
 class PlanOpts(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("use_graph", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("max_ns_steps", ctypes.c_int32), ("workspace_limit", ctypes.c_uint64),
-                ("resident_max_m", ctypes.c_int32), ("timing", ctypes.c_int32),
+                ("skinny_max_m", ctypes.c_int32), ("timing", ctypes.c_int32),
                 ("n_cu", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
 
 class BucketInfo(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("count", ctypes.c_int32),
                 ("n_transposed", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("cluster", ctypes.c_int32), ("groups", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64)]
+                ("chunks", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2),
+                ("workspace_bytes", ctypes.c_uint64)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -137,14 +138,14 @@ def make_descs(shapes, param_dtypes=None, grad_dtypes=None):
 
 
 def make_opts(mode="bf16", use_graph=False, eps=1e-7, max_ns_steps=16, workspace_limit=0,
-              resident_max_m=0, timing=False, n_cu=0) -> PlanOpts:
+              skinny_max_m=0, timing=False, n_cu=0) -> PlanOpts:
     o = muon_default_opts()
     o.mode = {"fp32": MUON_MODE_FP32, "bf16": MUON_MODE_BF16_MFMA}.get(mode, mode)
     o.use_graph = int(bool(use_graph))
     o.eps = eps
     o.max_ns_steps = max_ns_steps
     o.workspace_limit = workspace_limit
-    o.resident_max_m = resident_max_m
+    o.skinny_max_m = skinny_max_m
     o.timing = int(bool(timing))
     o.n_cu = n_cu
     return o
@@ -207,8 +208,8 @@ def info_dict(info: PlanInfo) -> dict:
         "launches_fixed": info.launches_fixed, "launches_per_ns": info.launches_per_ns,
         "buckets": [
             {"m": b.m, "n": b.n, "count": b.count, "n_transposed": b.n_transposed,
-             "path": "resident" if b.path == MUON_PATH_RESIDENT else "stream",
-             "cluster": b.cluster, "groups": b.groups, "workspace_bytes": int(b.workspace_bytes)}
+             "path": "skinny" if b.path == MUON_PATH_SKINNY else "stream",
+             "chunks": b.chunks, "workspace_bytes": int(b.workspace_bytes)}
             for b in info.buckets[: info.n_buckets]],
     }
 
@@ -243,7 +244,7 @@ class MuonPlan:
     """
 
     def __init__(self, params, grad_dtypes=None, mode: str = "bf16", use_graph=False, eps=1e-7,
-                 timing=False, resident_max_m=0, workspace_limit=0, max_ns_steps=16):
+                 timing=False, skinny_max_m=0, workspace_limit=0, max_ns_steps=16):
         import torch
         self.params = list(params)
         if not self.params:
@@ -259,7 +260,7 @@ class MuonPlan:
                                 [_dtype_code(p) for p in self.params],
                                 [MUON_BF16 if g == torch.bfloat16 or g == "bf16" else MUON_F32 for g in gd])
         self.opts = make_opts(mode=mode, use_graph=use_graph, eps=eps, timing=timing,
-                              resident_max_m=resident_max_m, workspace_limit=workspace_limit,
+                              skinny_max_m=skinny_max_m, workspace_limit=workspace_limit,
                               max_ns_steps=max_ns_steps)
         self.device = dev
         with torch.cuda.device(dev):

@@ -32,8 +32,6 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr uint32_t kPlanMagic = 0x4d554f4eu;  // "MUON"
-// Polls of a resident-kernel wait before it gives up (about 0.2 s).
-constexpr uint32_t kSpinLimit = 4u << 20;
 
 struct TimedLaunch {
   int cls;
@@ -96,34 +94,27 @@ hipError_t timed(muon_plan_t plan, int cls, hipStream_t s, bool timing, F&& laun
   return e;
 }
 
-hipError_t enqueue_resident(muon_plan_t plan, const muon::BucketPlan& bp, int ns, hipStream_t s,
-                            bool timing) {
+hipError_t enqueue_skinny(muon_plan_t plan, const muon::BucketPlan& bp, hipStream_t s, bool timing) {
   const muon::Plan& p = plan->p;
-  for (int g = 0; g < bp.groups; ++g) {
-    muon::ResidentLaunch L;
-    L.mats = at<muon::DevMat>(plan, bp.off_mats);
-    L.ptrs = at<muon::PtrEntry>(plan, p.off_ptrs);
-    L.sc = at<muon::DevScalars>(plan, p.off_scalars);
-    L.gram_parts = at<float>(plan, bp.off_gram);
-    L.sq_parts = at<double>(plan, bp.off_sqp);
-    L.ctrs = at<uint32_t>(plan, bp.off_ctr);
-    L.err = at<uint32_t>(plan, p.off_err);
-    L.m = (int)bp.m;
-    L.n = (int)bp.n;
-    L.cluster = bp.cluster;
-    L.tiles_per_wg = bp.tiles_per_wg;
-    L.tpw = bp.tpw;
-    L.count = (int)bp.slices.size();
-    L.mat_base = g * bp.mats_per_group;
-    const int left = (int)bp.slices.size() - L.mat_base;
-    L.n_mats = left < bp.mats_per_group ? left : bp.mats_per_group;
-    L.ns_steps = ns;
-    L.spin_limit = kSpinLimit;
-    L.bf16 = p.mode == MUON_MODE_BF16_MFMA;
-    hipError_t e = timed(plan, muon::kClsResident, s, timing, [&] { return muon::launch_resident(L, s); });
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  muon::SkinnyLaunch L;
+  L.mats = at<muon::DevMat>(plan, bp.off_mats);
+  L.ptrs = at<muon::PtrEntry>(plan, p.off_ptrs);
+  L.sc = at<muon::DevScalars>(plan, p.off_scalars);
+  L.gram_parts = at<double>(plan, bp.off_gram);
+  L.sq_parts = at<float>(plan, bp.off_sqp);
+  L.qs = at<float>(plan, bp.off_qs);
+  L.err = at<uint32_t>(plan, p.off_err);
+  L.m = (int)bp.m;
+  L.n = (int)bp.n;
+  L.n_chunks = bp.n_chunks;
+  L.count = (int)bp.slices.size();
+  L.bf16 = p.mode == MUON_MODE_BF16_MFMA;
+  hipError_t e;
+  if ((e = timed(plan, muon::kClsSkinnyGram, s, timing, [&] { return muon::launch_skinny_gram(L, s); })) != hipSuccess)
+    return e;
+  if ((e = timed(plan, muon::kClsSkinnyPoly, s, timing, [&] { return muon::launch_skinny_poly(L, s); })) != hipSuccess)
+    return e;
+  return timed(plan, muon::kClsSkinnyApply, s, timing, [&] { return muon::launch_skinny_apply(L, s); });
 }
 
 hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, hipStream_t s,
@@ -193,19 +184,16 @@ hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, 
   return hipSuccess;
 }
 
-hipError_t enqueue_streamed_buckets(muon_plan_t plan, int ns, hipStream_t s, bool timing) {
+// Every bucket's launches, in plan order.  The number of Newton-Schulz
+// rounds is read by the skinny kernels from the scalar block and fixes the
+// streamed launch sequence.
+hipError_t enqueue_buckets(muon_plan_t plan, int ns, hipStream_t s, bool timing) {
   for (const muon::BucketPlan& bp : plan->p.buckets) {
-    if (bp.path != MUON_PATH_STREAM) continue;
-    hipError_t e = enqueue_stream(plan, bp, ns, s, timing);
+    hipError_t e = bp.path == MUON_PATH_SKINNY ? enqueue_skinny(plan, bp, s, timing)
+                                               : enqueue_stream(plan, bp, ns, s, timing);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
-}
-
-bool has_streamed(const muon::Plan& p) {
-  for (const auto& b : p.buckets)
-    if (b.path == MUON_PATH_STREAM) return true;
-  return false;
 }
 
 void drop_graph(muon_plan_t plan) {
@@ -231,7 +219,7 @@ int muon_plan_describe(const muon_param_desc_t* descs, int32_t n_params, const m
   const int n_cu = (opts && opts->n_cu > 0) ? opts->n_cu : 256;
   muon::Plan p;
   std::string err;
-  const int rc = muon::make_plan(descs, n_params, opts, n_cu, 1, &p, &err);
+  const int rc = muon::make_plan(descs, n_params, opts, n_cu, &p, &err);
   if (rc != MUON_OK) return fail(rc, "%s", err.c_str());
   muon::fill_info(p, info);
   g_last_error.clear();
@@ -246,7 +234,7 @@ int muon_plan_create(const muon_param_desc_t* descs, int32_t n_params, const muo
   {
     muon::Plan probe;
     std::string err;
-    const int rc = muon::make_plan(descs, n_params, opts, 256, 1, &probe, &err);
+    const int rc = muon::make_plan(descs, n_params, opts, 256, &probe, &err);
     if (rc != MUON_OK && rc != MUON_ERR_OOM) return fail(rc, "%s", err.c_str());
   }
   int dev = 0, n_cu = 0;
@@ -260,19 +248,10 @@ int muon_plan_create(const muon_param_desc_t* descs, int32_t n_params, const muo
   if (!plan) return fail(MUON_ERR_OOM, "host allocation failed");
   plan->device = dev;
   std::string err;
-  int rc = muon::make_plan(descs, n_params, opts, n_cu, 1, &plan->p, &err);
+  int rc = muon::make_plan(descs, n_params, opts, n_cu, &plan->p, &err);
   if (rc != MUON_OK) {
     delete plan;
     return fail(rc, "%s", err.c_str());
-  }
-  // Every resident variant in use must fit at least one workgroup per CU,
-  // which is what the cooperative launches were sized for.
-  for (const auto& bp : plan->p.buckets) {
-    if (bp.path != MUON_PATH_RESIDENT) continue;
-    if (muon::resident_occupancy(bp.tpw, plan->p.mode == MUON_MODE_BF16_MFMA) < 1) {
-      delete plan;
-      return fail(MUON_ERR_UNSUPPORTED, "resident kernel (%d tiles per wave) does not fit a CU", bp.tpw);
-    }
   }
   const muon::Plan& p = plan->p;
   e = hipMalloc(&plan->ws, p.ws_total);
@@ -381,29 +360,21 @@ int muon_step(muon_plan_t plan, void* const* params, const void* const* grads, v
   v.eps = p.eps;
   v.ns_steps = ns_steps;
   v.pad = 0;
-  e = muon::launch_prologue(at<muon::DevScalars>(plan, p.off_scalars), v,
-                            at<uint32_t>(plan, p.off_ctrs), p.n_resident_slices, s);
+  e = muon::launch_prologue(at<muon::DevScalars>(plan, p.off_scalars), v, s);
   if (e != hipSuccess) return hip_fail(e, "prologue launch");
 
   const bool timing = p.timing != 0;
-  for (const auto& bp : p.buckets) {
-    if (bp.path != MUON_PATH_RESIDENT) continue;
-    e = enqueue_resident(plan, bp, ns_steps, s, timing);
-    if (e != hipSuccess) return hip_fail(e, "resident launch");
-  }
-  if (!has_streamed(p)) return MUON_OK;
-
   const bool graph = p.use_graph && !timing && s != nullptr;
   if (!graph) {
-    e = enqueue_streamed_buckets(plan, ns_steps, s, timing);
-    if (e != hipSuccess) return hip_fail(e, "streamed launch");
+    e = enqueue_buckets(plan, ns_steps, s, timing);
+    if (e != hipSuccess) return hip_fail(e, "launch");
     return MUON_OK;
   }
   if (plan->gexec == nullptr || plan->graph_ns != ns_steps || plan->graph_stream != s) {
     drop_graph(plan);
     e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
-    hipError_t le = enqueue_streamed_buckets(plan, ns_steps, s, false);
+    hipError_t le = enqueue_buckets(plan, ns_steps, s, false);
     hipGraph_t g = nullptr;
     e = hipStreamEndCapture(s, &g);
     if (le != hipSuccess) {
@@ -435,7 +406,7 @@ int muon_plan_status(muon_plan_t plan, uint32_t* device_error) {
   if (e == hipSuccess && word != 0) e = hipMemset(plan->ws + plan->p.off_err, 0, sizeof word);
   if (e != hipSuccess) return hip_fail(e, "reading the device error word");
   if (device_error) *device_error = word;
-  if (word != 0) return fail(MUON_ERR_DEVICE, "device error word 0x%x (a resident-kernel wait gave up)", word);
+  if (word != 0) return fail(MUON_ERR_DEVICE, "device error word 0x%x (bit 0: non-finite momentum norm)", word);
   return MUON_OK;
 }
 

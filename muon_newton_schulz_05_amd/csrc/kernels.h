@@ -7,30 +7,24 @@
 
 namespace muon {
 
-// Writes the step's scalars and clears the resident arrival counters.
-hipError_t launch_prologue(DevScalars* dst, const DevScalars& v, uint32_t* ctrs, int n_ctrs,
-                           hipStream_t s);
+// Writes the step's scalars.
+hipError_t launch_prologue(DevScalars* dst, const DevScalars& v, hipStream_t s);
 
-// ---------------------------------------------------------------- resident
-struct ResidentLaunch {
+// ---------------------------------------------------------------- skinny (m <= 32)
+struct SkinnyLaunch {
   const DevMat* mats;     // bucket's slice table
   const PtrEntry* ptrs;
   const DevScalars* sc;
-  float* gram_parts;      // [2][count][cluster][32*32] (round parity)
-  double* sq_parts;       // [count][cluster]
-  uint32_t* ctrs;         // [count]
-  uint32_t* err;
-  int m, n;
-  int cluster, tiles_per_wg, tpw;
-  int count;              // slices in the bucket
-  int mat_base, n_mats;   // slices of this cooperative launch
-  int ns_steps;
-  uint32_t spin_limit;
+  double* gram_parts;     // [count][n_chunks][m*m]
+  float* sq_parts;        // [count][n_chunks]
+  float* qs;              // [count][32*32]: s * Q
+  uint32_t* err;          // device error word
+  int m, n, n_chunks, count;
   int bf16;               // 1: bf16 matrix-core mode, 0: fp32 mode
 };
-hipError_t launch_resident(const ResidentLaunch& a, hipStream_t s);
-// Co-resident workgroups per CU of the resident kernel variant (0 on error).
-int resident_occupancy(int tpw, int bf16);
+hipError_t launch_skinny_gram(const SkinnyLaunch& a, hipStream_t s);
+hipError_t launch_skinny_poly(const SkinnyLaunch& a, hipStream_t s);
+hipError_t launch_skinny_apply(const SkinnyLaunch& a, hipStream_t s);
 
 // ---------------------------------------------------------------- streamed
 struct MomentumLaunch {

@@ -7,13 +7,16 @@
 
 namespace muon {
 
-constexpr int kMaxResidentM = 32;     // resident path: one 32-row MFMA tile holds all of m
-constexpr int kResidentWaves = 8;     // waves per resident workgroup (512 threads)
+constexpr int kMaxSkinnyM = 32;       // skinny path: one 32-row MFMA tile holds all of m
+constexpr int kSkinnyChunk = 256;     // skinny path: columns per workgroup (fixed by n alone)
 constexpr int kStreamPad = 128;       // streamed workspace dims are padded to this
 constexpr int kMomTile = 64;          // momentum kernel tile (oriented 64 x 64)
 
-enum KernelClass { kClsResident = 0, kClsMomentum, kClsNorm, kClsGram, kClsPoly, kClsApply,
-                   kClsUpdate, kNumClasses };
+enum KernelClass { kClsSkinnyGram = 0, kClsSkinnyPoly, kClsSkinnyApply, kClsMomentum, kClsNorm,
+                   kClsGram, kClsPoly, kClsApply, kClsUpdate, kNumClasses };
+
+// Bits of the plan's device error word.
+constexpr uint32_t kErrNonFinite = 1u;  // a slice's momentum norm was not finite
 
 // Scalars of one step, written to device memory by the prologue kernel.
 struct DevScalars {

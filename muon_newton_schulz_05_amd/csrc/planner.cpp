@@ -14,10 +14,6 @@ namespace {
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-// Tiles-per-wave values the resident kernel is compiled for.
-const int kTpwBf16[] = {1, 2, 4, 8, 14};
-const int kTpwF32[] = {1, 2, 4, 8};
-
 struct Alloc {
   uint64_t top = 0;
   uint64_t take(uint64_t bytes) {
@@ -29,19 +25,6 @@ struct Alloc {
 
 }  // namespace
 
-int resident_tpw_max(int mode) { return mode == MUON_MODE_FP32 ? 8 : 14; }
-
-int resident_tpw_pick(int mode, int need) {
-  if (mode == MUON_MODE_FP32) {
-    for (int t : kTpwF32)
-      if (t >= need) return t;
-  } else {
-    for (int t : kTpwBf16)
-      if (t >= need) return t;
-  }
-  return 0;
-}
-
 void default_opts(muon_plan_opts_t* o) {
   std::memset(o, 0, sizeof(*o));
   o->mode = MUON_MODE_BF16_MFMA;
@@ -49,13 +32,13 @@ void default_opts(muon_plan_opts_t* o) {
   o->eps = 1e-7f;
   o->max_ns_steps = 16;
   o->workspace_limit = 0;
-  o->resident_max_m = 0;
+  o->skinny_max_m = 0;
   o->timing = 0;
   o->n_cu = 0;
 }
 
 int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_opts_t* opts_in,
-              int n_cu, int occupancy, Plan* out, std::string* err) {
+              int n_cu, Plan* out, std::string* err) {
   char buf[256];
   if (descs == nullptr || out == nullptr) {
     *err = "null descriptor array or output";
@@ -80,12 +63,12 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
     *err = "max_ns_steps must be in [0, 1000]";
     return MUON_ERR_INVALID_ARGUMENT;
   }
-  if (opts.resident_max_m < -1 || opts.resident_max_m > kMaxResidentM) {
-    std::snprintf(buf, sizeof buf, "resident_max_m must be -1, 0 or in [1, %d]", kMaxResidentM);
+  if (opts.skinny_max_m < -1 || opts.skinny_max_m > kMaxSkinnyM) {
+    std::snprintf(buf, sizeof buf, "skinny_max_m must be -1, 0 or in [1, %d]", kMaxSkinnyM);
     *err = buf;
     return MUON_ERR_INVALID_ARGUMENT;
   }
-  if (n_cu <= 0 || occupancy <= 0) {
+  if (n_cu <= 0) {
     *err = "device description has no compute units";
     return MUON_ERR_INVALID_ARGUMENT;
   }
@@ -95,12 +78,11 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
   p.eps = opts.eps;
   p.max_ns_steps = opts.max_ns_steps;
   p.workspace_limit = opts.workspace_limit;
-  p.resident_max_m = opts.resident_max_m == 0 ? kMaxResidentM
-                     : opts.resident_max_m < 0 ? 0 : opts.resident_max_m;
+  p.skinny_max_m = opts.skinny_max_m == 0 ? kMaxSkinnyM
+                   : opts.skinny_max_m < 0 ? 0 : opts.skinny_max_m;
   p.timing = opts.timing ? 1 : 0;
   p.use_graph = opts.use_graph ? 1 : 0;
   p.n_cu = n_cu;
-  p.resident_occupancy = occupancy;
   p.n_params = n_params;
   p.descs.assign(descs, descs + n_params);
 
@@ -168,7 +150,7 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
       BucketPlan bp;
       bp.m = s.m;
       bp.n = s.n;
-      bp.path = s.m <= p.resident_max_m ? MUON_PATH_RESIDENT : MUON_PATH_STREAM;
+      bp.path = s.m <= p.skinny_max_m ? MUON_PATH_SKINNY : MUON_PATH_STREAM;
       p.buckets.push_back(bp);
     } else {
       b = it->second;
@@ -189,25 +171,12 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
     const uint64_t cnt = bp.slices.size();
     bp.ws_begin = ws.take(0);
     bp.off_mats = ws.take(sizeof(DevMat) * cnt);
-    if (bp.path == MUON_PATH_RESIDENT) {
-      const int ntiles = (int)((bp.n + 31) / 32);
-      const int per_wg_max = kResidentWaves * resident_tpw_max(p.mode);
-      bp.cluster = (ntiles + per_wg_max - 1) / per_wg_max;
-      bp.tiles_per_wg = (ntiles + bp.cluster - 1) / bp.cluster;
-      bp.tpw = resident_tpw_pick(p.mode, (bp.tiles_per_wg + kResidentWaves - 1) / kResidentWaves);
-      const int capacity = p.n_cu * p.resident_occupancy;
-      if (bp.cluster > capacity) {
-        std::snprintf(buf, sizeof buf, "slice [%lld,%lld] needs %d co-resident workgroups, device has %d",
-                      (long long)bp.m, (long long)bp.n, bp.cluster, capacity);
-        *err = buf;
-        return MUON_ERR_UNSUPPORTED;
-      }
-      bp.mats_per_group = capacity / bp.cluster;
-      bp.groups = (int)((cnt + bp.mats_per_group - 1) / bp.mats_per_group);
-      bp.off_gram = ws.take(2 * cnt * bp.cluster * 1024 * sizeof(float));
-      bp.off_sqp = ws.take(cnt * bp.cluster * sizeof(double));
-      p.n_resident_slices += (int)cnt;
-      p.launches_fixed += bp.groups;
+    if (bp.path == MUON_PATH_SKINNY) {
+      bp.n_chunks = (int)((bp.n + kSkinnyChunk - 1) / kSkinnyChunk);
+      bp.off_gram = ws.take(cnt * bp.n_chunks * bp.m * bp.m * sizeof(double));
+      bp.off_sqp = ws.take(cnt * bp.n_chunks * sizeof(float));
+      bp.off_qs = ws.take(cnt * 1024 * sizeof(float));
+      p.launches_fixed += 3;  // momentum + Gram partials, polynomial, apply + update
     } else {
       bp.mp = round_up(bp.m, kStreamPad);
       bp.np = round_up(bp.n, kStreamPad);
@@ -229,17 +198,6 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
       p.launches_per_ns += 3;  // gram, poly, apply (the last apply also updates W)
     }
     bp.ws_bytes = ws.take(0) - bp.ws_begin;
-  }
-  // Arrival counters of all resident slices sit in one block so that the
-  // prologue clears them with a single store pass.
-  p.off_ctrs = ws.take(sizeof(uint32_t) * (uint64_t)(p.n_resident_slices > 0 ? p.n_resident_slices : 1));
-  {
-    uint64_t pos = p.off_ctrs;
-    for (BucketPlan& bp : p.buckets) {
-      if (bp.path != MUON_PATH_RESIDENT) continue;
-      bp.off_ctr = pos;
-      pos += sizeof(uint32_t) * bp.slices.size();
-    }
   }
   p.ws_total = align_up(ws.top, 256);
   if (p.workspace_limit != 0 && p.ws_total > p.workspace_limit) {
@@ -269,8 +227,7 @@ void fill_info(const Plan& p, muon_plan_info_t* info) {
     o.count = (int)b.slices.size();
     o.n_transposed = b.n_transposed;
     o.path = b.path;
-    o.cluster = b.cluster;
-    o.groups = b.groups;
+    o.chunks = b.n_chunks;
     o.workspace_bytes = b.ws_bytes;
   }
 }

@@ -29,13 +29,9 @@ struct BucketPlan {
   std::vector<int> slices;  // indices into Plan::slices, in plan order
   int n_transposed = 0;
 
-  // resident path
-  int cluster = 0;          // workgroups per slice
-  int tiles_per_wg = 0;     // 32-column tiles per workgroup
-  int tpw = 0;              // tiles per wave (kernel instantiation)
-  int mats_per_group = 0;   // slices per cooperative launch
-  int groups = 0;
-  uint64_t off_gram = 0, off_sqp = 0, off_ctr = 0;
+  // skinny path (m <= 32)
+  int n_chunks = 0;         // 512-column chunks per slice
+  uint64_t off_gram = 0, off_sqp = 0, off_qs = 0;
 
   // streamed path
   int64_t mp = 0, np = 0;   // padded dims
@@ -55,32 +51,25 @@ struct Plan {
   float eps = 1e-7f;
   int max_ns_steps = 16;
   uint64_t workspace_limit = 0;
-  int resident_max_m = kMaxResidentM;
+  int skinny_max_m = kMaxSkinnyM;
   int timing = 0, use_graph = 0;
   int n_cu = 256;
-  int resident_occupancy = 1;  // co-resident resident-kernel workgroups per CU
 
   int n_params = 0;
   std::vector<muon_param_desc_t> descs;
   std::vector<Slice> slices;
   std::vector<BucketPlan> buckets;
-  uint64_t off_scalars = 0, off_err = 0, off_ptrs = 0, off_ctrs = 0;
-  int n_resident_slices = 0;
+  uint64_t off_scalars = 0, off_err = 0, off_ptrs = 0;
   uint64_t ws_total = 0;
   int launches_fixed = 0, launches_per_ns = 0;
 };
 
-// Largest tiles-per-wave instantiation of the resident kernel for a mode.
-int resident_tpw_max(int mode);
-// Smallest instantiated tiles-per-wave >= need (0 if none).
-int resident_tpw_pick(int mode, int need);
-
 void default_opts(muon_plan_opts_t* o);
 
-// Validate and plan.  n_cu / occupancy describe the device (create) or the
-// assumed device (describe).  Returns a muon_status_t; *err gets a message.
+// Validate and plan.  n_cu describes the device (create) or the assumed
+// device (describe).  Returns a muon_status_t; *err gets a message.
 int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_opts_t* opts,
-              int n_cu, int resident_occupancy, Plan* out, std::string* err);
+              int n_cu, Plan* out, std::string* err);
 
 void fill_info(const Plan& p, muon_plan_info_t* info);
 

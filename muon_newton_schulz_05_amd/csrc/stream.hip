@@ -24,9 +24,8 @@ namespace muon {
 namespace {
 
 // ------------------------------------------------------------------ prologue
-__global__ void k_prologue(DevScalars* dst, DevScalars v, uint32_t* ctrs, int n) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *dst = v;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) ctrs[i] = 0;
+__global__ void k_prologue(DevScalars* dst, DevScalars v) {
+  if (threadIdx.x == 0) *dst = v;
 }
 
 // ------------------------------------------------------------------ momentum
@@ -355,10 +354,8 @@ hipError_t run_gemm(const GemmCore& c, const Epi& e, int64_t rows, int count, hi
 
 }  // namespace
 
-hipError_t launch_prologue(DevScalars* dst, const DevScalars& v, uint32_t* ctrs, int n_ctrs,
-                           hipStream_t s) {
-  const int blocks = n_ctrs > 0 ? (n_ctrs + 255) / 256 : 1;
-  hipLaunchKernelGGL(k_prologue, dim3(blocks < 64 ? blocks : 64), dim3(256), 0, s, dst, v, ctrs, n_ctrs);
+hipError_t launch_prologue(DevScalars* dst, const DevScalars& v, hipStream_t s) {
+  hipLaunchKernelGGL(k_prologue, dim3(1), dim3(64), 0, s, dst, v);
   return hipGetLastError();
 }
 

@@ -50,7 +50,7 @@ def gpu_step(params, grads, moms, *, mode, lr, beta, ns_steps, coeffs, steps=1, 
     for _ in range(steps):
         plan.step(g_dev, m_dev, lr=lr, beta=beta, ns_steps=ns_steps, coeffs=coeffs)
     torch.cuda.synchronize()
-    assert plan.status() == 0, "a resident-kernel wait timed out"
+    assert plan.status() == 0, "device error word set"
     plan.close()
     return [to_host(p) for p in p_dev], [to_host(m) for m in m_dev]
 

@@ -59,7 +59,7 @@ def test_single_fp32_128x256():
 @pytest.mark.parametrize("mode", ["bf16", "fp32"])
 @pytest.mark.parametrize("shape", [(24, 10240), (10240, 24), (24, 1000), (7, 100), (32, 33),
                                    (1, 64), (16, 5000), (3, 24, 777), (17, 4099)])
-def test_resident_shapes(shape, mode):
+def test_skinny_shapes(shape, mode):
     check([shape], mode)
 
 
@@ -238,4 +238,63 @@ def test_step_rejects_bad_arguments_without_side_effects():
                   *Q, s)
     torch.cuda.synchronize()
     assert not p[0].any() and not m[0].any()
+    plan.close()
+
+
+def _conditioned(shape, kind, seed):
+    """Float32 gradients with controlled singular values (stored as given)."""
+    rng = np.random.default_rng(seed)
+    r, c = shape
+    m = min(r, c)
+    u, _ = np.linalg.qr(rng.standard_normal((r, m)))
+    v, _ = np.linalg.qr(rng.standard_normal((c, m)))
+    if kind == "logspaced":
+        s = np.logspace(0, -4, m)
+        g = (u * s) @ v.T
+    else:  # rank one plus noise
+        g = np.outer(rng.standard_normal(r), rng.standard_normal(c)) + 1e-4 * rng.standard_normal((r, c))
+    return (g * 1e-2).astype(np.float32)
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+@pytest.mark.parametrize("kind", ["logspaced", "rank1_noise"])
+@pytest.mark.parametrize("shape", [(24, 3000), (3000, 24), (32, 700)])
+def test_skinny_ill_conditioned(shape, kind, mode):
+    """The Gram-space rounds keep float32 X0 (split hi/lo on the matrix cores
+    in bf16 mode), so singular values spread over four decades still meet
+    the bar."""
+    g = _conditioned(shape, kind, 71)
+    params, moms = [np.zeros(shape, np.float32)], [np.zeros(shape, np.float32)]
+    w_gpu, _ = gpu_step(params, [g], moms, mode=mode, lr=1.0, beta=0.9, ns_steps=5, coeffs=Q)
+    _, _, o_ref = oracle_step(params, [g], moms, lr=1.0, beta=0.9, ns_steps=5, coeffs=Q)
+    err = max(update_errors(w_gpu[0], params[0], 1.0, o_ref[0]))
+    print(f"{shape} {kind} {mode}: {err:.3e}")
+    assert err <= TOL[mode]
+
+
+@pytest.mark.parametrize("kind", ["logspaced", "rank1_noise"])
+def test_streamed_ill_conditioned_fp32(kind):
+    shape = (96, 700)
+    g = _conditioned(shape, kind, 72)
+    params, moms = [np.zeros(shape, np.float32)], [np.zeros(shape, np.float32)]
+    w_gpu, _ = gpu_step(params, [g], moms, mode="fp32", lr=1.0, beta=0.9, ns_steps=5, coeffs=Q)
+    _, _, o_ref = oracle_step(params, [g], moms, lr=1.0, beta=0.9, ns_steps=5, coeffs=Q)
+    err = max(update_errors(w_gpu[0], params[0], 1.0, o_ref[0]))
+    print(f"{shape} {kind} fp32: {err:.3e}")
+    assert err <= TOL["fp32"]
+
+
+def test_nonfinite_gradient_sets_device_error():
+    import torch
+
+    from muon_newton_schulz_05_amd import MuonPlan
+    p = [torch.zeros(24, 600, device="cuda:0")]
+    g = [torch.ones(24, 600, device="cuda:0")]
+    g[0][3, 7] = float("inf")
+    m = [torch.zeros(24, 600, device="cuda:0")]
+    plan = MuonPlan(p, mode="bf16")
+    plan.step(g, m, lr=0.02, beta=0.9, ns_steps=5)
+    torch.cuda.synchronize()
+    assert plan.status() & 1
+    assert plan.status() == 0  # reading clears the word
     plan.close()

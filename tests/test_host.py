@@ -84,10 +84,10 @@ def test_plans_of_the_workloads(m):
     W = workloads.WORKLOADS
     assert bucket_keys(describe(m, W["single_128x256"])) == [(128, 256, 1, 0, "stream")]
     info = describe(m, W["fused_74x24x10240"])
-    assert bucket_keys(info) == [(24, 10240, 74, 0, "resident")]
-    assert info["buckets"][0]["cluster"] == 3 and info["buckets"][0]["groups"] == 1
-    assert info["launches_fixed"] == 2 and info["launches_per_ns"] == 0   # prologue + one kernel
-    assert bucket_keys(describe(m, W["moe_experts"])) == [(24, 10240, 32, 0, "resident"),
+    assert bucket_keys(info) == [(24, 10240, 74, 0, "skinny")]
+    assert info["buckets"][0]["chunks"] == 40
+    assert info["launches_fixed"] == 4 and info["launches_per_ns"] == 0   # prologue + three kernels
+    assert bucket_keys(describe(m, W["moe_experts"])) == [(24, 10240, 32, 0, "skinny"),
                                                           (1408, 2048, 64, 0, "stream")]
     info = describe(m, W["dense_h4096_l8"])
     assert bucket_keys(info) == [(4096, 12288, 8, 0, "stream"), (4096, 4096, 8, 0, "stream"),
@@ -98,30 +98,24 @@ def test_plans_of_the_workloads(m):
     assert describe(m, W["large_share"])["n_matrices"] == 8
 
 
-def test_fp32_mode_uses_smaller_clusters(m):
-    info = describe(m, workloads.WORKLOADS["fused_74x24x10240"], mode="fp32")
-    b = info["buckets"][0]
-    assert b["path"] == "resident" and b["cluster"] * 64 >= 320 and b["groups"] >= 1
-    assert b["count"] == 74
-
-
-def test_cluster_depends_on_shape_not_batch(m):
-    """Per-slice work split must not depend on the batch size (bitwise fusion)."""
+def test_chunks_depend_on_shape_not_batch(m):
+    """A slice's work split must not depend on the batch size (bitwise fusion)."""
     one = m.info_dict(m.muon_plan_describe(m.make_descs([(24, 10240)], ["f32"], ["bf16"]), m.make_opts()))
     many = m.info_dict(m.muon_plan_describe(m.make_descs([(24, 10240)] * 200, ["f32"] * 200, ["bf16"] * 200),
                                             m.make_opts()))
-    assert one["buckets"][0]["cluster"] == many["buckets"][0]["cluster"]
-    assert many["buckets"][0]["groups"] == -(-200 // (256 // many["buckets"][0]["cluster"]))
+    assert one["buckets"][0]["chunks"] == many["buckets"][0]["chunks"] == 40
+    fp32 = describe(m, workloads.WORKLOADS["fused_74x24x10240"], mode="fp32")
+    assert fp32["buckets"][0]["chunks"] == 40 and fp32["buckets"][0]["path"] == "skinny"
 
 
-def test_resident_can_be_disabled(m):
-    info = describe(m, workloads.WORKLOADS["fused_74x24x10240"], resident_max_m=-1)
+def test_skinny_path_can_be_disabled(m):
+    info = describe(m, workloads.WORKLOADS["fused_74x24x10240"], skinny_max_m=-1)
     assert info["buckets"][0]["path"] == "stream"
 
 
 def test_3d_slices_and_orientation(m):
     d = m.make_descs([(3, 50, 20), (20, 50), (50, 20)], ["f32"] * 3, ["f32"] * 3)
-    info = m.info_dict(m.muon_plan_describe(d, m.make_opts(resident_max_m=-1)))
+    info = m.info_dict(m.muon_plan_describe(d, m.make_opts(skinny_max_m=-1)))
     assert info["n_matrices"] == 5
     assert bucket_keys(info) == [(20, 50, 5, 4, "stream")]
 
@@ -147,10 +141,9 @@ def test_argument_errors(m):
     expect_error(m, INV, [(4, 4)], eps=-1.0)
     expect_error(m, INV, [(4, 4)], eps=float("nan"))
     expect_error(m, INV, [(4, 4)], max_ns_steps=-2)
-    expect_error(m, INV, [(4, 4)], resident_max_m=33)
+    expect_error(m, INV, [(4, 4)], skinny_max_m=33)
     expect_error(m, OOM, [(256, 256)], workspace_limit=1024)
     expect_error(m, UNS, [(40 + i, 100) for i in range(65)])
-    expect_error(m, UNS, [(24, 10_000_000)], n_cu=2)
 
 
 def test_zero_params_and_null_pointers(m):
