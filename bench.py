@@ -62,6 +62,78 @@ def make_gpu_inputs(wl: workloads.Workload, dev):
     return params, grads, moms
 
 
+KERNEL_SOURCES = {
+    "k_skinny_gram": ("skinny.hip", "device_common.h", "kernels.h", "layout.h"),
+    "k_skinny_apply": ("skinny.hip", "device_common.h", "kernels.h", "layout.h"),
+}
+
+
+def source_hash(files) -> str:
+    """sha256 of the `sha256sum` listing of a kernel's source files (the form
+    recorded beside the counter figures in profiles/)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "muon_newton_schulz_05_amd", "csrc")
+    lines = []
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            lines.append(f"{hashlib.sha256(fh.read()).hexdigest()}  muon_newton_schulz_05_amd/csrc/{f}\n")
+    return hashlib.sha256("".join(lines).encode()).hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE summaries
+    under profiles/, or None when none was taken on the current source."""
+    files = KERNEL_SOURCES.get(kernel)
+    pdir = os.path.join(ROOT, "profiles")
+    if not files or not os.path.isdir(pdir):
+        return None
+    want = source_hash(files)
+    for name in sorted(os.listdir(pdir)):
+        with open(os.path.join(pdir, name)) as fh:
+            for line in fh:
+                f = line.split()
+                if len(f) == 5 and f[0] == "traffic" and f[1] == kernel and f[2] == workload and f[3] == want:
+                    return float(f[4])
+    return None
+
+
+def measure_ceilings(dev, copy_mib: int = 1024, reps: int = 20, gemm: bool = True):
+    """Measured ceilings on this GPU: a plain device-to-device copy (torch's
+    copy kernel, read + write bytes counted) and a library bf16 GEMM
+    (torch.matmul, 8192^3, hipBLASLt)."""
+    import torch
+    n = copy_mib * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * n * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    out = {"copy_gbs": round(copy_gbs, 1), "copy_bytes_per_launch": 2 * n * 4}
+    if not gemm:
+        return out
+    k = 8192
+    a = torch.randn(k, k, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(k, k, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 2.0 * k ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    out.update(library_bf16_gemm_tflops=round(gemm_tf, 1), library_gemm_shape=[k, k, k])
+    return out
+
+
 def cpu_baseline(wl: workloads.Workload, budget_s: float):
     """The oracle, as it stands, timed on the host on a bounded sample of the
     workload: whole parameters in workload order until the budget is spent."""
@@ -108,6 +180,9 @@ def main():
     ap.add_argument("--mode", default=None, choices=["bf16", "fp32"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--graph", action="store_true", help="replay streamed launches from a HIP graph")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the copy/GEMM ceiling measurement")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only run the copy ceiling (calibrates the byte counters of a profiler)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -125,6 +200,9 @@ def main():
     warmup = args.warmup if args.warmup is not None else (2 if big else 10)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_only:
+        print(json.dumps(measure_ceilings(dev, gemm=False)), flush=True)
+        return
 
     params, grads, moms = make_gpu_inputs(wl, dev)
     torch.cuda.synchronize()
@@ -184,9 +262,10 @@ def main():
         nbytes = skinny_gram_b if dominant == "skinny_gram" else skinny_apply_b
         per_launch = nbytes / max(1, kernel_ms[dominant][1])
         achieved = per_launch / (dom_ms_per_launch * 1e-3) / 1e9
+        traffic = measured_traffic("k_" + dominant, wl.name)
         roof = {"bound": "hbm", "kernel": "k_" + dominant, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "algorithmic_bytes_per_launch": per_launch,
+                "traffic": traffic, "algorithmic_bytes_per_launch": per_launch,
                 "avg_launch_ms": round(dom_ms_per_launch, 5)}
     else:
         # Flops of the dominant matrix-core kernel class per launch.
@@ -231,6 +310,8 @@ def main():
         "launches_per_step": info["launches_fixed"] + info["launches_per_ns"] * wl.ns_steps,
         "device_error": status,
     }
+    if not args.no_ceilings:
+        out["ceilings"] = measure_ceilings(dev)
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 3)
