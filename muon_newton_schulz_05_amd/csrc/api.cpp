@@ -94,12 +94,17 @@ hipError_t timed(muon_plan_t plan, int cls, hipStream_t s, bool timing, F&& laun
   return e;
 }
 
-hipError_t enqueue_skinny(muon_plan_t plan, const muon::BucketPlan& bp, hipStream_t s, bool timing) {
+hipError_t enqueue_skinny(muon_plan_t plan, const muon::BucketPlan& bp, hipStream_t s, bool timing,
+                          const muon::DevScalars* first) {
   const muon::Plan& p = plan->p;
-  muon::SkinnyLaunch L;
+  muon::SkinnyLaunch L{};
   L.mats = at<muon::DevMat>(plan, bp.off_mats);
   L.ptrs = at<muon::PtrEntry>(plan, p.off_ptrs);
   L.sc = at<muon::DevScalars>(plan, p.off_scalars);
+  if (first) {
+    L.sv = *first;
+    L.sc_out = at<muon::DevScalars>(plan, p.off_scalars);
+  }
   L.gram_parts = at<double>(plan, bp.off_gram);
   L.sq_parts = at<float>(plan, bp.off_sqp);
   L.qs = at<float>(plan, bp.off_qs);
@@ -112,13 +117,61 @@ hipError_t enqueue_skinny(muon_plan_t plan, const muon::BucketPlan& bp, hipStrea
   hipError_t e;
   if ((e = timed(plan, muon::kClsSkinnyGram, s, timing, [&] { return muon::launch_skinny_gram(L, s); })) != hipSuccess)
     return e;
+  L.sc_out = nullptr;  // the scalar block is filled from here on
   if ((e = timed(plan, muon::kClsSkinnyPoly, s, timing, [&] { return muon::launch_skinny_poly(L, s); })) != hipSuccess)
     return e;
   return timed(plan, muon::kClsSkinnyApply, s, timing, [&] { return muon::launch_skinny_apply(L, s); });
 }
 
+// Newton-Schulz rounds of a large bf16 bucket (256 x 256 tile products).
+hipError_t enqueue_big_rounds(muon_plan_t plan, const muon::BucketPlan& bp, int ns, hipStream_t s,
+                              bool timing) {
+  const muon::Plan& p = plan->p;
+  const int cnt = (int)bp.slices.size();
+  const uint32_t* tsym = at<uint32_t>(plan, bp.off_tiles_sym);
+  const uint32_t* tfull = at<uint32_t>(plan, bp.off_tiles_full);
+  const int t8sym = (int)bp.tiles_sym.size(), t8full = (int)bp.tiles_full.size();
+  const muon::DevScalars* sc = at<muon::DevScalars>(plan, p.off_scalars);
+  float* a32 = at<float>(plan, bp.off_a32);
+  uint16_t* e16 = at<uint16_t>(plan, bp.off_a16);
+  uint16_t* r16 = at<uint16_t>(plan, bp.off_phi);
+  float* dg = at<float>(plan, bp.off_dg);
+  hipError_t e;
+  for (int it = 0; it < ns; ++it) {
+    const int src = it & 1, dst = src ^ 1;
+    const float* sfirst = it == 0 ? at<float>(plan, bp.off_scale) : nullptr;
+    muon::GramBigLaunch gl{plan->ws + bp.off_x[src], a32, e16, dg, sfirst, tsym, t8sym,
+                           bp.mp, bp.np, cnt};
+    if ((e = timed(plan, muon::kClsGram, s, timing, [&] { return muon::launch_gram_big(gl, s); })) != hipSuccess)
+      return e;
+    muon::PolyBigLaunch pl{e16, a32, dg, r16, sc, tsym, t8sym, bp.mp, cnt};
+    if ((e = timed(plan, muon::kClsPoly, s, timing, [&] { return muon::launch_poly_big(pl, s); })) != hipSuccess)
+      return e;
+    muon::ApplyBigLaunch al{};
+    al.r16 = r16;
+    al.xt_old = plan->ws + bp.off_xt[src];
+    al.x_new = plan->ws + bp.off_x[dst];
+    al.xt_new = plan->ws + bp.off_xt[dst];
+    al.scale = sfirst;
+    al.sc = sc;
+    al.tiles = tfull;
+    al.t8 = t8full;
+    al.mp = bp.mp;
+    al.np = bp.np;
+    al.m = bp.m;
+    al.n = bp.n;
+    al.count = cnt;
+    al.final_round = it == ns - 1;
+    al.mats = at<muon::DevMat>(plan, bp.off_mats);
+    al.ptrs = at<muon::PtrEntry>(plan, p.off_ptrs);
+    if ((e = timed(plan, muon::kClsApply, s, timing, [&] { return muon::launch_apply_big(al, s); })) != hipSuccess)
+      return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, hipStream_t s,
-                          bool timing) {
+                          bool timing, const muon::DevScalars* first) {
   const muon::Plan& p = plan->p;
   const int cnt = (int)bp.slices.size();
   const muon::DevMat* mats = at<muon::DevMat>(plan, bp.off_mats);
@@ -127,9 +180,24 @@ hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, 
   float* scale = at<float>(plan, bp.off_scale);
   hipError_t e;
 
-  muon::MomentumLaunch mo{mats, ptrs, sc, plan->ws + bp.off_x[0], plan->ws + bp.off_xt[0],
-                          at<float>(plan, bp.off_sq), bp.m, bp.n, bp.mp, bp.np, cnt, bp.km_tiles,
-                          bp.x_bytes};
+  muon::MomentumLaunch mo{};
+  mo.mats = mats;
+  mo.ptrs = ptrs;
+  mo.sc = sc;
+  if (first) {
+    mo.sv = *first;
+    mo.sc_out = const_cast<muon::DevScalars*>(sc);
+  }
+  mo.x = plan->ws + bp.off_x[0];
+  mo.xt = plan->ws + bp.off_xt[0];
+  mo.sq = at<float>(plan, bp.off_sq);
+  mo.m = bp.m;
+  mo.n = bp.n;
+  mo.mp = bp.mp;
+  mo.np = bp.np;
+  mo.count = cnt;
+  mo.km_tiles = bp.km_tiles;
+  mo.x_bytes = bp.x_bytes;
   if ((e = timed(plan, muon::kClsMomentum, s, timing, [&] { return muon::launch_momentum(mo, s); })) != hipSuccess)
     return e;
   muon::NormLaunch no{at<float>(plan, bp.off_sq), scale, sc, cnt, bp.km_tiles};
@@ -139,6 +207,7 @@ hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, 
     muon::Update0Launch u{mats, ptrs, sc, scale, bp.m, bp.n, cnt};
     return timed(plan, muon::kClsUpdate, s, timing, [&] { return muon::launch_update0(u, s); });
   }
+  if (bp.big) return enqueue_big_rounds(plan, bp, ns, s, timing);
   for (int it = 0; it < ns; ++it) {
     const int src = it & 1, dst = src ^ 1;
     const float* sfirst = it == 0 ? scale : nullptr;
@@ -187,11 +256,15 @@ hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, 
 // Every bucket's launches, in plan order.  The number of Newton-Schulz
 // rounds is read by the skinny kernels from the scalar block and fixes the
 // streamed launch sequence.
-hipError_t enqueue_buckets(muon_plan_t plan, int ns, hipStream_t s, bool timing) {
+// `first`: the step's scalars, to be written by the first kernel (eager
+// steps), or null when a prologue kernel has already written them.
+hipError_t enqueue_buckets(muon_plan_t plan, int ns, hipStream_t s, bool timing,
+                           const muon::DevScalars* first) {
   for (const muon::BucketPlan& bp : plan->p.buckets) {
-    hipError_t e = bp.path == MUON_PATH_SKINNY ? enqueue_skinny(plan, bp, s, timing)
-                                               : enqueue_stream(plan, bp, ns, s, timing);
+    hipError_t e = bp.path == MUON_PATH_SKINNY ? enqueue_skinny(plan, bp, s, timing, first)
+                                               : enqueue_stream(plan, bp, ns, s, timing, first);
     if (e != hipSuccess) return e;
+    first = nullptr;
   }
   return hipSuccess;
 }
@@ -279,6 +352,13 @@ int muon_plan_create(const muon_param_desc_t* descs, int32_t n_params, const muo
     }
     e = hipMemcpy(plan->ws + bp.off_mats, table.data(), sizeof(muon::DevMat) * table.size(),
                   hipMemcpyHostToDevice);
+    if (e == hipSuccess && bp.big) {
+      e = hipMemcpy(plan->ws + bp.off_tiles_sym, bp.tiles_sym.data(),
+                    sizeof(uint32_t) * bp.tiles_sym.size(), hipMemcpyHostToDevice);
+      if (e == hipSuccess)
+        e = hipMemcpy(plan->ws + bp.off_tiles_full, bp.tiles_full.data(),
+                      sizeof(uint32_t) * bp.tiles_full.size(), hipMemcpyHostToDevice);
+    }
   }
   if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&plan->pinned),
                                          sizeof(muon::PtrEntry) * p.n_params, hipHostMallocDefault);
@@ -360,21 +440,23 @@ int muon_step(muon_plan_t plan, void* const* params, const void* const* grads, v
   v.eps = p.eps;
   v.ns_steps = ns_steps;
   v.pad = 0;
-  e = muon::launch_prologue(at<muon::DevScalars>(plan, p.off_scalars), v, s);
-  if (e != hipSuccess) return hip_fail(e, "prologue launch");
-
   const bool timing = p.timing != 0;
   const bool graph = p.use_graph && !timing && s != nullptr;
   if (!graph) {
-    e = enqueue_buckets(plan, ns_steps, s, timing);
+    // Eager: the first kernel writes the scalar block itself.
+    e = enqueue_buckets(plan, ns_steps, s, timing, &v);
     if (e != hipSuccess) return hip_fail(e, "launch");
     return MUON_OK;
   }
+  // Graph replay: kernel arguments are frozen in the graph, so a prologue
+  // outside it writes this step's scalars first.
+  e = muon::launch_prologue(at<muon::DevScalars>(plan, p.off_scalars), v, s);
+  if (e != hipSuccess) return hip_fail(e, "prologue launch");
   if (plan->gexec == nullptr || plan->graph_ns != ns_steps || plan->graph_stream != s) {
     drop_graph(plan);
     e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
-    hipError_t le = enqueue_buckets(plan, ns_steps, s, false);
+    hipError_t le = enqueue_buckets(plan, ns_steps, s, false, nullptr);
     hipGraph_t g = nullptr;
     e = hipStreamEndCapture(s, &g);
     if (le != hipSuccess) {

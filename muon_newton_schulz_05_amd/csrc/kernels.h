@@ -11,10 +11,15 @@ namespace muon {
 hipError_t launch_prologue(DevScalars* dst, const DevScalars& v, hipStream_t s);
 
 // ---------------------------------------------------------------- skinny (m <= 32)
+// The first kernel of an eager step carries the step's scalars by value and
+// writes them to the plan's scalar block for the kernels after it (sc_out
+// non-null); every other launch reads them from the block (sc).
 struct SkinnyLaunch {
   const DevMat* mats;     // bucket's slice table
   const PtrEntry* ptrs;
   const DevScalars* sc;
+  DevScalars sv;          // scalars by value (used when sc_out is set)
+  DevScalars* sc_out;     // null, or the scalar block to fill
   double* gram_parts;     // [count][n_chunks][m*m]
   float* sq_parts;        // [count][n_chunks]
   float* qs;              // [count][32*32]: s * Q
@@ -31,6 +36,8 @@ struct MomentumLaunch {
   const DevMat* mats;
   const PtrEntry* ptrs;
   const DevScalars* sc;
+  DevScalars sv;          // as in SkinnyLaunch
+  DevScalars* sc_out;
   void* x;                // [count][mp][np]
   void* xt;               // [count][np][mp]
   float* sq;              // [count][km_tiles]
@@ -90,6 +97,56 @@ struct ApplyLaunch {
   const PtrEntry* ptrs;
 };
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
+
+// ---------------------------------------------------------------- streamed, large bf16 buckets
+// Products on 256 x 256 tiles in the order of a planner-built tile table
+// (entries tm | tn << 16; kNoTile pads the table to a multiple of 8).
+
+// A = s2 X X^T -> a32 (float), dg = diag(A) (float), e16 = A - diag(A) (bf16).
+struct GramBigLaunch {
+  const void* x;          // X [count][mp][np], bf16
+  float* a32;
+  uint16_t* e16;
+  float* dg;              // [count][mp]
+  const float* scale;     // {s, s^2} per slice on the first round, else null
+  const uint32_t* tiles;  // upper-triangle tiles
+  int t8;
+  int64_t mp, np;
+  int count;
+};
+hipError_t launch_gram_big(const GramBigLaunch& a, hipStream_t s);
+
+// R = (a - 1) I + b A + c A^2, with A^2 = E E + diag(d) A + A diag(d) - diag(d)^2 (bf16 out).
+struct PolyBigLaunch {
+  const uint16_t* e16;
+  const float* a32;
+  const float* dg;
+  uint16_t* r16;
+  const DevScalars* sc;
+  const uint32_t* tiles;  // upper-triangle tiles
+  int t8;
+  int64_t mp;
+  int count;
+};
+hipError_t launch_poly_big(const PolyBigLaunch& a, hipStream_t s);
+
+// X' = scale (X + R X); the final round subtracts lr X' from W instead.
+struct ApplyBigLaunch {
+  const uint16_t* r16;
+  const void* xt_old;     // X^T [count][np][mp]
+  void* x_new;
+  void* xt_new;
+  const float* scale;     // null after the first round
+  const DevScalars* sc;
+  const uint32_t* tiles;  // all tiles of [mp, np]
+  int t8;
+  int64_t mp, np, m, n;
+  int count;
+  int final_round;
+  const DevMat* mats;
+  const PtrEntry* ptrs;
+};
+hipError_t launch_apply_big(const ApplyBigLaunch& a, hipStream_t s);
 
 // ns_steps == 0: W -= lr * s * M.
 struct Update0Launch {

@@ -10,6 +10,9 @@ namespace muon {
 constexpr int kMaxSkinnyM = 32;       // skinny path: one 32-row MFMA tile holds all of m
 constexpr int kSkinnyChunk = 256;     // skinny path: columns per workgroup (fixed by n alone)
 constexpr int kStreamPad = 128;       // streamed workspace dims are padded to this
+constexpr int kBigTile = 256;         // large bf16 buckets: product tile, and their padding
+constexpr int kBigMinM = 513;         // bf16 buckets with m >= this take the large-tile products
+constexpr uint32_t kNoTile = 0xFFFFFFFFu;  // tile-table padding entry
 constexpr int kMomTile = 64;          // momentum kernel tile (oriented 64 x 64)
 
 enum KernelClass { kClsSkinnyGram = 0, kClsSkinnyPoly, kClsSkinnyApply, kClsMomentum, kClsNorm,

@@ -165,7 +165,7 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
   p.off_scalars = ws.take(sizeof(DevScalars));
   p.off_err = ws.take(sizeof(uint32_t));
   p.off_ptrs = ws.take(sizeof(PtrEntry) * (uint64_t)n_params);
-  p.launches_fixed = 1;  // prologue
+  p.launches_fixed = p.use_graph ? 1 : 0;  // graph replays need a prologue kernel for the scalars
   p.launches_per_ns = 0;
   for (BucketPlan& bp : p.buckets) {
     const uint64_t cnt = bp.slices.size();
@@ -178,11 +178,13 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
       bp.off_qs = ws.take(cnt * 1024 * sizeof(float));
       p.launches_fixed += 3;  // momentum + Gram partials, polynomial, apply + update
     } else {
-      bp.mp = round_up(bp.m, kStreamPad);
-      bp.np = round_up(bp.n, kStreamPad);
+      bp.big = p.mode == MUON_MODE_BF16_MFMA && bp.m >= kBigMinM;
+      const int64_t pad = bp.big ? kBigTile : kStreamPad;
+      bp.mp = round_up(bp.m, pad);
+      bp.np = round_up(bp.n, pad);
       bp.x_bytes = p.mode == MUON_MODE_FP32 ? 4 : 2;
-      bp.poly_f32 = p.mode == MUON_MODE_FP32 || bp.m <= 512;
-      bp.p_hilo = p.mode == MUON_MODE_BF16_MFMA && bp.m <= 512;
+      bp.poly_f32 = !bp.big;
+      bp.p_hilo = p.mode == MUON_MODE_BF16_MFMA && !bp.big;
       bp.km_tiles = (int)(((bp.m + kMomTile - 1) / kMomTile) * ((bp.n + kMomTile - 1) / kMomTile));
       const uint64_t xsz = cnt * bp.mp * bp.np * bp.x_bytes;
       const uint64_t msz = cnt * bp.mp * bp.mp;
@@ -194,6 +196,14 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
       bp.off_plo = bp.p_hilo ? ws.take(msz * 2) : 0;
       bp.off_sq = ws.take(cnt * bp.km_tiles * sizeof(float));
       bp.off_scale = ws.take(cnt * 2 * sizeof(float));
+      if (bp.big) {
+        bp.off_dg = ws.take(cnt * bp.mp * sizeof(float));
+        const int tm = (int)(bp.mp / kBigTile), tn = (int)(bp.np / kBigTile);
+        bp.tiles_sym = tile_order(tm, tm, true);
+        bp.tiles_full = tile_order(tm, tn, false);
+        bp.off_tiles_sym = ws.take(bp.tiles_sym.size() * sizeof(uint32_t));
+        bp.off_tiles_full = ws.take(bp.tiles_full.size() * sizeof(uint32_t));
+      }
       p.launches_fixed += 2;   // momentum, norm
       p.launches_per_ns += 3;  // gram, poly, apply (the last apply also updates W)
     }
@@ -208,6 +218,18 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
   }
   *out = std::move(p);
   return MUON_OK;
+}
+
+std::vector<uint32_t> tile_order(int tiles_m, int tiles_n, bool sym) {
+  constexpr int kRows = 4, kCols = 8;
+  std::vector<uint32_t> t;
+  for (int i0 = 0; i0 < tiles_m; i0 += kRows)
+    for (int j0 = sym ? (i0 / kCols) * kCols : 0; j0 < tiles_n; j0 += kCols)
+      for (int i = i0; i < i0 + kRows && i < tiles_m; ++i)
+        for (int j = j0; j < j0 + kCols && j < tiles_n; ++j)
+          if (!sym || j >= i) t.push_back((uint32_t)i | ((uint32_t)j << 16));
+  while (t.size() % 8) t.push_back(kNoTile);
+  return t;
 }
 
 void fill_info(const Plan& p, muon_plan_info_t* info) {

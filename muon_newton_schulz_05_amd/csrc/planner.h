@@ -34,6 +34,7 @@ struct BucketPlan {
   uint64_t off_gram = 0, off_sqp = 0, off_qs = 0;
 
   // streamed path
+  bool big = false;         // bf16 mode and m >= kBigMinM: 256 x 256 tile products
   int64_t mp = 0, np = 0;   // padded dims
   int x_bytes = 0;          // X element size (2: bf16, 4: fp32)
   bool poly_f32 = false;    // A^2 from float32 A (else bf16 copy of A)
@@ -41,6 +42,9 @@ struct BucketPlan {
   int km_tiles = 0;         // momentum-kernel tiles per slice
   uint64_t off_x[2] = {0, 0}, off_xt[2] = {0, 0};
   uint64_t off_a32 = 0, off_a16 = 0, off_phi = 0, off_plo = 0, off_sq = 0, off_scale = 0;
+  uint64_t off_dg = 0;                         // big: diagonal of A per slice
+  uint64_t off_tiles_sym = 0, off_tiles_full = 0;  // big: tile tables (uint32)
+  std::vector<uint32_t> tiles_sym, tiles_full;     // their contents
 
   uint64_t off_mats = 0;    // this bucket's DevMat table
   uint64_t ws_begin = 0, ws_bytes = 0;
@@ -72,5 +76,11 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
               int n_cu, Plan* out, std::string* err);
 
 void fill_info(const Plan& p, muon_plan_info_t* info);
+
+// Tile order of a 256 x 256-tiled product with tiles_m x tiles_n output
+// tiles (upper triangle only when sym), padded with kNoTile to a multiple
+// of 8.  Tiles are grouped into blocks of 4 tile rows x 8 tile columns, so the
+// 32 workgroups an XCD runs at once share 4 row panels and 8 column panels.
+std::vector<uint32_t> tile_order(int tiles_m, int tiles_n, bool sym);
 
 }  // namespace muon

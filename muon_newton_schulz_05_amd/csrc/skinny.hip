@@ -156,7 +156,8 @@ __global__ __launch_bounds__(kThreads) void k_skinny_gram(SkinnyLaunch a) {
   const int z = blockIdx.y, chunk = blockIdx.x;
   const DevMat d = a.mats[z];
   const PtrEntry pe = a.ptrs[d.param];
-  const float beta = a.sc->beta;
+  const float beta = a.sc_out ? a.sv.beta : a.sc->beta;
+  if (a.sc_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.sc_out = a.sv;
   const int m = a.m, n = a.n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   ChunkMap cm;
@@ -297,69 +298,111 @@ __global__ __launch_bounds__(kThreads) void k_skinny_gram(SkinnyLaunch a) {
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void k_skinny_poly(SkinnyLaunch a) {
-  __shared__ double A[32][33], Q[32][33], P[32][33], T[32][33];
+  // Double-buffered A and Q so that a product never overwrites its own input.
+  __shared__ double A[2][32][33], Q[2][32][33], P[32][33], S[32][33];
   __shared__ double sh_s;
   const int z = blockIdx.x;
   const int m = a.m, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const double ca = a.sc->a, cb = a.sc->b, cc = a.sc->c;
   const int ns = a.sc->ns_steps;
   const int mk = (m + 3) & ~3;  // contraction length, a multiple of 4
-  // Sum the chunk partials in chunk order.  Loads go out in batches of
-  // kBatch independent requests so the reduction is not one round trip per
-  // chunk.
-  constexpr int kBatch = 16;
-  auto chunk_sum = [&](const auto* base, int64_t stride) -> double {
-    double v = 0.0;
-    for (int c0 = 0; c0 < a.n_chunks; c0 += kBatch) {
-      double part[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) part[u] = c0 + u < a.n_chunks ? (double)base[(int64_t)(c0 + u) * stride] : 0.0;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) v += part[u];
+  const int mm = m * m;
+  const int nch = a.n_chunks;
+
+  // Sum of squares: wave 3 loads the chunk partials together and adds them
+  // in chunk order (lane 0 walks the loaded values), alongside the Gram sums.
+  if (wave == 3) {
+    const float* sq = a.sq_parts + (int64_t)z * nch;
+    double tot = 0.0;
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+      const double v = c0 + lane < nch ? (double)sq[c0 + lane] : 0.0;
+      const int cnt = min(64, nch - c0);
+      for (int u = 0; u < cnt; ++u) tot += __shfl(v, u);
     }
-    return v;
-  };
-  if (tid == 0) {
-    const double s = chunk_sum(a.sq_parts + (int64_t)z * a.n_chunks, 1);
-    sh_s = 1.0 / (sqrt(s) + (double)a.sc->eps);
-    if (!isfinite(s)) atomicOr(a.err, kErrNonFinite);
+    if (lane == 0) {
+      sh_s = 1.0 / (sqrt(tot) + (double)a.sc->eps);
+      if (!isfinite(tot)) atomicOr(a.err, kErrNonFinite);
+    }
   }
-  const double* parts = a.gram_parts + (int64_t)z * a.n_chunks * m * m;
+  // Gram sums: entry v = tid + 256 k of the compact m x m block, k < 4
+  // (m <= 32); the loads of all of a thread's entries for kBatch chunks are
+  // in flight together, and each entry is summed in chunk order.
+  constexpr int kBatch = 10, kPer = 4;
+  const double* parts = a.gram_parts + (int64_t)z * nch * mm;
+  double sum[kPer] = {0.0, 0.0, 0.0, 0.0};
+  for (int c0 = 0; c0 < nch; c0 += kBatch) {
+    double part[kPer][kBatch];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int v = tid + kThreads * k;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        part[k][u] = (v < mm && c0 + u < nch) ? parts[(int64_t)(c0 + u) * mm + v] : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) sum[k] += part[k][u];
+  }
   for (int e = tid; e < 1024; e += kThreads) {
-    const int i = e >> 5, j = e & 31;
-    T[i][j] = (i < m && j < m) ? chunk_sum(parts + i * m + j, (int64_t)m * m) : 0.0;
-    Q[i][j] = (i == j && i < m) ? 1.0 : 0.0;
+    A[0][e >> 5][e & 31] = 0.0;
+    Q[0][e >> 5][e & 31] = ((e >> 5) == (e & 31) && (e >> 5) < m) ? 1.0 : 0.0;
   }
   __syncthreads();
   const double s = sh_s;
-  for (int e = tid; e < 1024; e += kThreads) A[e >> 5][e & 31] = T[e >> 5][e & 31] * s * s;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int v = tid + kThreads * k;
+    if (v < mm) A[0][v / m][v % m] = sum[k] * s * s;
+  }
   __syncthreads();
+
+  // Each wave owns one 16 x 16 tile of a 32 x 32 product; f64 matrix-core
+  // layout: X lane l -> X[l mod 16][l / 16], Y lane l -> Y[l / 16][l mod 16],
+  // result register r -> row l / 16 + 4 r, column l mod 16.
   const int ti = 16 * (wave >> 1), tj = 16 * (wave & 1);
   const int li = lane & 15, lk = lane >> 4;
-  // out = X Y
-  auto mul = [&](double (*out)[33], double (*X)[33], double (*Y)[33]) {
+  auto prod = [&](const double (*X)[33], const double (*Y)[33]) {
     f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
     for (int k0 = 0; k0 < mk; k0 += 4)
       acc = __builtin_amdgcn_mfma_f64_16x16x4f64(X[ti + li][k0 + lk], Y[k0 + lk][tj + li], acc, 0, 0, 0);
-    __syncthreads();  // out may alias an input of another wave's tile
-#pragma unroll
-    for (int r = 0; r < 4; ++r) out[ti + lk + 4 * r][tj + li] = acc[r];
-    __syncthreads();
+    return acc;
   };
+  int cur = 0;
   for (int it = 0; it < ns; ++it) {
-    mul(T, A, A);  // T = A^2
-    for (int e = tid; e < 1024; e += kThreads) {
-      const int i = e >> 5, j = e & 31;
-      P[i][j] = cb * A[i][j] + cc * T[i][j] + ((i == j && i < m) ? ca : 0.0);
+    // P = a I + b A + c A^2
+    {
+      const f64x4_t t = prod(A[cur], A[cur]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = ti + lk + 4 * r, j = tj + li;
+        P[i][j] = cb * A[cur][i][j] + cc * t[r] + ((i == j && i < m) ? ca : 0.0);
+      }
     }
     __syncthreads();
-    mul(Q, P, Q);  // Q <- P Q
-    if (it + 1 < ns) {
-      mul(T, P, A);  // A <- P (P A) = P^2 A
-      mul(A, P, T);
+    // Q <- P Q and, unless this is the last round, S = P P
+    {
+      const f64x4_t q = prod(P, Q[cur]);
+      f64x4_t sp = {0.0, 0.0, 0.0, 0.0};
+      if (it + 1 < ns) sp = prod(P, P);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = ti + lk + 4 * r, j = tj + li;
+        Q[cur ^ 1][i][j] = q[r];
+        S[i][j] = sp[r];
+      }
     }
+    __syncthreads();
+    if (it + 1 < ns) {
+      // A <- P^2 A
+      const f64x4_t t = prod(S, A[cur]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) A[cur ^ 1][ti + lk + 4 * r][tj + li] = t[r];
+      __syncthreads();
+    }
+    cur ^= 1;
   }
-  for (int e = tid; e < 1024; e += kThreads) a.qs[(int64_t)z * 1024 + e] = (float)(s * Q[e >> 5][e & 31]);
+  for (int e = tid; e < 1024; e += kThreads) a.qs[(int64_t)z * 1024 + e] = (float)(s * Q[cur][e >> 5][e & 31]);
 }
 
 // ------------------------------------------------------------------ apply

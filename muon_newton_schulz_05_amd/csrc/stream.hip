@@ -39,7 +39,8 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumLaunch a) {
   const int64_t i0 = (int64_t)ti * kMomTile, j0 = (int64_t)tj * kMomTile;
   const DevMat d = a.mats[z];
   const PtrEntry pe = a.ptrs[d.param];
-  const float beta = a.sc->beta;
+  const float beta = a.sc_out ? a.sv.beta : a.sc->beta;
+  if (a.sc_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.sc_out = a.sv;
   const int tid = threadIdx.x;
 
   // Load along the stored rows (coalesced), keep M_new in LDS in oriented order.
@@ -114,8 +115,6 @@ struct GemmCore {
   int64_t sa, sb;            // matrix strides in elements
   int64_t K;                 // contraction length (multiple of the k-slice)
   int tiles_n;               // output tiles along j
-  int tiles_m;               // output tiles along i (large-tile kernel)
-  int sym;                   // output symmetric: only tiles with tn >= tm are computed
 };
 
 __device__ __forceinline__ f32x16_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -231,156 +230,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmCore c, Epi epi) {
       }
 }
 
-// ------------------------------------------------------------------ large bf16 GEMM
-// 256 x 256 output tile per 256-thread workgroup for bf16 operands: the four
-// waves each own a 128 x 128 quarter (4 x 4 blocks of the 32x32x16
-// instruction; the 256 accumulators live in the accumulation registers).
-// Operand k-slices of 64 elements (128 bytes a row) go from HBM straight into
-// LDS with gfx950's global_load_lds_dwordx4, so no registers hold them in
-// flight: one instruction fills 1 KB (8 rows) of LDS in lane order, and the
-// lanes choose which 16-byte chunk of their row to fetch so that chunk c of
-// row r lands in slot c ^ ((r / 2) mod 8).  With that swizzle the 16-byte
-// fragment reads of 16 consecutive rows touch 16 distinct bank groups.
-// Two stages: the next slice's loads fly while the current one is multiplied.
-// Workgroups are mapped to output tiles so that each XCD (workgroups are
-// dealt to the 8 XCDs round robin) works on a contiguous range of tiles,
-// ordered in groups of kGroupM tile rows for L2 reuse of both operands.
-constexpr int kBigBK = 64;                    // bf16 elements of k per slice
-constexpr int kGroupM = 4;
-
-#define LDS_PTR __attribute__((address_space(3)))
-
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
-
-template <int BM, int BN, class Epi>
-__global__ __launch_bounds__(256) void k_gemm_bf16(GemmCore c, Epi epi) {
-  constexpr int WM = BM / 2, WN = BN / 2;    // per-wave tile
-  constexpr int FM = WM / 32, FN = WN / 32;  // 32x32 blocks per wave
-  constexpr int IA = BM / 8 / 4, IB = BN / 8 / 4;  // load instructions per wave and slice
-  constexpr int STAGE = (BM + BN) * 128;     // bytes per stage
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
-
-  // Tile of this workgroup.
-  const int tiles_m = c.tiles_m, tiles_n = c.tiles_n;
-  const int T = c.sym ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
-  int b = blockIdx.x;
-  if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);  // contiguous tile range per XCD
-  int tm, tn;
-  if (c.sym) {  // upper triangle, row by row
-    tm = 0;
-    while (b >= tiles_m - tm) {
-      b -= tiles_m - tm;
-      ++tm;
-    }
-    tn = tm + b;
-  } else {
-    const int per_group = kGroupM * tiles_n;
-    const int g = b / per_group, first_m = g * kGroupM;
-    const int gm = min(kGroupM, tiles_m - first_m);
-    const int r0 = b - g * per_group;
-    tm = first_m + r0 % gm;
-    tn = r0 / gm;
-  }
-
-  const int z = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const char* A = c.a + ((int64_t)z * c.sa + (int64_t)tm * BM * c.lda) * 2;
-  const char* B = c.b + ((int64_t)z * c.sb + (int64_t)tn * BN * c.ldb) * 2;
-  const int nk = (int)(c.K / kBigBK);
-
-  // Per-lane byte offsets of the chunks this lane fetches (relative to the
-  // tile's first row, slice 0); instruction u of wave w fills rows
-  // 8 (w + 4 u) .. + 7.
-  uint32_t oa[IA], ob[IB];
-#pragma unroll
-  for (int u = 0; u < IA; ++u) {
-    const int row = 8 * (wave + 4 * u) + (lane >> 3);
-    oa[u] = (uint32_t)(row * c.lda * 2 + (((lane & 7) ^ swz(row)) << 4));
-  }
-#pragma unroll
-  for (int u = 0; u < IB; ++u) {
-    const int row = 8 * (wave + 4 * u) + (lane >> 3);
-    ob[u] = (uint32_t)(row * c.ldb * 2 + (((lane & 7) ^ swz(row)) << 4));
-  }
-  auto issue = [&](int kt, int stage) {
-    char LDS_PTR* base = (char LDS_PTR*)(lds + stage * STAGE);
-#pragma unroll
-    for (int u = 0; u < IA; ++u)
-      __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(A + (int64_t)kt * 128 + oa[u]),
-                                       (void LDS_PTR*)(base + (wave + 4 * u) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int u = 0; u < IB; ++u)
-      __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(B + (int64_t)kt * 128 + ob[u]),
-                                       (void LDS_PTR*)(base + BM * 128 + (wave + 4 * u) * 1024), 16, 0, 0);
-  };
-
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
-
-  const int ra = wm * WM + (lane & 31), rb = BM + wn * WN + (lane & 31);
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      issue(kt + 1, cur ^ 1);
-      // This wave's loads of slice kt are the ones issued before the last IA + IB.
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IA + IB) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    // A bare barrier: the wait above already covers this wave's loads of
-    // slice kt, and a fenced __syncthreads would also wait for slice kt + 1.
-    __builtin_amdgcn_s_barrier();  // every wave's part of slice kt is in LDS
-    const char* st = lds + cur * STAGE;
-#pragma unroll
-    for (int s = 0; s < kBigBK / 16; ++s) {
-      const int ck = 2 * s + (lane >> 5);
-      bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = ra + 32 * i;
-        af[i] = *reinterpret_cast<const bf16x8_t*>(st + r * 128 + ((ck ^ swz(r)) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = rb + 32 * j;
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + r * 128 + ((ck ^ swz(r)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(af[i], bfr[j], acc[i][j]);
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // slice kt fully read before its stage is refilled
-  }
-
-#pragma clang loop unroll(full)
-  for (int i = 0; i < FM; ++i)
-#pragma clang loop unroll(full)
-    for (int j = 0; j < FN; ++j)
-#pragma clang loop unroll(full)
-      for (int q = 0; q < 4; ++q) {
-        const int i0 = tm * BM + wm * WM + i * 32 + 8 * q + 4 * (lane >> 5);
-        const int jj = tn * BN + wn * WN + j * 32 + (lane & 31);
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = acc[i][j][4 * q + u];
-        epi(z, i0, jj, v);
-      }
-}
-
 // ------------------------------------------------------------------ epilogues
 struct GramEpi {
   float* a32;
   uint16_t* a16;
   const float* scale;
   int64_t mp;
-  int sym;  // only entries with j >= i are computed: write them and their mirror
   __device__ void operator()(int z, int i0, int j, const float v[4]) const {
     const float s = scale ? scale[2 * z + 1] : 1.f;
     const int64_t zb = (int64_t)z * mp * mp;
@@ -390,13 +245,8 @@ struct GramEpi {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = i0 + u;
-      if (sym && j < i) continue;
       a32[zb + (int64_t)i * mp + j] = val[u];
       if (a16) a16[zb + (int64_t)i * mp + j] = to_bf16(val[u]);
-      if (sym && j > i) {
-        a32[zb + (int64_t)j * mp + i] = val[u];
-        if (a16) a16[zb + (int64_t)j * mp + i] = to_bf16(val[u]);
-      }
     }
   }
 };
@@ -408,7 +258,6 @@ struct PolyEpi {
   int p_f32;
   const DevScalars* sc;
   int64_t mp;
-  int sym;  // only entries with j >= i are computed: write them and their mirror
   __device__ void put(int64_t idx, float val) const {
     if (p_f32) {
       static_cast<float*>(phi)[idx] = val;
@@ -423,12 +272,8 @@ struct PolyEpi {
     const int64_t zb = (int64_t)z * mp * mp;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u;
-      if (sym && j < i) continue;
-      const int64_t idx = zb + (int64_t)i * mp + j;
-      const float val = b * a32[idx] + c * v[u];
-      put(idx, val);
-      if (sym && j > i) put(zb + (int64_t)j * mp + i, val);
+      const int64_t idx = zb + (int64_t)(i0 + u) * mp + j;
+      put(idx, b * a32[idx] + c * v[u]);
     }
   }
 };
@@ -506,22 +351,9 @@ __global__ __launch_bounds__(256) void k_update0(Update0Launch a) {
   }
 }
 
-// bf16 products whose dimensions are multiples of 256 (and without a second
-// A operand) take the 256 x 256 kernel; the rest the 128 x 128 one.
 template <typename T, class Epi>
-hipError_t run_gemm(const GemmCore& c0, const Epi& e, int64_t rows, int count, hipStream_t s) {
-  GemmCore c = c0;
-  const int64_t cols = (int64_t)c.tiles_n * kBN;
-  if (sizeof(T) == 2 && c.a2 == nullptr && rows % 256 == 0 && cols % 256 == 0 && c.K % kBigBK == 0) {
-    c.tiles_m = (int)(rows / 256);
-    c.tiles_n = (int)(cols / 256);
-    const int tiles = c.sym ? c.tiles_m * (c.tiles_m + 1) / 2 : c.tiles_m * c.tiles_n;
-    hipLaunchKernelGGL((k_gemm_bf16<256, 256, Epi>), dim3(tiles, 1, count), dim3(256), 0, s, c, e);
-    return hipGetLastError();
-  }
-  c.sym = 0;  // the 128 x 128 kernel computes every tile
-  c.tiles_m = (int)(rows / kBM);
-  const int tiles = c.tiles_m * c.tiles_n;
+hipError_t run_gemm(const GemmCore& c, const Epi& e, int64_t rows, int count, hipStream_t s) {
+  const int tiles = (int)(rows / kBM) * c.tiles_n;
   hipLaunchKernelGGL((k_gemm<T, Epi>), dim3(tiles, 1, count), dim3(256), 0, s, c, e);
   return hipGetLastError();
 }
@@ -553,8 +385,7 @@ hipError_t launch_gram(const GramLaunch& a, hipStream_t s) {
   c.sa = c.sb = a.mp * a.np;
   c.K = a.np;
   c.tiles_n = (int)(a.mp / kBN);
-  c.sym = 1;  // X X^T is symmetric
-  GramEpi e{a.a32, a.a16, a.scale, a.mp, 1};
+  GramEpi e{a.a32, a.a16, a.scale, a.mp};
   return a.x_bytes == 2 ? run_gemm<uint16_t>(c, e, a.mp, a.count, s)
                         : run_gemm<float>(c, e, a.mp, a.count, s);
 }
@@ -568,8 +399,7 @@ hipError_t launch_poly(const PolyLaunch& a, hipStream_t s) {
   c.sa = c.sb = a.mp * a.mp;
   c.K = a.mp;
   c.tiles_n = (int)(a.mp / kBN);
-  c.sym = 1;  // A A is symmetric for symmetric A
-  PolyEpi e{a.a32, a.phi, a.plo, a.p_bytes == 4, a.sc, a.mp, 1};
+  PolyEpi e{a.a32, a.phi, a.plo, a.p_bytes == 4, a.sc, a.mp};
   return a.op_bytes == 2 ? run_gemm<uint16_t>(c, e, a.mp, a.count, s)
                          : run_gemm<float>(c, e, a.mp, a.count, s);
 }
@@ -584,7 +414,6 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   c.sa = a.mp * a.mp;
   c.sb = a.np * a.mp;
   c.K = a.mp;
-  c.sym = 0;
   c.tiles_n = (int)(a.np / kBN);
   if (a.x_bytes == 2) {
     if (a.final_round) {

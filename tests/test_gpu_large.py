@@ -1,0 +1,106 @@
+"""Parity of the large-slice products (bf16 mode, m > 512: 256 x 256 tiles,
+float32 diagonal kept out of the bf16 operands, identity-shifted polynomial).
+
+Sizes are chosen so that the oracle runs in seconds while the products still
+span several 256-tiles and ragged edges: padding in m and n, both storage
+orientations, 3-D stacks, rows of W that are not whole 16-byte groups, bf16
+weights, every final-round position (k = 1, 2, 5) and repeated steps.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from gpu_helpers import TOL, gpu_step, make_inputs, oracle_step, slice_rel_errors, update_errors
+
+pytestmark = pytest.mark.gpu
+
+Q = (3.4445, -4.7750, 2.0315)
+# Expected worst error of this arithmetic at these sizes is about 4e-3 to
+# 8e-3; the bar is the bf16-mode tolerance.
+BAR = TOL["bf16"]
+
+
+def _check(shapes, *, ns=5, steps=1, param_dtypes=None, w_std=0.0, m_std=0.0, seed=3, lr=1.0):
+    params, grads, moms = make_inputs(shapes, "bf16", seed, 1e-3, param_dtypes, w_std, m_std)
+    w_gpu, m_gpu = gpu_step(params, grads, moms, mode="bf16", lr=lr, beta=0.95, ns_steps=ns, coeffs=Q,
+                            steps=steps)
+    w_ref, m_ref, o_ref = oracle_step(params, grads, moms, lr=lr, beta=0.95, ns_steps=ns, coeffs=Q,
+                                      steps=steps)
+    worst = 0.0
+    for i in range(len(shapes)):
+        if steps == 1:
+            errs = update_errors(w_gpu[i], params[i], lr, o_ref[i])
+        else:  # compare the accumulated change of W, which the initial W would swamp
+            w0 = params[i].astype(np.float64)
+            errs = slice_rel_errors(w_gpu[i].astype(np.float64) - w0, w_ref[i] - w0)
+        worst = max(worst, max(errs))
+        assert max(slice_rel_errors(m_gpu[i], m_ref[i])) <= 1e-6
+    print(f"{shapes} ns={ns} steps={steps}: worst {worst:.3e}", flush=True)
+    assert worst <= BAR, worst
+    return worst
+
+
+@pytest.mark.parametrize("shape", [(600, 700), (700, 600), (1024, 1280), (514, 517), (2, 520, 1030)])
+def test_large_shapes(shape):
+    _check([shape])
+
+
+@pytest.mark.parametrize("ns", [0, 1, 2])
+def test_large_round_counts(ns):
+    _check([(640, 900), (900, 640)], ns=ns)
+
+
+def test_large_bf16_weights_nonzero_state():
+    """bf16 weights are rounded to nearest even after the update, so the check
+    allows one bf16 rounding of W on top of the bf16-mode bar on lr O."""
+    import oracle
+    shapes = [(600, 1000), (1000, 600)]
+    params, grads, moms = make_inputs(shapes, "bf16", 41, 1e-3, "bf16", 0.02, 1e-3)
+    w_gpu, _ = gpu_step(params, grads, moms, mode="bf16", lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    w_ref, _, o_ref = oracle_step(params, grads, moms, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    for i in range(len(shapes)):
+        err = np.linalg.norm(oracle.decode(w_gpu[i]) - w_ref[i])
+        bound = 2.0 ** -8 * np.linalg.norm(w_ref[i]) + 0.02 * BAR * np.linalg.norm(o_ref[i])
+        print(f"bf16 W {shapes[i]}: {err:.3e} (bound {bound:.3e})", flush=True)
+        assert err <= bound
+
+
+def test_large_three_steps_and_mixed_plan():
+    _check([(24, 3000), (96, 200), (600, 700), (700, 600)], steps=3, w_std=0.02, m_std=1e-3, lr=0.02)
+
+
+def test_large_deterministic():
+    shapes = [(600, 700), (2, 520, 1030)]
+    params, grads, moms = make_inputs(shapes, "bf16", 12)
+    a, _ = gpu_step(params, grads, moms, mode="bf16", lr=1.0, beta=0.95, ns_steps=5, coeffs=Q)
+    b, _ = gpu_step(params, grads, moms, mode="bf16", lr=1.0, beta=0.95, ns_steps=5, coeffs=Q)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_large_graph_replay_matches_eager():
+    import torch
+
+    from gpu_helpers import to_device, to_host
+    from muon_newton_schulz_05_amd import MuonPlan
+    shapes = [(600, 700), (24, 800)]
+    params, grads, moms = make_inputs(shapes, "bf16", 62, w_std=0.02)
+    dev = "cuda:0"
+    outs = []
+    for use_graph in (False, True):
+        p = [to_device(x, dev) for x in params]
+        g = [to_device(x, dev) for x in grads]
+        m = [to_device(x, dev) for x in moms]
+        plan = MuonPlan(p, grad_dtypes=[x.dtype for x in g], mode="bf16", use_graph=use_graph)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            for lr in (0.02, 0.01, 0.03):
+                plan.step(g, m, lr=lr, beta=0.9, ns_steps=5, coeffs=Q)
+                s.synchronize()
+        torch.cuda.synchronize()
+        outs.append([to_host(x) for x in p + m])
+        plan.close()
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y)

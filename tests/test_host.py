@@ -86,16 +86,37 @@ def test_plans_of_the_workloads(m):
     info = describe(m, W["fused_74x24x10240"])
     assert bucket_keys(info) == [(24, 10240, 74, 0, "skinny")]
     assert info["buckets"][0]["chunks"] == 40
-    assert info["launches_fixed"] == 4 and info["launches_per_ns"] == 0   # prologue + three kernels
+    assert info["launches_fixed"] == 3 and info["launches_per_ns"] == 0   # three kernels (eager: no prologue)
     assert bucket_keys(describe(m, W["moe_experts"])) == [(24, 10240, 32, 0, "skinny"),
                                                           (1408, 2048, 64, 0, "stream")]
     info = describe(m, W["dense_h4096_l8"])
     assert bucket_keys(info) == [(4096, 12288, 8, 0, "stream"), (4096, 4096, 8, 0, "stream"),
                                  (4096, 16384, 16, 8, "stream")]
-    assert info["launches_fixed"] == 1 + 3 * 2 and info["launches_per_ns"] == 3 * 3
+    assert info["launches_fixed"] == 3 * 2 and info["launches_per_ns"] == 3 * 3
     assert bucket_keys(describe(m, W["large_share"])) == [(8192, 8192, 4, 0, "stream"),
                                                           (4096, 16384, 4, 4, "stream")]
     assert describe(m, W["large_share"])["n_matrices"] == 8
+
+
+def test_graph_plans_count_the_scalar_prologue(m):
+    """Eager steps let the first kernel write the step's scalars; a graph
+    replay needs one extra kernel ahead of the graph for them."""
+    W = workloads.WORKLOADS
+    eager = describe(m, W["fused_74x24x10240"])
+    graph = describe(m, W["fused_74x24x10240"], use_graph=True)
+    assert graph["launches_fixed"] == eager["launches_fixed"] + 1
+
+
+def test_large_bucket_workspace_is_padded_to_the_big_tile(m):
+    """bf16 buckets with m > 512 are padded to 256 (1408 -> 1536); their
+    workspace holds X and X^T twice, A (float32), E and R (bf16), the
+    diagonal and the two tile tables."""
+    d = m.make_descs([(1408, 2048)], ["f32"], ["bf16"])
+    big = m.info_dict(m.muon_plan_describe(d, m.make_opts(mode="bf16")))["buckets"][0]["workspace_bytes"]
+    mp, np_ = 1536, 2048
+    assert big >= 4 * mp * np_ * 2 + mp * mp * (4 + 2 + 2) + mp * 4
+    small = m.info_dict(m.muon_plan_describe(d, m.make_opts(mode="fp32")))["buckets"][0]["workspace_bytes"]
+    assert small >= 4 * 1408 * 2048 * 4 + 1408 * 1408 * (4 + 4)
 
 
 def test_chunks_depend_on_shape_not_batch(m):
