@@ -123,48 +123,30 @@ hipError_t enqueue_skinny(muon_plan_t plan, const muon::BucketPlan& bp, hipStrea
   return timed(plan, muon::kClsSkinnyApply, s, timing, [&] { return muon::launch_skinny_apply(L, s); });
 }
 
-// Newton-Schulz rounds of a large bf16 bucket (256 x 256 tile products).
-hipError_t enqueue_big_rounds(muon_plan_t plan, const muon::BucketPlan& bp, int ns, hipStream_t s,
-                              bool timing) {
+// Newton-Schulz rounds of all large bf16 buckets: one launch per product
+// phase and round, each walking its tile table across the buckets.
+hipError_t enqueue_big_rounds(muon_plan_t plan, int ns, hipStream_t s, bool timing) {
   const muon::Plan& p = plan->p;
-  const int cnt = (int)bp.slices.size();
-  const uint32_t* tsym = at<uint32_t>(plan, bp.off_tiles_sym);
-  const uint32_t* tfull = at<uint32_t>(plan, bp.off_tiles_full);
-  const int t8sym = (int)bp.tiles_sym.size(), t8full = (int)bp.tiles_full.size();
-  const muon::DevScalars* sc = at<muon::DevScalars>(plan, p.off_scalars);
-  float* a32 = at<float>(plan, bp.off_a32);
-  uint16_t* e16 = at<uint16_t>(plan, bp.off_a16);
-  uint16_t* r16 = at<uint16_t>(plan, bp.off_phi);
-  float* dg = at<float>(plan, bp.off_dg);
+  muon::BigArgs g{};
+  g.buckets = at<muon::BigBucket>(plan, p.off_big_params);
+  g.sc = at<muon::DevScalars>(plan, p.off_scalars);
+  g.ptrs = at<muon::PtrEntry>(plan, p.off_ptrs);
   hipError_t e;
   for (int it = 0; it < ns; ++it) {
-    const int src = it & 1, dst = src ^ 1;
-    const float* sfirst = it == 0 ? at<float>(plan, bp.off_scale) : nullptr;
-    muon::GramBigLaunch gl{plan->ws + bp.off_x[src], a32, e16, dg, sfirst, tsym, t8sym,
-                           bp.mp, bp.np, cnt};
-    if ((e = timed(plan, muon::kClsGram, s, timing, [&] { return muon::launch_gram_big(gl, s); })) != hipSuccess)
+    g.src = it & 1;
+    g.first = it == 0;
+    g.tiles = at<muon::BigTile>(plan, p.off_big_tab[0]);
+    g.t8 = (int)p.big_tab[0].size();
+    if ((e = timed(plan, muon::kClsGram, s, timing, [&] { return muon::launch_big(muon::kBigGram, g, s); })) != hipSuccess)
       return e;
-    muon::PolyBigLaunch pl{e16, a32, dg, r16, sc, tsym, t8sym, bp.mp, cnt};
-    if ((e = timed(plan, muon::kClsPoly, s, timing, [&] { return muon::launch_poly_big(pl, s); })) != hipSuccess)
+    g.tiles = at<muon::BigTile>(plan, p.off_big_tab[1]);
+    g.t8 = (int)p.big_tab[1].size();
+    if ((e = timed(plan, muon::kClsPoly, s, timing, [&] { return muon::launch_big(muon::kBigPoly, g, s); })) != hipSuccess)
       return e;
-    muon::ApplyBigLaunch al{};
-    al.r16 = r16;
-    al.xt_old = plan->ws + bp.off_xt[src];
-    al.x_new = plan->ws + bp.off_x[dst];
-    al.xt_new = plan->ws + bp.off_xt[dst];
-    al.scale = sfirst;
-    al.sc = sc;
-    al.tiles = tfull;
-    al.t8 = t8full;
-    al.mp = bp.mp;
-    al.np = bp.np;
-    al.m = bp.m;
-    al.n = bp.n;
-    al.count = cnt;
-    al.final_round = it == ns - 1;
-    al.mats = at<muon::DevMat>(plan, bp.off_mats);
-    al.ptrs = at<muon::PtrEntry>(plan, p.off_ptrs);
-    if ((e = timed(plan, muon::kClsApply, s, timing, [&] { return muon::launch_apply_big(al, s); })) != hipSuccess)
+    g.tiles = at<muon::BigTile>(plan, p.off_big_tab[2]);
+    g.t8 = (int)p.big_tab[2].size();
+    const muon::BigKind k = it == ns - 1 ? muon::kBigFinal : muon::kBigApply;
+    if ((e = timed(plan, muon::kClsApply, s, timing, [&] { return muon::launch_big(k, g, s); })) != hipSuccess)
       return e;
   }
   return hipSuccess;
@@ -207,7 +189,7 @@ hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, 
     muon::Update0Launch u{mats, ptrs, sc, scale, bp.m, bp.n, cnt};
     return timed(plan, muon::kClsUpdate, s, timing, [&] { return muon::launch_update0(u, s); });
   }
-  if (bp.big) return enqueue_big_rounds(plan, bp, ns, s, timing);
+  if (bp.big) return hipSuccess;  // rounds run grouped over all large buckets
   for (int it = 0; it < ns; ++it) {
     const int src = it & 1, dst = src ^ 1;
     const float* sfirst = it == 0 ? scale : nullptr;
@@ -266,6 +248,7 @@ hipError_t enqueue_buckets(muon_plan_t plan, int ns, hipStream_t s, bool timing,
     if (e != hipSuccess) return e;
     first = nullptr;
   }
+  if (!plan->p.big.empty() && ns > 0) return enqueue_big_rounds(plan, ns, s, timing);
   return hipSuccess;
 }
 
@@ -352,13 +335,34 @@ int muon_plan_create(const muon_param_desc_t* descs, int32_t n_params, const muo
     }
     e = hipMemcpy(plan->ws + bp.off_mats, table.data(), sizeof(muon::DevMat) * table.size(),
                   hipMemcpyHostToDevice);
-    if (e == hipSuccess && bp.big) {
-      e = hipMemcpy(plan->ws + bp.off_tiles_sym, bp.tiles_sym.data(),
-                    sizeof(uint32_t) * bp.tiles_sym.size(), hipMemcpyHostToDevice);
-      if (e == hipSuccess)
-        e = hipMemcpy(plan->ws + bp.off_tiles_full, bp.tiles_full.data(),
-                      sizeof(uint32_t) * bp.tiles_full.size(), hipMemcpyHostToDevice);
+  }
+  if (e == hipSuccess && !p.big.empty()) {
+    std::vector<muon::BigBucket> bbs;
+    for (int b : p.big) {
+      const muon::BucketPlan& bp = p.buckets[b];
+      muon::BigBucket bb{};
+      for (int i = 0; i < 2; ++i) {
+        bb.x[i] = plan->ws + bp.off_x[i];
+        bb.xt[i] = plan->ws + bp.off_xt[i];
+      }
+      bb.a32 = at<float>(plan, bp.off_a32);
+      bb.e16 = at<uint16_t>(plan, bp.off_a16);
+      bb.dg = at<float>(plan, bp.off_dg);
+      bb.r16 = at<uint16_t>(plan, bp.off_phi);
+      bb.scale = at<float>(plan, bp.off_scale);
+      bb.mats = at<muon::DevMat>(plan, bp.off_mats);
+      bb.m = bp.m;
+      bb.n = bp.n;
+      bb.mp = bp.mp;
+      bb.np = bp.np;
+      bb.vec = (bp.m % 4 == 0) && (bp.n % 4 == 0);
+      bbs.push_back(bb);
     }
+    e = hipMemcpy(plan->ws + p.off_big_params, bbs.data(), sizeof(muon::BigBucket) * bbs.size(),
+                  hipMemcpyHostToDevice);
+    for (int ph = 0; ph < 3 && e == hipSuccess; ++ph)
+      e = hipMemcpy(plan->ws + p.off_big_tab[ph], p.big_tab[ph].data(),
+                    sizeof(muon::BigTile) * p.big_tab[ph].size(), hipMemcpyHostToDevice);
   }
   if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&plan->pinned),
                                          sizeof(muon::PtrEntry) * p.n_params, hipHostMallocDefault);

@@ -99,54 +99,23 @@ struct ApplyLaunch {
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
 
 // ---------------------------------------------------------------- streamed, large bf16 buckets
-// Products on 256 x 256 tiles in the order of a planner-built tile table
-// (entries tm | tn << 16; kNoTile pads the table to a multiple of 8).
-
-// A = s2 X X^T -> a32 (float), dg = diag(A) (float), e16 = A - diag(A) (bf16).
-struct GramBigLaunch {
-  const void* x;          // X [count][mp][np], bf16
-  float* a32;
-  uint16_t* e16;
-  float* dg;              // [count][mp]
-  const float* scale;     // {s, s^2} per slice on the first round, else null
-  const uint32_t* tiles;  // upper-triangle tiles
-  int t8;
-  int64_t mp, np;
-  int count;
-};
-hipError_t launch_gram_big(const GramBigLaunch& a, hipStream_t s);
-
-// R = (a - 1) I + b A + c A^2, with A^2 = E E + diag(d) A + A diag(d) - diag(d)^2 (bf16 out).
-struct PolyBigLaunch {
-  const uint16_t* e16;
-  const float* a32;
-  const float* dg;
-  uint16_t* r16;
+// One launch per product phase covers every large bucket; the tile table
+// (entries: bucket, slice, 256 x 256 output tile) fixes the order.
+enum BigKind { kBigGram = 0, kBigPoly = 1, kBigApply = 2, kBigFinal = 3 };
+struct BigArgs {
+  const BigBucket* buckets;
+  const BigTile* tiles;
+  int t8;                 // table length (multiple of 8)
+  int src;                // this round reads X[src], X^T[src]
+  int first;              // first round: fold the normalisation scale in
   const DevScalars* sc;
-  const uint32_t* tiles;  // upper-triangle tiles
-  int t8;
-  int64_t mp;
-  int count;
-};
-hipError_t launch_poly_big(const PolyBigLaunch& a, hipStream_t s);
-
-// X' = scale (X + R X); the final round subtracts lr X' from W instead.
-struct ApplyBigLaunch {
-  const uint16_t* r16;
-  const void* xt_old;     // X^T [count][np][mp]
-  void* x_new;
-  void* xt_new;
-  const float* scale;     // null after the first round
-  const DevScalars* sc;
-  const uint32_t* tiles;  // all tiles of [mp, np]
-  int t8;
-  int64_t mp, np, m, n;
-  int count;
-  int final_round;
-  const DevMat* mats;
   const PtrEntry* ptrs;
 };
-hipError_t launch_apply_big(const ApplyBigLaunch& a, hipStream_t s);
+//  kBigGram   A = s2 X X^T -> a32, dg = diag(A), e16 = A - diag(A) (bf16)
+//  kBigPoly   R = (a - 1) I + b A + c (E E + diag(d) A + A diag(d) - diag(d)^2) -> r16
+//  kBigApply  X'[src^1] = s (X + R X), with X'^T alongside
+//  kBigFinal  W <- W - lr s (X + R X) through each slice's storage layout
+hipError_t launch_big(BigKind kind, const BigArgs& a, hipStream_t s);
 
 // ns_steps == 0: W -= lr * s * M.
 struct Update0Launch {

@@ -44,4 +44,26 @@ struct DevMat {
   int64_t slice_off;   // element offset of the slice inside its parameter
 };
 
+// Large bf16 buckets run each product phase as one launch over all of
+// them: a tile table entry names the bucket, the slice and the output tile.
+struct BigTile {
+  uint32_t bz;  // bucket << 24 | slice; kNoTile marks padding
+  uint32_t mn;  // tm | tn << 16 (256 x 256 output tiles)
+};
+
+// Device addresses of one large bucket's workspace (filled at plan creation).
+struct BigBucket {
+  char* x[2];          // X ping-pong, [count][mp][np] bf16
+  char* xt[2];         // X^T ping-pong, [count][np][mp] bf16
+  float* a32;          // A, [count][mp][mp]
+  uint16_t* e16;       // A without its diagonal, bf16
+  float* dg;           // diagonal of A, [count][mp]
+  uint16_t* r16;       // (a - 1) I + b A + c A^2, bf16
+  float* scale;        // [count][2] = {s, s^2}
+  const DevMat* mats;  // slice table
+  int64_t m, n, mp, np;
+  int32_t vec;         // m and n are multiples of 4 (whole 16-byte W groups)
+  int32_t pad;
+};
+
 }  // namespace muon

@@ -1,6 +1,8 @@
 // planner.cpp -- validation, orientation, shape buckets and workspace layout.
 #include "planner.h"
 
+#include <algorithm>
+
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -196,18 +198,26 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
       bp.off_plo = bp.p_hilo ? ws.take(msz * 2) : 0;
       bp.off_sq = ws.take(cnt * bp.km_tiles * sizeof(float));
       bp.off_scale = ws.take(cnt * 2 * sizeof(float));
-      if (bp.big) {
-        bp.off_dg = ws.take(cnt * bp.mp * sizeof(float));
-        const int tm = (int)(bp.mp / kBigTile), tn = (int)(bp.np / kBigTile);
-        bp.tiles_sym = tile_order(tm, tm, true);
-        bp.tiles_full = tile_order(tm, tn, false);
-        bp.off_tiles_sym = ws.take(bp.tiles_sym.size() * sizeof(uint32_t));
-        bp.off_tiles_full = ws.take(bp.tiles_full.size() * sizeof(uint32_t));
-      }
+      if (bp.big) bp.off_dg = ws.take(cnt * bp.mp * sizeof(float));
       p.launches_fixed += 2;   // momentum, norm
-      p.launches_per_ns += 3;  // gram, poly, apply (the last apply also updates W)
+      if (!bp.big) p.launches_per_ns += 3;  // gram, poly, apply (the last apply also updates W)
     }
     bp.ws_bytes = ws.take(0) - bp.ws_begin;
+  }
+  // Large buckets share one launch per product phase.
+  for (int b = 0; b < (int)p.buckets.size(); ++b)
+    if (p.buckets[b].big) p.big.push_back(b);
+  if (p.big.size() > 255) {
+    *err = "too many distinct large shapes in one plan (at most 255)";
+    return MUON_ERR_UNSUPPORTED;
+  }
+  if (!p.big.empty()) {
+    p.launches_per_ns += 3;
+    p.off_big_params = ws.take(p.big.size() * sizeof(BigBucket));
+    for (int ph = 0; ph < 3; ++ph) {
+      p.big_tab[ph] = big_table(p, ph);
+      p.off_big_tab[ph] = ws.take(p.big_tab[ph].size() * sizeof(BigTile));
+    }
   }
   p.ws_total = align_up(ws.top, 256);
   if (p.workspace_limit != 0 && p.ws_total > p.workspace_limit) {
@@ -220,15 +230,48 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
   return MUON_OK;
 }
 
-std::vector<uint32_t> tile_order(int tiles_m, int tiles_n, bool sym) {
-  constexpr int kRows = 4, kCols = 8;
-  std::vector<uint32_t> t;
-  for (int i0 = 0; i0 < tiles_m; i0 += kRows)
-    for (int j0 = sym ? (i0 / kCols) * kCols : 0; j0 < tiles_n; j0 += kCols)
-      for (int i = i0; i < i0 + kRows && i < tiles_m; ++i)
-        for (int j = j0; j < j0 + kCols && j < tiles_n; ++j)
-          if (!sym || j >= i) t.push_back((uint32_t)i | ((uint32_t)j << 16));
-  while (t.size() % 8) t.push_back(kNoTile);
+std::vector<BigTile> big_table(const Plan& p, int phase) {
+  constexpr int kRows = 4, kCols = 8, kXcd = 8;
+  struct Block {
+    int64_t k;  // contraction length of every tile in the block
+    std::vector<BigTile> tiles;
+  };
+  std::vector<Block> blocks;
+  for (int bi = 0; bi < (int)p.big.size(); ++bi) {
+    const BucketPlan& bp = p.buckets[p.big[bi]];
+    const int tm = (int)(bp.mp / kBigTile);
+    const int tn = phase == 2 ? (int)(bp.np / kBigTile) : tm;
+    const bool sym = phase != 2;
+    const int64_t k = phase == 0 ? bp.np : bp.mp;
+    for (int z = 0; z < (int)bp.slices.size(); ++z)
+      for (int i0 = 0; i0 < tm; i0 += kRows)
+        for (int j0 = sym ? (i0 / kCols) * kCols : 0; j0 < tn; j0 += kCols) {
+          Block blk{k, {}};
+          for (int i = i0; i < i0 + kRows && i < tm; ++i)
+            for (int j = j0; j < j0 + kCols && j < tn; ++j)
+              if (!sym || j >= i)
+                blk.tiles.push_back(BigTile{(uint32_t)bi << 24 | (uint32_t)z, (uint32_t)i | (uint32_t)j << 16});
+          if (!blk.tiles.empty()) blocks.push_back(std::move(blk));
+        }
+  }
+  std::stable_sort(blocks.begin(), blocks.end(), [](const Block& x, const Block& y) { return x.k > y.k; });
+  std::vector<BigTile> part[kXcd];
+  int64_t load[kXcd] = {};
+  for (const Block& blk : blocks) {
+    int x = 0;
+    for (int i = 1; i < kXcd; ++i)
+      if (load[i] < load[x]) x = i;
+    part[x].insert(part[x].end(), blk.tiles.begin(), blk.tiles.end());
+    load[x] += blk.k * (int64_t)blk.tiles.size();
+  }
+  size_t len = 0;
+  for (auto& v : part) len = std::max(len, v.size());
+  std::vector<BigTile> t;
+  t.reserve(len * kXcd);
+  for (auto& v : part) {
+    v.resize(len, BigTile{kNoTile, 0});
+    t.insert(t.end(), v.begin(), v.end());
+  }
   return t;
 }
 

@@ -42,9 +42,7 @@ struct BucketPlan {
   int km_tiles = 0;         // momentum-kernel tiles per slice
   uint64_t off_x[2] = {0, 0}, off_xt[2] = {0, 0};
   uint64_t off_a32 = 0, off_a16 = 0, off_phi = 0, off_plo = 0, off_sq = 0, off_scale = 0;
-  uint64_t off_dg = 0;                         // big: diagonal of A per slice
-  uint64_t off_tiles_sym = 0, off_tiles_full = 0;  // big: tile tables (uint32)
-  std::vector<uint32_t> tiles_sym, tiles_full;     // their contents
+  uint64_t off_dg = 0;      // big: diagonal of A per slice
 
   uint64_t off_mats = 0;    // this bucket's DevMat table
   uint64_t ws_begin = 0, ws_bytes = 0;
@@ -64,6 +62,12 @@ struct Plan {
   std::vector<Slice> slices;
   std::vector<BucketPlan> buckets;
   uint64_t off_scalars = 0, off_err = 0, off_ptrs = 0;
+  // Large bf16 buckets: their indices, the device BigBucket array and one
+  // tile table per product phase (kBigGram, kBigPoly, kBigApply).
+  std::vector<int> big;
+  uint64_t off_big_params = 0;
+  std::vector<BigTile> big_tab[3];
+  uint64_t off_big_tab[3] = {0, 0, 0};
   uint64_t ws_total = 0;
   int launches_fixed = 0, launches_per_ns = 0;
 };
@@ -77,10 +81,12 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
 
 void fill_info(const Plan& p, muon_plan_info_t* info);
 
-// Tile order of a 256 x 256-tiled product with tiles_m x tiles_n output
-// tiles (upper triangle only when sym), padded with kNoTile to a multiple
-// of 8.  Tiles are grouped into blocks of 4 tile rows x 8 tile columns, so the
-// 32 workgroups an XCD runs at once share 4 row panels and 8 column panels.
-std::vector<uint32_t> tile_order(int tiles_m, int tiles_n, bool sym);
+// Tile table of one product phase over the plan's large buckets (phase 0:
+// X X^T, 1: E E, 2: R X).  Output tiles are grouped in blocks of 4 tile rows
+// x 8 tile columns of one slice (upper triangle only for the symmetric
+// phases); blocks are dealt, longest contraction first, to the 8 XCD
+// stretches of the table, each block to the stretch with the least work so
+// far; stretches are padded with kNoTile to a common length.
+std::vector<BigTile> big_table(const Plan& p, int phase);
 
 }  // namespace muon

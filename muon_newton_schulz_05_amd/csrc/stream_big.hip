@@ -11,8 +11,8 @@
 //   poly   R = (a - 1) I + b A + c A^2 with
 //            A^2 = E E + diag(d) A + A diag(d) - diag(d)^2,
 //          where only E E runs on the matrix cores; R is rounded to bf16;
-//   apply  X' = s (X + R X) = s (a X + (b A + c A^2) X); the X term enters the
-//          accumulators exactly through an identity block on the matrix cores.
+//   apply  X' = s (X + R X) = s (a X + (b A + c A^2) X); the X term is added
+//          in float32 in the epilogue (bf16 X is exact in float32).
 //
 // Keeping the diagonal out of the bf16 operands and shifting the polynomial by
 // the identity leaves bf16 rounding only on the small off-diagonal part of A
@@ -22,44 +22,72 @@
 //
 // The kernel: 256 x 256 output tile per 256-thread workgroup, each of the
 // four waves owning 128 x 128 (4 x 4 blocks of v_mfma_f32_32x32x16_bf16).
-// Operand k-slices of 64 elements (128 bytes a row) go from HBM straight into
-// LDS with gfx950's global_load_lds_dwordx4, two stages deep; lane l of a
-// load lands at byte 16 l of its 1 KB destination, and each lane fetches the
-// 16-byte chunk c of its row that belongs in slot c ^ ((row / 2) mod 8), so
-// the 16-byte fragment reads of 16 consecutive rows hit distinct bank groups.
-// Output tiles come from a table that the planner orders for cache reuse;
-// workgroups are dealt to the 8 XCDs round robin, so workgroup b takes table
-// entry (b mod 8) * T/8 + b/8 and every XCD walks a contiguous stretch.
+// Operand k-slices of kBK elements go from HBM straight into LDS with
+// gfx950's global_load_lds_dwordx4, kNS stages deep with one barrier per
+// slice; lane l of a load lands at byte 16 l of its 1 KB destination, and
+// each lane fetches the 16-byte chunk of its row that belongs in its slot
+// under the XOR swizzle below, so the 16-byte fragment reads of 16
+// consecutive rows hit distinct bank groups.  (Measured on the large
+// workloads: 64-element slices in 2 stages, 32 in 3 and 32 in 4 are within
+// 2% of each other; the matrix cores, not load latency, set the pace.)
+// One launch per phase covers every large bucket.  Output tiles come from a
+// table that the planner builds: workgroups are dealt to the 8 XCDs round
+// robin, so workgroup b takes entry (b mod 8) * T/8 + b/8 and XCD x walks the
+// x-th stretch of the table.  Each stretch holds whole blocks of 4 x 8 tiles
+// (the 32 workgroups an XCD runs at once share 4 row and 8 column panels in
+// its L2), longest contraction first, with the work balanced over the XCDs.
 // Symmetric products (X X^T, E E) list only tiles on or above the diagonal;
 // an off-diagonal tile is also written to its mirror position.  The epilogue
 // turns the accumulators around in LDS and writes whole rows of 16-byte
 // pieces, in the tile's own orientation and, where needed, transposed.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace muon {
 namespace {
 
-constexpr int kBK = 64;                       // bf16 elements of k per slice
-constexpr int kStage = (kBigTile + kBigTile) * 128;  // bytes per stage
+constexpr int kBK = 64;                      // bf16 elements of k per slice
+constexpr int kNS = 2;                       // LDS stages (slices in flight: kNS - 1)
+constexpr int kRB = 2 * kBK;                 // bytes of one tile row per slice
+constexpr int kCPR = kRB / 16;               // 16-byte chunks per row
+constexpr int kRPI = 1024 / kRB;             // rows filled by one 1 KB load instruction
+constexpr int kRW = 256 / kRB;               // rows per 256-byte span of the LDS banks
+constexpr int kLI = kBigTile / kRPI / 4;     // load instructions per wave, operand and slice
+constexpr int kStage = 2 * kBigTile * kRB;   // bytes per stage (A and B tiles)
+constexpr int kStageBytes = 128 * 256 * 4;   // epilogue staging: 128 rows of 256 floats
+constexpr int kLds = kNS * kStage > kStageBytes ? kNS * kStage : kStageBytes;
 constexpr int kViewRow = 1, kViewCol = 2;
+static_assert(kBK % 16 == 0 && kCPR <= 8 && kNS >= 2 && kLds <= 160 * 1024, "tile geometry");
 
 #define LDS_PTR __attribute__((address_space(3)))
 
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// Chunk c of tile row r sits in LDS slot c ^ swz(r): the 16 rows that one
+// 16-lane group of a fragment read touches then cover 16 distinct 16-byte
+// bank groups.
+__device__ __forceinline__ int swz(int r) { return (r / kRW) & (kCPR - 1); }
+
+// Wait until at most `slices` k-slices of this wave's operand loads are in flight.
+__device__ __forceinline__ void wait_loads(int slices) {
+  static_assert(kNS - 2 <= 3, "extend the cases");
+  switch (slices) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLI) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kLI) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * kLI) : "memory"); break;
+  }
+}
 
 __device__ __forceinline__ f32x16_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-struct BigCore {
-  const char* a;          // row operand, matrix 0 (bf16, rows contiguous along k)
-  const char* b;          // column operand, matrix 0
-  int64_t lda, ldb;       // row strides in elements
-  int64_t sa, sb;         // matrix strides in elements
-  int64_t K;              // contraction length, multiple of kBK
-  const uint32_t* tiles;  // tile table: tm | tn << 16, kNoTile for padding
-  int t8;                 // table length (multiple of 8)
+// Operands of one tile's product: rows of A and of B are contiguous along k.
+struct Operands {
+  const char* a;
+  const char* b;
+  int64_t lda, ldb, K;
 };
 
 __device__ __forceinline__ void st_bf16x4(uint16_t* p, f32x4_t v) {
@@ -74,46 +102,48 @@ __device__ __forceinline__ void st_f32x4(float* p, f32x4_t v) {
 }
 
 template <class Epi>
-__global__ __launch_bounds__(256) void k_gemm_big(BigCore c, Epi epi) {
+__global__ __launch_bounds__(256) void k_gemm_big(BigArgs g) {
   constexpr int FM = 4, FN = 4;    // 32x32 blocks per wave along i and j
-  constexpr int IA = 8, IB = 8;    // load instructions per wave and slice
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) char lds[kLds];
 
   int b = blockIdx.x;
-  b = (b & 7) * (c.t8 >> 3) + (b >> 3);
-  const uint32_t t = c.tiles[b];
-  if (t == kNoTile) return;  // uniform over the workgroup, before any barrier
-  const int tm = (int)(t & 0xFFFFu), tn = (int)(t >> 16);
+  b = (b & 7) * (g.t8 >> 3) + (b >> 3);
+  const BigTile t = g.tiles[b];
+  if (t.bz == kNoTile) return;  // uniform over the workgroup, before any barrier
+  const BigBucket& bb = g.buckets[t.bz >> 24];  // read in place: fields are indexed by round parity
+  const int z = (int)(t.bz & 0xFFFFFFu);
+  const int tm = (int)(t.mn & 0xFFFFu), tn = (int)(t.mn >> 16);
+  const Operands op = Epi::operands(g, bb, z);
 
-  const int z = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // The wave index is uniform over the wave; saying so keeps branches on it scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const char* A = c.a + ((int64_t)z * c.sa + (int64_t)tm * kBigTile * c.lda) * 2;
-  const char* B = c.b + ((int64_t)z * c.sb + (int64_t)tn * kBigTile * c.ldb) * 2;
-  const int nk = (int)(c.K / kBK);
+  const char* A = op.a + (int64_t)tm * kBigTile * op.lda * 2;
+  const char* B = op.b + (int64_t)tn * kBigTile * op.ldb * 2;
+  const int nk = (int)(op.K / kBK);
 
-  // Instruction u of wave w fills rows 8 (w + 4 u) .. + 7 of an operand tile.
-  uint32_t oa[IA], ob[IB];
+  // Load instruction u of wave w fills rows kRPI (w + 4 u) .. + kRPI - 1 of an
+  // operand tile; lane l lands in slot l mod kCPR of row l / kCPR and fetches
+  // the chunk that belongs there.
+  uint32_t oa[kLI], ob[kLI];
 #pragma unroll
-  for (int u = 0; u < IA; ++u) {
-    const int row = 8 * (wave + 4 * u) + (lane >> 3);
-    oa[u] = (uint32_t)(row * c.lda * 2 + (((lane & 7) ^ swz(row)) << 4));
-  }
-#pragma unroll
-  for (int u = 0; u < IB; ++u) {
-    const int row = 8 * (wave + 4 * u) + (lane >> 3);
-    ob[u] = (uint32_t)(row * c.ldb * 2 + (((lane & 7) ^ swz(row)) << 4));
+  for (int u = 0; u < kLI; ++u) {
+    const int row = kRPI * (wave + 4 * u) + lane / kCPR;
+    const int chunk = (lane % kCPR) ^ swz(row);
+    oa[u] = (uint32_t)(row * op.lda * 2 + chunk * 16);
+    ob[u] = (uint32_t)(row * op.ldb * 2 + chunk * 16);
   }
   auto issue = [&](int kt, int stage) {
     char LDS_PTR* base = (char LDS_PTR*)(lds + stage * kStage);
 #pragma unroll
-    for (int u = 0; u < IA; ++u)
-      __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(A + (int64_t)kt * 128 + oa[u]),
+    for (int u = 0; u < kLI; ++u)
+      __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(A + (int64_t)kt * kRB + oa[u]),
                                        (void LDS_PTR*)(base + (wave + 4 * u) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int u = 0; u < IB; ++u)
-      __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(B + (int64_t)kt * 128 + ob[u]),
-                                       (void LDS_PTR*)(base + kBigTile * 128 + (wave + 4 * u) * 1024), 16, 0, 0);
+    for (int u = 0; u < kLI; ++u)
+      __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(B + (int64_t)kt * kRB + ob[u]),
+                                       (void LDS_PTR*)(base + kBigTile * kRB + (wave + 4 * u) * 1024), 16, 0, 0);
   };
 
   f32x16_t acc[FM][FN];
@@ -123,75 +153,94 @@ __global__ __launch_bounds__(256) void k_gemm_big(BigCore c, Epi epi) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
   const int ra = wm * 128 + (lane & 31), rb = kBigTile + wn * 128 + (lane & 31);
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      issue(kt + 1, cur ^ 1);
-      // This wave's loads of slice kt are the ones issued before the last IA + IB.
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IA + IB) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    // A bare barrier: the wait above already covers this wave's loads of
-    // slice kt, and a fenced __syncthreads would also wait for slice kt + 1.
-    __builtin_amdgcn_s_barrier();  // every wave's part of slice kt is in LDS
-    const char* st = lds + cur * kStage;
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
+  // Multiply one resident slice.  The fragments of k-substep s + 1 are read
+  // from LDS while the 16 products of substep s run (two fragment sets), and
+  // the scheduling hints interleave one fragment read with every two
+  // products, so the matrix cores are not left waiting on LDS.
+  constexpr int kSub = kBK / 16;
+  auto multiply = [&](const char* st) {
+    bf16x8_t af[2][FM], bfr[2][FN];
+    auto fragments = [&](int s, int buf) {
       const int ck = 2 * s + (lane >> 5);
-      bf16x8_t af[FM], bfr[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = ra + 32 * i;
-        af[i] = *reinterpret_cast<const bf16x8_t*>(st + r * 128 + ((ck ^ swz(r)) << 4));
+        af[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + r * kRB + ((ck ^ swz(r)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int r = rb + 32 * j;
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + r * 128 + ((ck ^ swz(r)) << 4));
+        bfr[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + r * kRB + ((ck ^ swz(r)) << 4));
       }
+    };
+    fragments(0, 0);
+#pragma unroll
+    for (int s = 0; s < kSub; ++s) {
+      if (s + 1 < kSub) fragments(s + 1, (s + 1) & 1);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(af[i], bfr[j], acc[i][j]);
-      if constexpr (Epi::kIdentity) {
-        // acc += I B over the slices that run along the tile's own rows:
-        // k-substep s of slice kt covers tile rows 64 (kt mod 4) + 16 s ..,
-        // which lie in block blk of the waves with this wm.
-        if ((kt >> 2) == tm) {
-          const int blk = 2 * (kt & 3) + (s >> 1) - 4 * wm;
-          if (blk >= 0 && blk < FM) {
-            // Row operand lane l holds A[l mod 32][8 (l / 32) + e], e = 0..7.
-            const int d = (lane & 31) - 16 * (s & 1) - 8 * (lane >> 5);
-            bf16x8_t id;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) id[e] = d == e ? (__bf16)1.0f : (__bf16)0.0f;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-              if (i == blk) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(id, bfr[j], acc[i][j]);
-              }
-          }
-        }
-      }
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(af[s & 1][i], bfr[s & 1][j], acc[i][j]);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // slice kt fully read before its stage is refilled
+    // Order: the first substep's 8 reads, then (2 products, 1 read) x 8 per
+    // following substep, then the last substep's 16 products.
+    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+#pragma unroll
+    for (int s = 0; s + 1 < kSub; ++s)
+#pragma unroll
+      for (int q = 0; q < FM + FN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+  };
+
+  // kNS - 1 slices in flight.  Iteration kt: wait for this wave's loads of
+  // slice kt; one barrier then says that every wave's part of slice kt is in
+  // LDS and that every wave has finished reading slice kt - 1, whose stage is
+  // refilled with slice kt + kNS - 1 before slice kt is multiplied.  (One
+  // loop: peeling the last slices off made the compiler spill the
+  // accumulators around the epilogue.)
+#pragma unroll
+  for (int p = 0; p < kNS - 1; ++p)
+    if (p < nk) issue(p, p);
+  int stage = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_loads(min(kNS - 2, nk - 1 - kt));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS access moves across the barrier
+    if (kt + kNS - 1 < nk) issue(kt + kNS - 1, stage == 0 ? kNS - 1 : stage - 1);
+    multiply(lds + stage * kStage);
+    stage = stage == kNS - 1 ? 0 : stage + 1;
   }
+  __syncthreads();  // every wave is done with the stages before they hold the epilogue
 
   // ---- epilogue.  Accumulator layout of a 32x32 block: lane l, register r ->
   // row 8 (r / 4) + 4 (l / 32) + r mod 4, column l mod 32.  Half of the tile
-  // (128 x 256 float32 = 128 KB) is staged at a time.
-  const auto cx = epi.context(z);
-  const int views = epi.views(cx, tm == tn);
-  const float pre = epi.prescale(cx);
+  // (128 x 256 float32 = 128 KB) is staged at a time; each half is then
+  // written as whole rows of 16-byte pieces.  What an epilogue reads besides
+  // the product (old X, W, A, the diagonal) is loaded kBatch pieces at a
+  // time, the first batch before the staging so its latency is hidden.
+  const auto cx = Epi::context(g, bb, z);
+  const int views = Epi::views(cx, tm == tn);
+  const float pre = Epi::prescale(cx);
   float* stg = reinterpret_cast<float*>(lds);
-  if (views & kViewRow) {
-    // Row view: staged [i][j]; 16-byte slot s of row r sits at s ^ (8 ((r / 4) mod 2)).
-#pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
+  auto pass = [&](auto view_tag, int h) {
+    constexpr int V = decltype(view_tag)::value;
+    constexpr int NB = Epi::kBatch;
+    const int row0 = (V == kViewRow ? tm : tn) * kBigTile + h * 128;
+    const int col0 = (V == kViewRow ? tn : tm) * kBigTile;
+    typename Epi::Aux aux[NB];
+    auto load_batch = [&](int b0) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int idx = (b0 + u) * 256 + tid;
+        aux[u] = Epi::load(cx, V, row0 + (idx >> 6), col0 + 4 * (idx & 63));
+      }
+    };
+    load_batch(0);
+    if constexpr (V == kViewRow) {
+      // Staged [i][j]; 16-byte slot s of row r sits at s ^ (8 ((r / 4) mod 2)).
       if (wm == h) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -207,23 +256,9 @@ __global__ __launch_bounds__(256) void k_gemm_big(BigCore c, Epi epi) {
                 stg[r * 256 + ps * 4 + (col & 3)] = pre * acc[i][j][4 * q + u];
               }
       }
-      __syncthreads();
-#pragma unroll 4
-      for (int it = 0; it < 32; ++it) {
-        const int idx = it * 256 + tid;
-        const int r = idx >> 6, s = idx & 63;
-        const int ps = s ^ (((r >> 2) & 1) << 3);
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + r * 256 + ps * 4);
-        epi.store(cx, kViewRow, tm * kBigTile + h * 128 + r, tn * kBigTile + s * 4, v);
-      }
-      __syncthreads();
-    }
-  }
-  if (views & kViewCol) {
-    // Column view: staged [j][i] (four consecutive i per lane are one 16-byte
-    // slot); slot s of row r sits at s ^ (r mod 16).
-#pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
+    } else {
+      // Staged [j][i] (four consecutive i per lane are one 16-byte slot);
+      // slot s of row r sits at s ^ (r mod 16).
       if (wn == h) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -242,46 +277,67 @@ __global__ __launch_bounds__(256) void k_gemm_big(BigCore c, Epi epi) {
               *reinterpret_cast<f32x4_t*>(stg + rc * 256 + ps * 4) = v;
             }
       }
-      __syncthreads();
-#pragma unroll 4
-      for (int it = 0; it < 32; ++it) {
-        const int idx = it * 256 + tid;
-        const int r = idx >> 6, s = idx & 63;
-        const int ps = s ^ (r & 15);
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + r * 256 + ps * 4);
-        epi.store(cx, kViewCol, tn * kBigTile + h * 128 + r, tm * kBigTile + s * 4, v);
-      }
-      __syncthreads();
     }
+    __syncthreads();
+#pragma unroll
+    for (int b0 = 0; b0 < 32; b0 += NB) {
+      if (b0 > 0) load_batch(b0);
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int idx = (b0 + u) * 256 + tid;
+        const int r = idx >> 6, sl = idx & 63;
+        const int ps = V == kViewRow ? sl ^ (((r >> 2) & 1) << 3) : sl ^ (r & 15);
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + r * 256 + ps * 4);
+        Epi::store(cx, V, row0 + r, col0 + 4 * sl, v, aux[u]);
+      }
+    }
+    __syncthreads();
+  };
+  if (views & kViewRow) {
+    pass(std::integral_constant<int, kViewRow>{}, 0);
+    pass(std::integral_constant<int, kViewRow>{}, 1);
+  }
+  if (views & kViewCol) {
+    pass(std::integral_constant<int, kViewCol>{}, 0);
+    pass(std::integral_constant<int, kViewCol>{}, 1);
   }
 }
 
 // ------------------------------------------------------------------ epilogues
-// store(cx, view, r, c, v): v holds entries (r, c .. c+3) of the output in the
-// given view (kViewCol: of the transposed output); c is a multiple of 4.
+// Each phase supplies its operands and an epilogue.  load(cx, view, r, c)
+// fetches what the epilogue needs besides the product for entries
+// (r, c .. c+3) of the output in the given view (kViewCol: of the transposed
+// output), c a multiple of 4; store(cx, view, r, c, v, aux) writes them.
+
+__device__ __forceinline__ f32x4_t ld_bf16x4(const uint16_t* p) {
+  const u32x2_t w = *reinterpret_cast<const MUON_GLOBAL u32x2_t*>(as_global(p));
+  return f32x4_t{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+}
 
 // A = s2 X X^T: float32 A, float32 diagonal, bf16 A with a zero diagonal.
-struct GramEpiBig {
-  static constexpr bool kIdentity = false;
-  float* a32;
-  uint16_t* e16;
-  float* dg;
-  const float* scale;  // {s, s^2} per slice on the first round, else null
-  int64_t mp;
+struct GramPhase {
+  static __device__ Operands operands(const BigArgs& g, const BigBucket& bb, int z) {
+    const char* x = bb.x[g.src] + (int64_t)z * bb.mp * bb.np * 2;
+    return Operands{x, x, bb.np, bb.np, bb.np};
+  }
   struct Ctx {
     float* a32;
     uint16_t* e16;
     float* dg;
+    int64_t mp;
     float pre;
   };
-  __device__ Ctx context(int z) const {
-    const int64_t o = (int64_t)z * mp * mp;
-    return Ctx{a32 + o, e16 + o, dg + (int64_t)z * mp, scale ? scale[2 * z + 1] : 1.f};
+  static __device__ Ctx context(const BigArgs& g, const BigBucket& bb, int z) {
+    const int64_t o = (int64_t)z * bb.mp * bb.mp;
+    return Ctx{bb.a32 + o, bb.e16 + o, bb.dg + (int64_t)z * bb.mp, bb.mp, g.first ? bb.scale[2 * z + 1] : 1.f};
   }
-  __device__ float prescale(const Ctx& x) const { return x.pre; }
-  __device__ int views(const Ctx&, bool diag) const { return diag ? kViewRow : kViewRow | kViewCol; }
-  __device__ void store(const Ctx& x, int, int r, int c, f32x4_t v) const {
-    const int64_t idx = (int64_t)r * mp + c;
+  static __device__ float prescale(const Ctx& x) { return x.pre; }
+  static __device__ int views(const Ctx&, bool diag) { return diag ? kViewRow : kViewRow | kViewCol; }
+  struct Aux {};
+  static constexpr int kBatch = 32;
+  static __device__ Aux load(const Ctx&, int, int, int) { return Aux{}; }
+  static __device__ void store(const Ctx& x, int, int r, int c, f32x4_t v, Aux) {
+    const int64_t idx = (int64_t)r * x.mp + c;
     st_f32x4(x.a32 + idx, v);
     const int d = r - c;  // position of the diagonal in this piece, if any
     if (d >= 0 && d < 4) {
@@ -297,30 +353,37 @@ struct GramEpiBig {
 };
 
 // R = (a - 1) I + b A + c (E E + diag(d) A + A diag(d) - diag(d)^2), in bf16.
-struct PolyEpiBig {
-  static constexpr bool kIdentity = false;
-  const float* a32;
-  const float* dg;
-  uint16_t* r16;
-  const DevScalars* sc;
-  int64_t mp;
+struct PolyPhase {
+  static __device__ Operands operands(const BigArgs&, const BigBucket& bb, int z) {
+    const char* e = reinterpret_cast<const char*>(bb.e16 + (int64_t)z * bb.mp * bb.mp);
+    return Operands{e, e, bb.mp, bb.mp, bb.mp};
+  }
   struct Ctx {
     const float* a32;
     const float* dg;
     uint16_t* r16;
+    int64_t mp;
     float b, c, am1;
   };
-  __device__ Ctx context(int z) const {
-    const int64_t o = (int64_t)z * mp * mp;
-    return Ctx{a32 + o, dg + (int64_t)z * mp, r16 + o, sc->b, sc->c, sc->a - 1.f};
+  static __device__ Ctx context(const BigArgs& g, const BigBucket& bb, int z) {
+    const int64_t o = (int64_t)z * bb.mp * bb.mp;
+    return Ctx{bb.a32 + o, bb.dg + (int64_t)z * bb.mp, bb.r16 + o, bb.mp, g.sc->b, g.sc->c, g.sc->a - 1.f};
   }
-  __device__ float prescale(const Ctx&) const { return 1.f; }
-  __device__ int views(const Ctx&, bool diag) const { return diag ? kViewRow : kViewRow | kViewCol; }
-  __device__ void store(const Ctx& x, int, int r, int c, f32x4_t ee) const {
-    const int64_t idx = (int64_t)r * mp + c;
-    const f32x4_t a = ld_f32x4(x.a32 + idx);
-    const float dr = *reinterpret_cast<const MUON_GLOBAL float*>(as_global(x.dg + r));
-    const f32x4_t dc = ld_f32x4(x.dg + c);
+  static __device__ float prescale(const Ctx&) { return 1.f; }
+  static __device__ int views(const Ctx&, bool diag) { return diag ? kViewRow : kViewRow | kViewCol; }
+  struct Aux {
+    f32x4_t a, dc;  // A (r, c .. c+3) and d (c .. c+3)
+    float dr;       // d (r)
+  };
+  static constexpr int kBatch = 8;
+  static __device__ Aux load(const Ctx& x, int, int r, int c) {
+    return Aux{ld_f32x4(x.a32 + (int64_t)r * x.mp + c), ld_f32x4(x.dg + c),
+               *reinterpret_cast<const MUON_GLOBAL float*>(as_global(x.dg + r))};
+  }
+  static __device__ void store(const Ctx& x, int, int r, int c, f32x4_t ee, const Aux& q) {
+    const int64_t idx = (int64_t)r * x.mp + c;
+    const f32x4_t a = q.a, dc = q.dc;
+    const float dr = q.dr;
     f32x4_t o;
 #define MUON_POLY_ONE(comp, u)                                                      \
     {                                                                               \
@@ -337,137 +400,138 @@ struct PolyEpiBig {
   }
 };
 
-// X' = s (X + R X): written as X' [mp][np] and X'^T [np][mp].
-struct ApplyEpiBig {
-  static constexpr bool kIdentity = true;
-  uint16_t* x_new;
-  uint16_t* xt_new;
-  const float* scale;
-  int64_t mp, np;
+// Operands of R X: rows of R and rows of X^T (both contiguous along k = m).
+__device__ __forceinline__ Operands apply_operands(const BigArgs& g, const BigBucket& bb, int z) {
+  return Operands{reinterpret_cast<const char*>(bb.r16 + (int64_t)z * bb.mp * bb.mp),
+                  bb.xt[g.src] + (int64_t)z * bb.np * bb.mp * 2, bb.mp, bb.mp, bb.mp};
+}
+
+// X' = s (X + R X): X' [mp][np] from the row view, X'^T [np][mp] from the column view.
+struct ApplyPhase {
+  static __device__ Operands operands(const BigArgs& g, const BigBucket& bb, int z) {
+    return apply_operands(g, bb, z);
+  }
   struct Ctx {
-    uint16_t* x;
-    uint16_t* xt;
+    const uint16_t* x_old;
+    const uint16_t* xt_old;
+    uint16_t* x_new;
+    uint16_t* xt_new;
+    int64_t mp, np;
     float pre;
   };
-  __device__ Ctx context(int z) const {
-    const int64_t o = (int64_t)z * mp * np;
-    return Ctx{x_new + o, xt_new + o, scale ? scale[2 * z] : 1.f};
+  static __device__ Ctx context(const BigArgs& g, const BigBucket& bb, int z) {
+    const int64_t o = (int64_t)z * bb.mp * bb.np * 2;
+    return Ctx{reinterpret_cast<const uint16_t*>(bb.x[g.src] + o),
+               reinterpret_cast<const uint16_t*>(bb.xt[g.src] + o),
+               reinterpret_cast<uint16_t*>(bb.x[g.src ^ 1] + o),
+               reinterpret_cast<uint16_t*>(bb.xt[g.src ^ 1] + o), bb.mp, bb.np,
+               g.first ? bb.scale[2 * z] : 1.f};
   }
-  __device__ float prescale(const Ctx& x) const { return x.pre; }
-  __device__ int views(const Ctx&, bool) const { return kViewRow | kViewCol; }
-  __device__ void store(const Ctx& x, int view, int r, int c, f32x4_t v) const {
-    if (view == kViewRow) st_bf16x4(x.x + (int64_t)r * np + c, v);
-    else st_bf16x4(x.xt + (int64_t)r * mp + c, v);
+  static __device__ float prescale(const Ctx&) { return 1.f; }
+  static __device__ int views(const Ctx&, bool) { return kViewRow | kViewCol; }
+  using Aux = u32x2_t;  // old X (r, c .. c+3), bf16
+  static constexpr int kBatch = 16;
+  static __device__ Aux load(const Ctx& x, int view, int r, int c) {
+    const uint16_t* p = view == kViewRow ? x.x_old + (int64_t)r * x.np + c : x.xt_old + (int64_t)r * x.mp + c;
+    return *reinterpret_cast<const MUON_GLOBAL u32x2_t*>(as_global(p));
+  }
+  static __device__ void store(const Ctx& x, int view, int r, int c, f32x4_t v, Aux o) {
+    const int64_t idx = view == kViewRow ? (int64_t)r * x.np + c : (int64_t)r * x.mp + c;
+    const f32x4_t y{x.pre * (v.x + bf16_lo(o.x)), x.pre * (v.y + bf16_hi(o.x)), x.pre * (v.z + bf16_lo(o.y)),
+                    x.pre * (v.w + bf16_hi(o.y))};
+    st_bf16x4((view == kViewRow ? x.x_new : x.xt_new) + idx, y);
   }
 };
 
-// Last round: W <- W - lr s (X + R X), through the slice's own layout (the row
+// Last round: W <- W - lr s (X + R X) through the slice's own layout (the row
 // view for a slice stored [m, n], the column view for one stored [n, m]).
-struct FinalEpiBig {
-  static constexpr bool kIdentity = true;
-  const DevMat* mats;
-  const PtrEntry* ptrs;
-  const float* scale;
-  const DevScalars* sc;
-  int64_t m, n;
-  int vec;  // rows of W are whole 16-byte groups (m and n multiples of 4)
+struct FinalPhase {
+  static __device__ Operands operands(const BigArgs& g, const BigBucket& bb, int z) {
+    return apply_operands(g, bb, z);
+  }
   struct Ctx {
     char* w;
-    int64_t rows, len;  // stored rows and row length of this slice
-    int pdtype;
-    float pre;
-    int view;
+    const uint16_t* xo;  // X (row view) or X^T (column view) of this round
+    int64_t rows, len;   // stored rows and row length of the slice
+    int64_t xstride;     // row stride of xo
+    int pdtype, view, vec;
+    float k;             // lr s
   };
-  __device__ Ctx context(int z) const {
-    const DevMat d = mats[z];
-    const PtrEntry pe = ptrs[d.param];
-    const int esz = d.pdtype == 1 ? 2 : 4;
+  static __device__ Ctx context(const BigArgs& g, const BigBucket& bb, int z) {
+    const DevMat d = bb.mats[z];
+    const PtrEntry pe = g.ptrs[d.param];
     Ctx x;
-    x.w = static_cast<char*>(pe.w) + d.slice_off * esz;
-    x.rows = d.transposed ? n : m;
-    x.len = d.transposed ? m : n;
-    x.pdtype = d.pdtype;
-    x.pre = sc->lr * (scale ? scale[2 * z] : 1.f);
+    x.w = static_cast<char*>(pe.w) + d.slice_off * (d.pdtype == 1 ? 2 : 4);
+    const int64_t o = (int64_t)z * bb.mp * bb.np * 2;
     x.view = d.transposed ? kViewCol : kViewRow;
+    x.xo = reinterpret_cast<const uint16_t*>((d.transposed ? bb.xt[g.src] : bb.x[g.src]) + o);
+    x.xstride = d.transposed ? bb.mp : bb.np;
+    x.rows = d.transposed ? bb.n : bb.m;
+    x.len = d.transposed ? bb.m : bb.n;
+    x.pdtype = d.pdtype;
+    x.vec = bb.vec;
+    x.k = g.sc->lr * (g.first ? bb.scale[2 * z] : 1.f);
     return x;
   }
-  __device__ float prescale(const Ctx&) const { return 1.f; }
-  __device__ int views(const Ctx& x, bool) const { return x.view; }
-  __device__ void store(const Ctx& x, int, int r, int c, f32x4_t v) const {
-    if (r >= x.rows || c >= x.len) return;
+  static __device__ float prescale(const Ctx&) { return 1.f; }
+  static __device__ int views(const Ctx& x, bool) { return x.view; }
+  struct Aux {
+    f32x4_t w;   // W (r, c .. c+3) as float32 (entries past the row end unused)
+    u32x2_t xo;  // old X in this view, bf16
+  };
+  static constexpr int kBatch = 8;
+  static __device__ Aux load(const Ctx& x, int, int r, int c) {
+    Aux q{};
+    if (r >= x.rows || c >= x.len) return q;
+    q.xo = *reinterpret_cast<const MUON_GLOBAL u32x2_t*>(as_global(x.xo + (int64_t)r * x.xstride + c));
     const int64_t idx = (int64_t)r * x.len + c;
-    if (vec && c + 3 < x.len) {
+    if (x.vec && c + 3 < x.len) {
       if (x.pdtype == 1) {  // bfloat16 W
-        MUON_GLOBAL u32x2_t* p = reinterpret_cast<MUON_GLOBAL u32x2_t*>(as_global(x.w) + 2 * idx);
-        const u32x2_t w = *p;
-        *p = u32x2_t{pack_bf16x2(bf16_lo(w.x) - x.pre * v.x, bf16_hi(w.x) - x.pre * v.y),
-                     pack_bf16x2(bf16_lo(w.y) - x.pre * v.z, bf16_hi(w.y) - x.pre * v.w)};
+        const u32x2_t w = *reinterpret_cast<const MUON_GLOBAL u32x2_t*>(as_global(x.w) + 2 * idx);
+        q.w = f32x4_t{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
       } else {
-        MUON_GLOBAL f32x4_t* p = reinterpret_cast<MUON_GLOBAL f32x4_t*>(as_global(x.w) + 4 * idx);
-        const f32x4_t w = *p;
-        *p = f32x4_t{w.x - x.pre * v.x, w.y - x.pre * v.y, w.z - x.pre * v.z, w.w - x.pre * v.w};
+        q.w = *reinterpret_cast<const MUON_GLOBAL f32x4_t*>(as_global(x.w) + 4 * idx);
+      }
+    } else {
+      q.w.x = load_as_f32(x.w, idx, x.pdtype);
+      q.w.y = c + 1 < x.len ? load_as_f32(x.w, idx + 1, x.pdtype) : 0.f;
+      q.w.z = c + 2 < x.len ? load_as_f32(x.w, idx + 2, x.pdtype) : 0.f;
+      q.w.w = c + 3 < x.len ? load_as_f32(x.w, idx + 3, x.pdtype) : 0.f;
+    }
+    return q;
+  }
+  static __device__ void store(const Ctx& x, int, int r, int c, f32x4_t v, const Aux& q) {
+    if (r >= x.rows || c >= x.len) return;
+    const f32x4_t n{q.w.x - x.k * (v.x + bf16_lo(q.xo.x)), q.w.y - x.k * (v.y + bf16_hi(q.xo.x)),
+                    q.w.z - x.k * (v.z + bf16_lo(q.xo.y)), q.w.w - x.k * (v.w + bf16_hi(q.xo.y))};
+    const int64_t idx = (int64_t)r * x.len + c;
+    if (x.vec && c + 3 < x.len) {
+      if (x.pdtype == 1) {  // bfloat16 W, rounded to nearest even
+        *reinterpret_cast<MUON_GLOBAL u32x2_t*>(as_global(x.w) + 2 * idx) =
+            u32x2_t{pack_bf16x2(n.x, n.y), pack_bf16x2(n.z, n.w)};
+      } else {
+        *reinterpret_cast<MUON_GLOBAL f32x4_t*>(as_global(x.w) + 4 * idx) = n;
       }
       return;
     }
-    const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (c + u < x.len) {
-        const float w = load_as_f32(x.w, idx + u, x.pdtype);
-        store_from_f32(x.w, idx + u, x.pdtype, w - x.pre * vv[u]);
-      }
-    }
+    store_from_f32(x.w, idx, x.pdtype, n.x);
+    if (c + 1 < x.len) store_from_f32(x.w, idx + 1, x.pdtype, n.y);
+    if (c + 2 < x.len) store_from_f32(x.w, idx + 2, x.pdtype, n.z);
+    if (c + 3 < x.len) store_from_f32(x.w, idx + 3, x.pdtype, n.w);
   }
 };
 
-template <class Epi>
-hipError_t run_big(const BigCore& c, const Epi& e, int count, hipStream_t s) {
-  hipLaunchKernelGGL(k_gemm_big<Epi>, dim3(c.t8, 1, count), dim3(256), 0, s, c, e);
-  return hipGetLastError();
-}
-
 }  // namespace
 
-hipError_t launch_gram_big(const GramBigLaunch& a, hipStream_t s) {
-  BigCore c{};
-  c.a = c.b = static_cast<const char*>(a.x);
-  c.lda = c.ldb = a.np;
-  c.sa = c.sb = a.mp * a.np;
-  c.K = a.np;
-  c.tiles = a.tiles;
-  c.t8 = a.t8;
-  return run_big(c, GramEpiBig{a.a32, a.e16, a.dg, a.scale, a.mp}, a.count, s);
-}
-
-hipError_t launch_poly_big(const PolyBigLaunch& a, hipStream_t s) {
-  BigCore c{};
-  c.a = c.b = reinterpret_cast<const char*>(a.e16);
-  c.lda = c.ldb = a.mp;
-  c.sa = c.sb = a.mp * a.mp;
-  c.K = a.mp;
-  c.tiles = a.tiles;
-  c.t8 = a.t8;
-  return run_big(c, PolyEpiBig{a.a32, a.dg, a.r16, a.sc, a.mp}, a.count, s);
-}
-
-hipError_t launch_apply_big(const ApplyBigLaunch& a, hipStream_t s) {
-  BigCore c{};
-  c.a = reinterpret_cast<const char*>(a.r16);
-  c.b = static_cast<const char*>(a.xt_old);
-  c.lda = a.mp;
-  c.ldb = a.mp;
-  c.sa = a.mp * a.mp;
-  c.sb = a.np * a.mp;
-  c.K = a.mp;
-  c.tiles = a.tiles;
-  c.t8 = a.t8;
-  if (a.final_round) {
-    const int vec = (a.m % 4 == 0) && (a.n % 4 == 0);
-    return run_big(c, FinalEpiBig{a.mats, a.ptrs, a.scale, a.sc, a.m, a.n, vec}, a.count, s);
+hipError_t launch_big(BigKind kind, const BigArgs& a, hipStream_t s) {
+  const dim3 grid(a.t8), block(256);
+  switch (kind) {
+    case kBigGram: hipLaunchKernelGGL(k_gemm_big<GramPhase>, grid, block, 0, s, a); break;
+    case kBigPoly: hipLaunchKernelGGL(k_gemm_big<PolyPhase>, grid, block, 0, s, a); break;
+    case kBigApply: hipLaunchKernelGGL(k_gemm_big<ApplyPhase>, grid, block, 0, s, a); break;
+    case kBigFinal: hipLaunchKernelGGL(k_gemm_big<FinalPhase>, grid, block, 0, s, a); break;
   }
-  return run_big(c, ApplyEpiBig{static_cast<uint16_t*>(a.x_new), static_cast<uint16_t*>(a.xt_new),
-                                a.scale, a.mp, a.np},
-                 a.count, s);
+  return hipGetLastError();
 }
 
 }  // namespace muon

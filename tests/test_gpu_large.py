@@ -104,3 +104,10 @@ def test_large_graph_replay_matches_eager():
         plan.close()
     for x, y in zip(*outs):
         assert np.array_equal(x, y)
+
+
+def test_several_large_shapes_share_the_grouped_launches():
+    """Three different large oriented shapes (one of them stored transposed,
+    one a 3-D stack) in one plan: every product phase is one launch over all
+    of them, walking one tile table, and each slice must still match."""
+    _check([(600, 700), (1100, 520), (2, 768, 1024), (24, 900)])

@@ -92,7 +92,7 @@ def test_plans_of_the_workloads(m):
     info = describe(m, W["dense_h4096_l8"])
     assert bucket_keys(info) == [(4096, 12288, 8, 0, "stream"), (4096, 4096, 8, 0, "stream"),
                                  (4096, 16384, 16, 8, "stream")]
-    assert info["launches_fixed"] == 3 * 2 and info["launches_per_ns"] == 3 * 3
+    assert info["launches_fixed"] == 3 * 2 and info["launches_per_ns"] == 3   # phases grouped over the buckets
     assert bucket_keys(describe(m, W["large_share"])) == [(8192, 8192, 4, 0, "stream"),
                                                           (4096, 16384, 4, 4, "stream")]
     assert describe(m, W["large_share"])["n_matrices"] == 8
@@ -206,3 +206,109 @@ def test_workspace_grows_with_batch(m):
     a = m.info_dict(m.muon_plan_describe(m.make_descs([(100, 300)] * 2), None))
     b = m.info_dict(m.muon_plan_describe(m.make_descs([(100, 300)] * 4), None))
     assert b["workspace_bytes"] > a["workspace_bytes"]
+
+
+TABLE_HARNESS = r"""
+#include <cstdio>
+#include <vector>
+#include "planner.h"
+int main(int argc, char** argv) {
+  // argv: mode, then triples rows cols count (2-D or stacked 3-D shapes)
+  std::vector<muon_param_desc_t> d;
+  for (int i = 2; i + 2 < argc; i += 3) {
+    muon_param_desc_t x{};
+    long e = std::atol(argv[i + 2]);
+    x.ndim = e > 1 ? 3 : 2;
+    x.param_dtype = MUON_F32;
+    x.grad_dtype = MUON_BF16;
+    if (e > 1) { x.shape[0] = e; x.shape[1] = std::atol(argv[i]); x.shape[2] = std::atol(argv[i + 1]); }
+    else { x.shape[0] = std::atol(argv[i]); x.shape[1] = std::atol(argv[i + 1]); }
+    d.push_back(x);
+  }
+  muon_plan_opts_t o;
+  muon::default_opts(&o);
+  o.mode = (muon_mode_t)std::atoi(argv[1]);
+  muon::Plan p;
+  std::string err;
+  if (muon::make_plan(d.data(), (int)d.size(), &o, 256, &p, &err) != 0) { std::printf("ERR %s\n", err.c_str()); return 1; }
+  std::printf("big %zu\n", p.big.size());
+  for (size_t i = 0; i < p.big.size(); ++i) {
+    const auto& b = p.buckets[p.big[i]];
+    std::printf("bucket %zu %lld %lld %lld %lld %zu\n", i, (long long)b.m, (long long)b.n, (long long)b.mp,
+                (long long)b.np, b.slices.size());
+  }
+  for (int ph = 0; ph < 3; ++ph) {
+    std::printf("table %d %zu\n", ph, p.big_tab[ph].size());
+    for (auto& t : p.big_tab[ph]) std::printf("%u %u\n", t.bz, t.mn);
+  }
+  return 0;
+}
+"""
+
+
+def _tables(shapes):
+    """Run the planner (compiled from source with g++) on large bf16 shapes and
+    return its buckets and the three tile tables."""
+    import tempfile
+    src = os.path.join(ROOT, "muon_newton_schulz_05_amd", "csrc")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.cpp")
+        exe = os.path.join(d, "t")
+        open(c, "w").write(TABLE_HARNESS)
+        subprocess.run(["g++", "-std=c++17", "-O1", "-I", src, c, os.path.join(src, "planner.cpp"), "-o", exe],
+                       check=True)
+        args = [exe, "1"] + [str(v) for s in shapes for v in s]
+        out = subprocess.run(args, capture_output=True, text=True, check=True).stdout.split("\n")
+    buckets, tables, k = [], [], 0
+    nb = int(out[0].split()[1])
+    for i in range(nb):
+        f = out[1 + i].split()
+        buckets.append(tuple(int(x) for x in f[2:]))
+    k = 1 + nb
+    for _ in range(3):
+        n = int(out[k].split()[2])
+        tables.append([tuple(int(x) for x in out[k + 1 + j].split()) for j in range(n)])
+        k += 1 + n
+    return buckets, tables
+
+
+def test_large_tile_tables_cover_every_tile_once():
+    """Each phase's table lists every output tile of every large slice exactly
+    once (upper triangle for X X^T and E E), pads only with the empty marker,
+    has a length that is a multiple of 8, and its 8 XCD stretches carry work
+    within one block of each other."""
+    shapes = [(4096, 12288, 2), (4096, 4096, 3), (16384, 4096, 1), (1408, 2048, 5), (600, 700, 1)]
+    buckets, tables = _tables(shapes)
+    assert [b[:2] for b in buckets] == [(4096, 12288), (4096, 4096), (4096, 16384), (1408, 2048), (600, 700)]
+    no_tile = 0xFFFFFFFF
+    for ph, tab in enumerate(tables):
+        assert len(tab) % 8 == 0
+        seen = set()
+        for bz, mn in tab:
+            if bz == no_tile:
+                continue
+            key = (bz >> 24, bz & 0xFFFFFF, mn & 0xFFFF, mn >> 16)
+            assert key not in seen
+            seen.add(key)
+        want = set()
+        for bi, (m, n, mp, np_, cnt) in enumerate(buckets):
+            assert mp % 256 == 0 and np_ % 256 == 0 and mp >= m and np_ >= n
+            tm, tn = mp // 256, (np_ // 256 if ph == 2 else mp // 256)
+            for z in range(cnt):
+                for i in range(tm):
+                    for j in range(tn):
+                        if ph == 2 or j >= i:
+                            want.add((bi, z, i, j))
+        assert seen == want
+        # work per XCD stretch (contraction length per tile)
+        L = len(tab) // 8
+        work = []
+        for x in range(8):
+            w = 0
+            for bz, mn in tab[x * L:(x + 1) * L]:
+                if bz != no_tile:
+                    m, n, mp, np_, cnt = buckets[bz >> 24]
+                    w += np_ if ph == 0 else mp
+            work.append(w)
+        biggest_block = 32 * max((b[3] if ph == 0 else b[2]) for b in buckets)
+        assert max(work) - min(work) <= biggest_block
