@@ -4,10 +4,12 @@
  * One Muon step, per 2-D weight slice W of shape [R, C]:
  *   1. M <- beta * M + G                       (momentum of the gradient)
  *   2. X <- M, transposed when R > C            (so X is [m, n], m = min(R, C))
+ *      (with the Nesterov option: X <- G + beta * M)
  *   3. X <- X / (||X||_F + eps)                 (whole-matrix Frobenius normalisation)
  *   4. k times: A = X X^T;  X <- a X + (b A + c A^2) X      (Newton-Schulz)
  *   5. O <- X, transposed back when R > C
  *   6. W <- W - lr * O
+ *      (options: W <- W - lr * wd * W - lr * f * O, see muon_plan_opts_t)
  *
  * Sources, by page and section:
  *  - "关于分布式Muon的想法整合及讨论" (notes on distributed Muon), §1 Introduction:
@@ -101,8 +103,19 @@ typedef struct {
                               -1 = never (every slice takes the streamed path)                */
   int32_t timing;          /* 1: time each kernel class with HIP events (muon_plan_timings)   */
   int32_t n_cu;            /* compute units to plan for; 0 = the device's (describe: 256)     */
-  int32_t reserved[3];
+  /* Update variants, all off by default (the pages print no update formula;
+   * these are the standard Muon options):                                     */
+  int32_t nesterov;        /* 1: orthogonalise G + beta M (M already updated) instead of M   */
+  int32_t update_scale;    /* muon_update_scale_t: factor f on O, from the stored [R, C]    */
+  float weight_decay;      /* wd >= 0: W <- W - lr wd W - lr f O (decoupled)                 */
 } muon_plan_opts_t;
+
+/* Shape factor f of the update of a slice stored as [R, C]. */
+typedef enum {
+  MUON_SCALE_NONE = 0,     /* f = 1                        */
+  MUON_SCALE_ASPECT = 1,   /* f = sqrt(max(1, R / C))      */
+  MUON_SCALE_RMS = 2       /* f = 0.2 sqrt(max(R, C))      */
+} muon_update_scale_t;
 
 /* How a bucket of same-shape slices is executed.
  *  MUON_PATH_SKINNY: m <= 32.  One pass forms the first Gram matrix (split over
@@ -146,7 +159,9 @@ void muon_default_opts(muon_plan_opts_t* opts);
  * oriented shape (m, n) and given a kernel path; the workspace is allocated
  * once on the current device.  opts may be NULL (defaults).
  * Errors: INVALID_ARGUMENT (null pointers, n_params <= 0, ndim not 2 or 3, a
- * dimension <= 0 or >= 2^31, unknown dtype or mode, bad eps/max_ns_steps),
+ * dimension <= 0 or >= 2^31, unknown dtype or mode, bad eps/max_ns_steps,
+ * nesterov not 0 or 1, unknown update_scale, weight_decay negative or not
+ * finite),
  * UNSUPPORTED (more than MUON_MAX_BUCKETS shapes), OOM, HIP. */
 int muon_plan_create(const muon_param_desc_t* descs, int32_t n_params,
                      const muon_plan_opts_t* opts, muon_plan_t* out_plan);

@@ -114,6 +114,7 @@ hipError_t enqueue_skinny(muon_plan_t plan, const muon::BucketPlan& bp, hipStrea
   L.n_chunks = bp.n_chunks;
   L.count = (int)bp.slices.size();
   L.bf16 = p.mode == MUON_MODE_BF16_MFMA;
+  L.nesterov = p.nesterov;
   hipError_t e;
   if ((e = timed(plan, muon::kClsSkinnyGram, s, timing, [&] { return muon::launch_skinny_gram(L, s); })) != hipSuccess)
     return e;
@@ -442,8 +443,10 @@ int muon_step(muon_plan_t plan, void* const* params, const void* const* grads, v
   v.b = b;
   v.c = c;
   v.eps = p.eps;
+  v.decay = lr * p.weight_decay;
   v.ns_steps = ns_steps;
-  v.pad = 0;
+  v.nesterov = p.nesterov;
+  v.scale_mode = p.update_scale;
   const bool timing = p.timing != 0;
   const bool graph = p.use_graph && !timing && s != nullptr;
   if (!graph) {

@@ -73,4 +73,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Shape factor f of the update of a slice with oriented shape [m, n]
+// (m <= n), stored transposed ([n, m], R > C) or not ([m, n]).
+__device__ __forceinline__ float update_factor(int scale_mode, int64_t m, int64_t n, int transposed) {
+  if (scale_mode == 1) return transposed ? sqrtf((float)n / (float)m) : 1.f;  // sqrt(max(1, R / C))
+  if (scale_mode == 2) return 0.2f * sqrtf((float)n);                        // 0.2 sqrt(max(R, C))
+  return 1.f;
+}
+
 }  // namespace muon

@@ -26,6 +26,7 @@ struct SkinnyLaunch {
   uint32_t* err;          // device error word
   int m, n, n_chunks, count;
   int bf16;               // 1: bf16 matrix-core mode, 0: fp32 mode
+  int nesterov;           // the plan's Nesterov option (selects the apply kernel)
 };
 hipError_t launch_skinny_gram(const SkinnyLaunch& a, hipStream_t s);
 hipError_t launch_skinny_poly(const SkinnyLaunch& a, hipStream_t s);

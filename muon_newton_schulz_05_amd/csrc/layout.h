@@ -21,11 +21,14 @@ enum KernelClass { kClsSkinnyGram = 0, kClsSkinnyPoly, kClsSkinnyApply, kClsMome
 // Bits of the plan's device error word.
 constexpr uint32_t kErrNonFinite = 1u;  // a slice's momentum norm was not finite
 
-// Scalars of one step, written to device memory by the prologue kernel.
+// Scalars of one step (carried by value to the step's first kernel, which
+// writes them to the plan's scalar block; or written by a prologue kernel).
 struct DevScalars {
   float lr, beta, a, b, c, eps;
+  float decay;          // lr * weight decay: W <- W - decay W - lr f O
   int32_t ns_steps;
-  int32_t pad;
+  int32_t nesterov;     // orthogonalise G + beta M instead of M
+  int32_t scale_mode;   // muon_update_scale_t
 };
 
 // Device pointers of one parameter.

@@ -70,6 +70,18 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
     *err = buf;
     return MUON_ERR_INVALID_ARGUMENT;
   }
+  if (opts.nesterov != 0 && opts.nesterov != 1) {
+    *err = "nesterov must be 0 or 1";
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  if (opts.update_scale < MUON_SCALE_NONE || opts.update_scale > MUON_SCALE_RMS) {
+    *err = "unknown update_scale";
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  if (!std::isfinite(opts.weight_decay) || opts.weight_decay < 0.f) {
+    *err = "weight_decay must be finite and >= 0";
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
   if (n_cu <= 0) {
     *err = "device description has no compute units";
     return MUON_ERR_INVALID_ARGUMENT;
@@ -84,6 +96,9 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
                    : opts.skinny_max_m < 0 ? 0 : opts.skinny_max_m;
   p.timing = opts.timing ? 1 : 0;
   p.use_graph = opts.use_graph ? 1 : 0;
+  p.nesterov = opts.nesterov;
+  p.update_scale = opts.update_scale;
+  p.weight_decay = opts.weight_decay;
   p.n_cu = n_cu;
   p.n_params = n_params;
   p.descs.assign(descs, descs + n_params);

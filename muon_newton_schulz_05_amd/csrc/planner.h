@@ -55,6 +55,8 @@ struct Plan {
   uint64_t workspace_limit = 0;
   int skinny_max_m = kMaxSkinnyM;
   int timing = 0, use_graph = 0;
+  int nesterov = 0, update_scale = MUON_SCALE_NONE;  // update variants
+  float weight_decay = 0.f;
   int n_cu = 256;
 
   int n_params = 0;

@@ -158,6 +158,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny_gram(SkinnyLaunch a) {
   const DevMat d = a.mats[z];
   const PtrEntry pe = a.ptrs[d.param];
   const float beta = a.sc_out ? a.sv.beta : a.sc->beta;
+  const bool nesterov = (a.sc_out ? a.sv.nesterov : a.sc->nesterov) != 0;
   if (a.sc_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.sc_out = a.sv;
   const int m = a.m, n = a.n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -168,7 +169,8 @@ __global__ __launch_bounds__(kThreads) void k_skinny_gram(SkinnyLaunch a) {
 
   zero_unfilled(st, m, cm.cw, tid);
 
-  // Issue every load of the chunk, then M <- beta M + G, store M, stage it.
+  // Issue every load of the chunk, then M <- beta M + G, store M, stage the
+  // matrix that is orthogonalised: M, or G + beta M with Nesterov momentum.
   auto pass = [&](auto gtype) {
     using GT = decltype(gtype);
     float lm[kChunks][4], lg[kChunks][4];
@@ -196,9 +198,12 @@ __global__ __launch_bounds__(kThreads) void k_skinny_gram(SkinnyLaunch a) {
       int64_t off;
       int cnt, i0, j0;
       cm.piece(v, off, cnt, i0, j0);
-      float mn[4];
+      float mn[4], xs[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) mn[u] = fmaf(beta, lm[k][u], lg[k][u]);
+      for (int u = 0; u < 4; ++u) {
+        mn[u] = fmaf(beta, lm[k][u], lg[k][u]);
+        xs[u] = nesterov ? fmaf(beta, mn[u], lg[k][u]) : mn[u];
+      }
       if (cnt == 4 && cm.vec_ok) {
         st_vec4<F32>(Mb, off, mn);
       } else {
@@ -207,14 +212,14 @@ __global__ __launch_bounds__(kThreads) void k_skinny_gram(SkinnyLaunch a) {
           if (u < cnt) st_elem<F32>(Mb, off + u, mn[u]);
       }
       if (!cm.tr && cnt == 4) {
-        *reinterpret_cast<f32x4_t*>(&st[i0][j0]) = f32x4_t{mn[0], mn[1], mn[2], mn[3]};
+        *reinterpret_cast<f32x4_t*>(&st[i0][j0]) = f32x4_t{xs[0], xs[1], xs[2], xs[3]};
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (u >= cnt) break;
           int i, j;
           cm.pos(i0, j0, u, i, j);
-          st[i][j] = mn[u];
+          st[i][j] = xs[u];
         }
       }
     }
@@ -290,7 +295,9 @@ __global__ __launch_bounds__(kThreads) void k_skinny_gram(SkinnyLaunch a) {
 }
 
 // ------------------------------------------------------------------ apply
-template <bool BF16>
+// NEST: Nesterov momentum (X = G + beta M); chosen at launch from the plan so
+// that the plain kernel carries no second code path.
+template <bool BF16, bool NEST>
 __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
   __shared__ __attribute__((aligned(16))) float st[32][kStride];
   __shared__ float qs[32][33];
@@ -298,19 +305,24 @@ __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
   const int z = blockIdx.y, chunk = blockIdx.x;
   const DevMat d = a.mats[z];
   const PtrEntry pe = a.ptrs[d.param];
-  const float lr = a.sc->lr;
+  const float lr = a.sc->lr, decay = a.sc->decay, beta = a.sc->beta;
   const int m = a.m, n = a.n;
+  const float lrf = lr * update_factor(a.sc->scale_mode, m, n, d.transposed);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   ChunkMap cm;
   cm.init(m, n, chunk * kCols, min(kCols, n - chunk * kCols), d.transposed != 0, d.slice_off);
   const char* const Mb = reinterpret_cast<const char*>(pe.m + d.slice_off);
+  const char* const Gb = static_cast<const char*>(pe.g) + d.slice_off * (d.gdtype ? 2 : 4);
   char* const Wb = static_cast<char*>(pe.w) + d.slice_off * (d.pdtype ? 2 : 4);
 
   for (int e = tid; e < 1024; e += kThreads) qs[e >> 5][e & 31] = a.qs[(int64_t)z * 1024 + e];
 
-  auto run = [&](auto wtype) {
+  // gmode: 0 = X is M; 1 / 2 = Nesterov, X = G + beta M with G in float32 / bf16.
+  auto run = [&](auto wtype, auto gmode) {
     using WT = decltype(wtype);
+    constexpr int GM = decltype(gmode)::value;
+    using GT = std::integral_constant<bool, GM == 2>;
     float lm[kChunks][4], lw[kChunks][4];
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) {
@@ -318,18 +330,25 @@ __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
       int64_t off = 0;
       int cnt = 0, i0 = 0, j0 = 0;
       if (v < cm.total) cm.piece(v, off, cnt, i0, j0);
+      float lg[4] = {0.f, 0.f, 0.f, 0.f};
       if (cnt == 4 && cm.vec_ok) {
         ld_vec4<F32>(Mb, off, lm[k]);
         ld_vec4<WT>(Wb, off, lw[k]);
+        if constexpr (GM != 0) ld_vec4<GT>(Gb, off, lg);
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           lm[k][u] = u < cnt ? ld_elem<F32>(Mb, off + u) : 0.f;
           lw[k][u] = u < cnt ? ld_elem<WT>(Wb, off + u) : 0.f;
+          if constexpr (GM != 0) lg[u] = u < cnt ? ld_elem<GT>(Gb, off + u) : 0.f;
         }
       }
+      if constexpr (GM != 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lm[k][u] = fmaf(beta, lm[k][u], lg[u]);
+      }
     }
-    // Stage M in oriented order.
+    // Stage X (M, or G + beta M) in oriented order.
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) {
       const int v = tid + kThreads * k;
@@ -408,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
     }
     __syncthreads();
 
-    // W <- W - lr O in storage order.
+    // W <- W - decay W - lr f O in storage order.
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) {
       const int v = tid + kThreads * k;
@@ -420,13 +439,13 @@ __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
       if (!cm.tr && cnt == 4) {
         const f32x4_t o4 = *reinterpret_cast<const f32x4_t*>(&st[i0][j0]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = lw[k][u] - lr * o4[u];
+        for (int u = 0; u < 4; ++u) w[u] = lw[k][u] - decay * lw[k][u] - lrf * o4[u];
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           int i = 0, j = 0;
           if (u < cnt) cm.pos(i0, j0, u, i, j);
-          w[u] = lw[k][u] - lr * (u < cnt ? st[i][j] : 0.f);
+          w[u] = lw[k][u] - decay * lw[k][u] - lrf * (u < cnt ? st[i][j] : 0.f);
         }
       }
       if (cnt == 4 && cm.vec_ok) {
@@ -440,8 +459,19 @@ __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
   };
   // Rows >= m and columns >= cw of the staging block read as zero.
   zero_unfilled(st, m, cm.cw, tid);
-  if (d.pdtype) run(B16{});
-  else run(F32{});
+  using G0 = std::integral_constant<int, 0>;
+  using G1 = std::integral_constant<int, 1>;
+  using G2 = std::integral_constant<int, 2>;
+  if constexpr (!NEST) {
+    if (d.pdtype) run(B16{}, G0{});
+    else run(F32{}, G0{});
+  } else if (d.gdtype) {
+    if (d.pdtype) run(B16{}, G2{});
+    else run(F32{}, G2{});
+  } else {
+    if (d.pdtype) run(B16{}, G1{});
+    else run(F32{}, G1{});
+  }
 }
 
 }  // namespace
@@ -455,8 +485,13 @@ hipError_t launch_skinny_gram(const SkinnyLaunch& a, hipStream_t s) {
 
 hipError_t launch_skinny_apply(const SkinnyLaunch& a, hipStream_t s) {
   const dim3 grid(a.n_chunks, a.count);
-  if (a.bf16) hipLaunchKernelGGL(k_skinny_apply<true>, grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(k_skinny_apply<false>, grid, dim3(kThreads), 0, s, a);
+  if (a.nesterov) {
+    if (a.bf16) hipLaunchKernelGGL((k_skinny_apply<true, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_skinny_apply<false, true>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (a.bf16) hipLaunchKernelGGL((k_skinny_apply<true, false>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_skinny_apply<false, false>), grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny_poly(SkinnyLaunch a) {
   const int ti = 16 * (wave >> 1), tj = 16 * (wave & 1);
   const int li = lane & 15, lk = lane >> 4;
   // All 32 columns of the zero-padded buffers: the operands of the eight
-  // k-steps are read from LDS first, then the products run back to back.
+  // k-steps are read from LDS first, then the products run.
   auto prod = [&](const double (*X)[33], const double (*Y)[33]) {
     double xv[8], yv[8];
 #pragma unroll
@@ -97,10 +97,14 @@ __global__ __launch_bounds__(kThreads) void k_skinny_poly(SkinnyLaunch a) {
       xv[q] = X[ti + li][4 * q + lk];
       yv[q] = Y[4 * q + lk][tj + li];
     }
-    f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+    // Two independent chains (even and odd k-steps) keep two products in flight.
+    f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[q], yv[q], acc, 0, 0, 0);
-    return acc;
+    for (int q = 0; q < 8; q += 2) {
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[q], yv[q], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[q + 1], yv[q + 1], acc1, 0, 0, 0);
+    }
+    return acc0 + acc1;
   };
   int cur = 0;
   for (int it = 0; it < ns; ++it) {

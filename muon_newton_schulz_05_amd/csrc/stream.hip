@@ -40,10 +40,12 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumLaunch a) {
   const DevMat d = a.mats[z];
   const PtrEntry pe = a.ptrs[d.param];
   const float beta = a.sc_out ? a.sv.beta : a.sc->beta;
+  const bool nesterov = (a.sc_out ? a.sv.nesterov : a.sc->nesterov) != 0;
   if (a.sc_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.sc_out = a.sv;
   const int tid = threadIdx.x;
 
-  // Load along the stored rows (coalesced), keep M_new in LDS in oriented order.
+  // Load along the stored rows (coalesced), keep X0 in LDS in oriented order:
+  // M_new, or G + beta M_new with Nesterov momentum.
   for (int q = 0; q < 16; ++q) {
     const int fast = tid & 63, slow = (tid >> 6) + 4 * q;
     const int ii = d.transposed ? fast : slow;
@@ -52,8 +54,10 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumLaunch a) {
     float v = 0.f;
     if (i < a.m && j < a.n) {
       const int64_t idx = d.slice_off + (d.transposed ? j * a.m + i : i * a.n + j);
-      v = fmaf(beta, pe.m[idx], load_as_f32(pe.g, idx, d.gdtype));
-      pe.m[idx] = v;
+      const float g = load_as_f32(pe.g, idx, d.gdtype);
+      const float mn = fmaf(beta, pe.m[idx], g);
+      pe.m[idx] = mn;
+      v = nesterov ? fmaf(beta, mn, g) : mn;
     }
     tile[ii][jj] = v;
   }
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmCore c, Epi epi) {
     row[h] = idx >> 2;
     c16[h] = idx & 3;
   }
-  uint4 ra[2], rb[2];
+  u32x4_t ra[2], rb[2];
   const int nk = (int)(c.K / BK);
   const int total = A2 ? 2 * nk : nk;
 
@@ -153,15 +157,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmCore c, Epi epi) {
     const char* Ab = it >= nk ? A2 : A;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      ra[h] = *reinterpret_cast<const uint4*>(Ab + ((int64_t)row[h] * c.lda + (int64_t)kt * BK) * (int64_t)sizeof(T) + c16[h] * 16);
-      rb[h] = *reinterpret_cast<const uint4*>(B + ((int64_t)row[h] * c.ldb + (int64_t)kt * BK) * (int64_t)sizeof(T) + c16[h] * 16);
+      ra[h] = *reinterpret_cast<const u32x4_t*>(Ab + ((int64_t)row[h] * c.lda + (int64_t)kt * BK) * (int64_t)sizeof(T) + c16[h] * 16);
+      rb[h] = *reinterpret_cast<const u32x4_t*>(B + ((int64_t)row[h] * c.ldb + (int64_t)kt * BK) * (int64_t)sizeof(T) + c16[h] * 16);
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      *reinterpret_cast<uint4*>(&lds[buf][0][row[h] * kLdsRow + c16[h] * 16]) = ra[h];
-      *reinterpret_cast<uint4*>(&lds[buf][1][row[h] * kLdsRow + c16[h] * 16]) = rb[h];
+      *reinterpret_cast<u32x4_t*>(&lds[buf][0][row[h] * kLdsRow + c16[h] * 16]) = ra[h];
+      *reinterpret_cast<u32x4_t*>(&lds[buf][1][row[h] * kLdsRow + c16[h] * 16]) = rb[h];
     }
   };
 
@@ -320,9 +324,10 @@ struct FinalEpi {
   int64_t mp, np, m, n;
   __device__ void operator()(int z, int i0, int j, const float v[4]) const {
     const float s = scale ? scale[2 * z] : 1.f;
-    const float a = sc->a, lr = sc->lr;
     const DevMat d = mats[z];
     const PtrEntry pe = ptrs[d.param];
+    const float a = sc->a, decay = sc->decay;
+    const float lrf = sc->lr * update_factor(sc->scale_mode, m, n, d.transposed);
     const int64_t zo = (int64_t)z * mp * np;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -331,7 +336,7 @@ struct FinalEpi {
         const float val = s * fmaf(a, x_to_f32(x_old[zo + i * np + j]), v[u]);
         const int64_t idx = d.slice_off + (d.transposed ? (int64_t)j * m + i : i * n + j);
         const float w = load_as_f32(pe.w, idx, d.pdtype);
-        store_from_f32(pe.w, idx, d.pdtype, w - lr * val);
+        store_from_f32(pe.w, idx, d.pdtype, w - decay * w - lrf * val);
       }
     }
   }
@@ -342,12 +347,15 @@ __global__ __launch_bounds__(256) void k_update0(Update0Launch a) {
   const int z = blockIdx.y;
   const DevMat d = a.mats[z];
   const PtrEntry pe = a.ptrs[d.param];
-  const float k = a.sc->lr * a.scale[2 * z];
+  const float k = a.sc->lr * update_factor(a.sc->scale_mode, a.m, a.n, d.transposed) * a.scale[2 * z];
+  const float decay = a.sc->decay, beta = a.sc->beta;
+  const bool nesterov = a.sc->nesterov != 0;
   const int64_t total = a.m * a.n;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
     const int64_t idx = d.slice_off + e;  // stored order; O and W share the layout
     const float w = load_as_f32(pe.w, idx, d.pdtype);
-    store_from_f32(pe.w, idx, d.pdtype, w - k * pe.m[idx]);
+    const float x = nesterov ? fmaf(beta, pe.m[idx], load_as_f32(pe.g, idx, d.gdtype)) : pe.m[idx];
+    store_from_f32(pe.w, idx, d.pdtype, w - decay * w - k * x);
   }
 }
 

@@ -443,8 +443,9 @@ struct ApplyPhase {
   }
 };
 
-// Last round: W <- W - lr s (X + R X) through the slice's own layout (the row
-// view for a slice stored [m, n], the column view for one stored [n, m]).
+// Last round: W <- W - decay W - lr f s (X + R X) through the slice's own
+// layout (the row view for a slice stored [m, n], the column view for one
+// stored [n, m]); decay = lr wd and f the shape factor (both options).
 struct FinalPhase {
   static __device__ Operands operands(const BigArgs& g, const BigBucket& bb, int z) {
     return apply_operands(g, bb, z);
@@ -455,7 +456,8 @@ struct FinalPhase {
     int64_t rows, len;   // stored rows and row length of the slice
     int64_t xstride;     // row stride of xo
     int pdtype, view, vec;
-    float k;             // lr s
+    float k;             // lr f s
+    float decay;         // lr wd
   };
   static __device__ Ctx context(const BigArgs& g, const BigBucket& bb, int z) {
     const DevMat d = bb.mats[z];
@@ -470,7 +472,8 @@ struct FinalPhase {
     x.len = d.transposed ? bb.m : bb.n;
     x.pdtype = d.pdtype;
     x.vec = bb.vec;
-    x.k = g.sc->lr * (g.first ? bb.scale[2 * z] : 1.f);
+    x.k = g.sc->lr * update_factor(g.sc->scale_mode, bb.m, bb.n, d.transposed) * (g.first ? bb.scale[2 * z] : 1.f);
+    x.decay = g.sc->decay;
     return x;
   }
   static __device__ float prescale(const Ctx&) { return 1.f; }
@@ -502,8 +505,10 @@ struct FinalPhase {
   }
   static __device__ void store(const Ctx& x, int, int r, int c, f32x4_t v, const Aux& q) {
     if (r >= x.rows || c >= x.len) return;
-    const f32x4_t n{q.w.x - x.k * (v.x + bf16_lo(q.xo.x)), q.w.y - x.k * (v.y + bf16_hi(q.xo.x)),
-                    q.w.z - x.k * (v.z + bf16_lo(q.xo.y)), q.w.w - x.k * (v.w + bf16_hi(q.xo.y))};
+    const f32x4_t n{q.w.x - x.decay * q.w.x - x.k * (v.x + bf16_lo(q.xo.x)),
+                    q.w.y - x.decay * q.w.y - x.k * (v.y + bf16_hi(q.xo.x)),
+                    q.w.z - x.decay * q.w.z - x.k * (v.z + bf16_lo(q.xo.y)),
+                    q.w.w - x.decay * q.w.w - x.k * (v.w + bf16_hi(q.xo.y))};
     const int64_t idx = (int64_t)r * x.len + c;
     if (x.vec && c + 3 < x.len) {
       if (x.pdtype == 1) {  // bfloat16 W, rounded to nearest even

@@ -6,6 +6,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 
 from .muon_ref import (  # noqa: F401
     DEFAULT_EPS,
+    UPDATE_SCALES,
     decode,
     f32,
     frobenius_normalize,
@@ -14,4 +15,6 @@ from .muon_ref import (  # noqa: F401
     newton_schulz,
     orient,
     orthogonalize,
+    update_direction,
+    update_scale,
 )

@@ -43,6 +43,13 @@ Readings taken where the pages are silent (each is also listed in the design doc):
 * Momentum: heavy-ball ``M <- beta M + G``, stored rounded to float32.
 * Normaliser: ``X / (||X||_F + eps)``, eps = 1e-7 by default.
 * Update: ``W <- W - lr O``; no shape-dependent factor, no weight decay.
+  The pages print no update formula, so the standard Muon variants are
+  offered as options that default off (``nesterov``, ``weight_decay``,
+  ``update_scale``): with Nesterov momentum the orthogonalised matrix is
+  ``G + beta M`` (M already updated) instead of M; decoupled weight decay
+  shrinks the weights, ``W <- W - lr wd W - lr f O``; and f is 1 ("none"),
+  ``sqrt(max(1, R / C))`` ("aspect") or ``0.2 sqrt(max(R, C))`` ("rms"),
+  computed from the slice's stored shape [R, C].
 * Scalars (lr, beta, a, b, c) are float32 values; they enter the float64
   arithmetic as the float32-rounded numbers.
 
@@ -121,6 +128,29 @@ def orthogonalize(m: np.ndarray, steps: int, a: float, b: float, c: float,
     return x.T if transposed else x
 
 
+def update_direction(m_new: np.ndarray, g: np.ndarray, beta: float, nesterov: bool) -> np.ndarray:
+    """The matrix that is orthogonalised: the new momentum, or with Nesterov
+    momentum the gradient plus beta times the new momentum (an option; the
+    pages only speak of the momentum, [Notes] §1)."""
+    if not nesterov:
+        return decode(m_new)
+    return decode(g) + f32(beta) * decode(m_new)
+
+
+UPDATE_SCALES = ("none", "aspect", "rms")
+
+
+def update_scale(rows: int, cols: int, mode: str) -> float:
+    """Shape factor f of a slice stored as [rows, cols] (an option)."""
+    if mode == "none":
+        return 1.0
+    if mode == "aspect":
+        return float(np.sqrt(max(1.0, rows / cols)))
+    if mode == "rms":
+        return 0.2 * float(np.sqrt(max(rows, cols)))
+    raise ValueError(f"unknown update scale {mode!r}")
+
+
 def _slices(shape: tuple[int, ...]):
     """Index tuples of the independent 2-D slices of a 2-D or 3-D tensor
     ([Blog], expert split: only the last two dimensions take part)."""
@@ -134,23 +164,28 @@ def _slices(shape: tuple[int, ...]):
 
 
 def muon_step(params, grads, momenta, *, lr: float, beta: float, ns_steps: int,
-              a: float, b: float, c: float, eps: float = DEFAULT_EPS):
+              a: float, b: float, c: float, eps: float = DEFAULT_EPS, nesterov: bool = False,
+              weight_decay: float = 0.0, update_scale_mode: str = "none"):
     """One Muon step over a list of parameters.
 
     Each parameter is 2-D [R, C] or 3-D [E, R, C]; every 2-D slice is handled
     on its own.  Returns ``(new_params, new_momenta, updates)``: new parameters
     as float64 arrays (not rounded to the parameter's storage type), new
-    momenta as float32 arrays and the orthogonalised directions O as float64.
+    momenta as float32 arrays and the orthogonalised directions O as float64
+    (before the shape factor).
     """
     new_params, new_momenta, updates = [], [], []
     lr = f32(lr)
+    wd = f32(weight_decay)
     for w, g, m in zip(params, grads, momenta):
         w64 = decode(w)
         m_new = momentum_update(m, g, beta)
+        d = update_direction(m_new, g, beta, nesterov)
+        f = update_scale(d.shape[-2], d.shape[-1], update_scale_mode)
         o = np.zeros(m_new.shape, dtype=np.float64)
         for sl in _slices(m_new.shape):
-            o[sl] = orthogonalize(m_new[sl], ns_steps, a, b, c, eps)
-        new_params.append(w64 - lr * o)
+            o[sl] = orthogonalize(d[sl], ns_steps, a, b, c, eps)
+        new_params.append(w64 - lr * wd * w64 - lr * f * o)
         new_momenta.append(m_new)
         updates.append(o)
     return new_params, new_momenta, updates

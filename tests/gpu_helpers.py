@@ -55,12 +55,14 @@ def gpu_step(params, grads, moms, *, mode, lr, beta, ns_steps, coeffs, steps=1, 
     return [to_host(p) for p in p_dev], [to_host(m) for m in m_dev]
 
 
-def oracle_step(params, grads, moms, *, lr, beta, ns_steps, coeffs, steps=1):
+def oracle_step(params, grads, moms, *, lr, beta, ns_steps, coeffs, steps=1, nesterov=False,
+                weight_decay=0.0, update_scale="none"):
     w, m = list(params), list(moms)
     o = None
     for _ in range(steps):
         w, m, o = oracle.muon_step(w, grads, m, lr=lr, beta=beta, ns_steps=ns_steps,
-                                   a=coeffs[0], b=coeffs[1], c=coeffs[2])
+                                   a=coeffs[0], b=coeffs[1], c=coeffs[2], nesterov=nesterov,
+                                   weight_decay=weight_decay, update_scale_mode=update_scale)
     return w, m, o
 
 

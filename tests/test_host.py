@@ -52,6 +52,8 @@ int main(void) {
   printf("%zu %zu %zu %zu\n", offsetof(muon_param_desc_t, shape), offsetof(muon_plan_opts_t, workspace_limit),
          offsetof(muon_plan_opts_t, n_cu), offsetof(muon_plan_info_t, buckets));
   printf("%zu %zu\n", offsetof(muon_bucket_info_t, workspace_bytes), offsetof(muon_plan_info_t, launches_per_ns));
+  printf("%zu %zu %zu\n", offsetof(muon_plan_opts_t, nesterov), offsetof(muon_plan_opts_t, update_scale),
+         offsetof(muon_plan_opts_t, weight_decay));
   return 0;
 }
 '''
@@ -65,7 +67,8 @@ int main(void) {
     got = [ctypes.sizeof(b.ParamDesc), ctypes.sizeof(b.PlanOpts), ctypes.sizeof(b.BucketInfo),
            ctypes.sizeof(b.PlanInfo), b.ParamDesc.shape.offset, b.PlanOpts.workspace_limit.offset,
            b.PlanOpts.n_cu.offset, b.PlanInfo.buckets.offset, b.BucketInfo.workspace_bytes.offset,
-           b.PlanInfo.launches_per_ns.offset]
+           b.PlanInfo.launches_per_ns.offset, b.PlanOpts.nesterov.offset, b.PlanOpts.update_scale.offset,
+           b.PlanOpts.weight_decay.offset]
     assert got == vals
 
 
@@ -163,6 +166,10 @@ def test_argument_errors(m):
     expect_error(m, INV, [(4, 4)], eps=float("nan"))
     expect_error(m, INV, [(4, 4)], max_ns_steps=-2)
     expect_error(m, INV, [(4, 4)], skinny_max_m=33)
+    expect_error(m, INV, [(4, 4)], nesterov=2)
+    expect_error(m, INV, [(4, 4)], update_scale=3)
+    expect_error(m, INV, [(4, 4)], weight_decay=-0.1)
+    expect_error(m, INV, [(4, 4)], weight_decay=float("inf"))
     expect_error(m, OOM, [(256, 256)], workspace_limit=1024)
     expect_error(m, UNS, [(40 + i, 100) for i in range(65)])
 

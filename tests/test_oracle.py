@@ -375,3 +375,100 @@ def test_planted_slice_mistake_is_caught(monkeypatch):
         # a whole 3-D tensor cannot be oriented as one matrix
         muon_ref.muon_step([np.zeros_like(g)], [g], [np.zeros_like(g)], lr=0.1, beta=0.9,
                            ns_steps=5, a=QUINTIC[0], b=QUINTIC[1], c=QUINTIC[2])
+
+
+# --------------------------------------------------- opt-in update variants
+# (Nesterov momentum, decoupled weight decay, shape factor; off by default.)
+
+def _orthonormal_pair(shape, seed):
+    """Two rank-one matrices u1 v1^T and u2 v2^T with u1 _|_ u2, v1 _|_ v2, unit norms."""
+    rng = np.random.default_rng(seed)
+    u, _ = np.linalg.qr(rng.standard_normal((shape[0], 2)))
+    v, _ = np.linalg.qr(rng.standard_normal((shape[1], 2)))
+    return u[:, 0], v[:, 0], u[:, 1], v[:, 1]
+
+
+def nesterov_pair_error(step, nesterov, beta=0.9, shape=(6, 9)):
+    """Two steps from M = 0 with G1 = u1 v1^T then G2 = u2 v2^T.  Heavy ball
+    gives M2 = beta G1 + G2 (singular values beta and 1); with Nesterov the
+    orthogonalised matrix is G2 + beta M2 = beta^2 G1 + (1 + beta) G2.  O then
+    has singular values p^5 of those values over their 2-norm, on the same
+    singular vectors."""
+    u1, v1, u2, v2 = _orthonormal_pair(shape, 5)
+    g1 = np.outer(u1, v1).astype(np.float32)
+    g2 = np.outer(u2, v2).astype(np.float32)
+    b = float(np.float32(beta))
+    zero = np.zeros(shape, np.float32)
+    _, m1, _ = step([zero], [g1], [zero], lr=1.0, beta=beta, ns_steps=5, a=QUINTIC[0], b=QUINTIC[1],
+                    c=QUINTIC[2], nesterov=nesterov)
+    _, _, o = step([zero], [g2], m1, lr=1.0, beta=beta, ns_steps=5, a=QUINTIC[0], b=QUINTIC[1],
+                   c=QUINTIC[2], nesterov=nesterov)
+    # The exact singular values of the float32-stored G1 and G2 differ from 1
+    # by float32 rounding only; the pin tolerance allows for that.
+    s = np.array([b * b, 1.0 + b]) if nesterov else np.array([b, 1.0])
+    s = s / np.linalg.norm(s)
+    ps = p_scalar(s, QUINTIC, 5)
+    expect = ps[0] * np.outer(u1, v1) + ps[1] * np.outer(u2, v2)
+    return np.max(np.abs(o[0] - expect))
+
+
+@pytest.mark.parametrize("nesterov", [False, True])
+def test_nesterov_closed_form(nesterov):
+    assert nesterov_pair_error(oracle.muon_step, nesterov) < 3e-5
+
+
+def test_nesterov_changes_the_direction():
+    """The two closed forms differ, so the pin can tell the variants apart."""
+    b = 0.9
+    r_plain = b / 1.0
+    r_nest = b * b / (1.0 + b)
+    assert abs(r_plain - r_nest) > 0.4
+
+
+def test_weight_decay_with_zero_gradient_only_shrinks():
+    rng = np.random.default_rng(11)
+    w = rng.standard_normal((5, 8)).astype(np.float32)
+    zero = np.zeros_like(w)
+    lr, wd = 0.02, 0.1
+    w_new, _, o = oracle.muon_step([w], [zero], [zero], lr=lr, beta=0.95, ns_steps=5, a=QUINTIC[0],
+                                   b=QUINTIC[1], c=QUINTIC[2], weight_decay=wd)
+    assert not o[0].any()
+    lr32, wd32 = float(np.float32(lr)), float(np.float32(wd))
+    np.testing.assert_allclose(w_new[0], w.astype(np.float64) * (1.0 - lr32 * wd32), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("mode,shape,factor", [
+    ("none", (12, 5), 1.0),
+    ("aspect", (12, 5), np.sqrt(12 / 5)),
+    ("aspect", (5, 12), 1.0),
+    ("rms", (12, 5), 0.2 * np.sqrt(12)),
+    ("rms", (5, 12), 0.2 * np.sqrt(12)),
+])
+def test_update_scale_and_decay_rank1(mode, shape, factor):
+    """Rank one G (integers, exact in float32): O = p^5(1) u v^T / (|u||v|),
+    and W1 = (1 - lr wd) W0 - lr f O with the factor f of the stored shape."""
+    rng = np.random.default_rng(4)
+    u = rng.integers(-6, 7, shape[0]).astype(np.float64)
+    v = rng.integers(-6, 7, shape[1]).astype(np.float64)
+    u[0], v[0] = 2.0, -3.0
+    g = np.outer(u, v).astype(np.float32)
+    w = rng.standard_normal(shape).astype(np.float32)
+    zero = np.zeros(shape, np.float32)
+    lr, wd = 0.05, 0.2
+    w_new, _, _ = oracle.muon_step([w], [g], [zero], lr=lr, beta=0.9, ns_steps=5, a=QUINTIC[0],
+                                   b=QUINTIC[1], c=QUINTIC[2], eps=0.0, weight_decay=wd,
+                                   update_scale_mode=mode)
+    lr32, wd32 = float(np.float32(lr)), float(np.float32(wd))
+    o = float(p_exact(Fraction(1), QUINTIC, 5)) * np.outer(u, v) / (np.linalg.norm(u) * np.linalg.norm(v))
+    expect = (1.0 - lr32 * wd32) * w.astype(np.float64) - lr32 * factor * o
+    np.testing.assert_allclose(w_new[0], expect, rtol=0, atol=1e-12)
+
+
+def test_planted_nesterov_mistakes_are_caught(monkeypatch):
+    """Broken directions: Nesterov ignored, or (1 + beta) M instead of G + beta M."""
+    real = muon_ref.update_direction
+    monkeypatch.setattr(muon_ref, "update_direction", lambda m, g, beta, nest: real(m, g, beta, False))
+    assert nesterov_pair_error(muon_ref.muon_step, True) > 1e-3
+    monkeypatch.setattr(muon_ref, "update_direction",
+                        lambda m, g, beta, nest: (1.0 + float(np.float32(beta))) * real(m, g, beta, False))
+    assert nesterov_pair_error(muon_ref.muon_step, True) > 1e-3
