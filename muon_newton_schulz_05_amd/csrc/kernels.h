@@ -20,7 +20,7 @@ struct SkinnyLaunch {
   const DevScalars* sc;
   DevScalars sv;          // scalars by value (used when sc_out is set)
   DevScalars* sc_out;     // null, or the scalar block to fill
-  double* gram_parts;     // [count][n_chunks][m*m]
+  double* gram_parts;     // [count][n_chunks][m(m+1)/2]: upper triangles, packed by rows
   float* sq_parts;        // [count][n_chunks]
   float* qs;              // [count][32*32]: s * Q
   uint32_t* err;          // device error word

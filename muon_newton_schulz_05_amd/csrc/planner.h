@@ -30,7 +30,7 @@ struct BucketPlan {
   int n_transposed = 0;
 
   // skinny path (m <= 32)
-  int n_chunks = 0;         // 512-column chunks per slice
+  int n_chunks = 0;         // 256-column chunks per slice
   uint64_t off_gram = 0, off_sqp = 0, off_qs = 0;
 
   // streamed path

@@ -17,12 +17,12 @@
 //
 // Three kernels per bucket, all batched over the bucket's slices:
 //   k_skinny_gram   momentum M <- beta M + G (stored), and per 256-column
-//                   chunk the sum of squares and the Gram partial of X0 = M,
-//                   on the matrix cores (split-K over the long dimension);
-//   k_skinny_poly   (skinny_poly.hip) per slice: s = 1/(||M||_F + eps),
-//                   A0 = s^2 sum of the partials, the k-round recurrence in
-//                   float64, Qs = s Q;
-//   k_skinny_apply  O = Qs M (matrix cores), W <- W - lr O.
+//                   chunk the sum of squares and the Gram partial of X0 (M,
+//                   or G + beta M with Nesterov momentum) on the matrix cores
+//                   (split-K over the long dimension);
+//   k_skinny_poly   per slice: s = 1/(||X0||_F + eps), A0 = s^2 sum of the
+//                   partials, the k-round recurrence in float64, Qs = s Q;
+//   k_skinny_apply  O = Qs X0 (matrix cores), W <- W - decay W - lr f O.
 // Chunks are fixed by n alone, so a slice's arithmetic does not depend on the
 // batch it is fused into.  Both memory passes stream 16-byte accesses in
 // storage order and turn them around in LDS, so one code path serves slices
@@ -135,10 +135,10 @@ struct ChunkMap {
   }
 };
 
-// Zero the part of a staging block that a chunk does not fill: rows >= m,
-// and columns >= cw of the other rows.
-__device__ __forceinline__ void zero_unfilled(float (*st)[kStride], int m, int cw, int tid) {
-  for (int e = tid; e < (32 - m) * kCols; e += kThreads) st[m + e / kCols][e % kCols] = 0.f;
+// Zero the part of a staging block of `rows` rows that a chunk does not
+// fill: rows m .. rows-1, and columns >= cw of the rows below m.
+__device__ __forceinline__ void zero_unfilled(float (*st)[kStride], int rows, int m, int cw, int tid) {
+  for (int e = tid; e < (rows - m) * kCols; e += kThreads) st[m + e / kCols][e % kCols] = 0.f;
   if (cw < kCols) {
     const int w = kCols - cw;
     for (int e = tid; e < m * w; e += kThreads) st[e / w][cw + e % w] = 0.f;
@@ -146,20 +146,30 @@ __device__ __forceinline__ void zero_unfilled(float (*st)[kStride], int m, int c
 }
 
 // ------------------------------------------------------------------ gram
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_skinny_gram(SkinnyLaunch a) {
-  __shared__ __attribute__((aligned(16))) float st[32][kStride];
-  __shared__ float wsq[kWaves];
-  // The waves' Gram partials (float64) reuse the staging block once it has been read.
-  double (*red)[1024] = reinterpret_cast<double (*)[1024]>(&st[0][0]);
-  static_assert(kWaves * 1024 * 2 <= 32 * kStride, "reduction buffer must fit the staging block");
+// LDS of k_skinny_gram: the m staged rows, or the waves' m x m float64
+// partials that reuse them, whichever is larger.  Holding only m rows (not
+// 32) lets more workgroups share a CU, so one workgroup's arithmetic
+// overlaps another's memory traffic.
+inline size_t skinny_gram_lds(int m) {
+  const size_t stage = (size_t)m * kStride * sizeof(float);
+  const size_t red = (size_t)kWaves * m * m * sizeof(double);
+  return stage > red ? stage : red;
+}
 
-  const int z = blockIdx.y, chunk = blockIdx.x;
+// One 256-column chunk of slice z: M <- beta M + G (stored), the chunk's sum
+// of squares and its Gram partial.  lds: skinny_gram_lds(m) bytes; wsq:
+// kWaves floats.
+template <bool BF16>
+__device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const DevScalars& S, int z, int chunk,
+                                           float* lds, float* wsq) {
+  float (*st)[kStride] = reinterpret_cast<float (*)[kStride]>(lds);  // rows 0 .. m-1
+  // The waves' Gram partials (float64, m x m each) reuse the staging block once it has been read.
+  double* red = reinterpret_cast<double*>(lds);
+
   const DevMat d = a.mats[z];
   const PtrEntry pe = a.ptrs[d.param];
-  const float beta = a.sc_out ? a.sv.beta : a.sc->beta;
-  const bool nesterov = (a.sc_out ? a.sv.nesterov : a.sc->nesterov) != 0;
-  if (a.sc_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.sc_out = a.sv;
+  const float beta = S.beta;
+  const bool nesterov = S.nesterov != 0;
   const int m = a.m, n = a.n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   ChunkMap cm;
@@ -167,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny_gram(SkinnyLaunch a) {
   char* const Mb = reinterpret_cast<char*>(pe.m + d.slice_off);
   const char* const Gb = static_cast<const char*>(pe.g) + d.slice_off * (d.gdtype ? 2 : 4);
 
-  zero_unfilled(st, m, cm.cw, tid);
+  zero_unfilled(st, m, m, cm.cw, tid);
 
   // Issue every load of the chunk, then M <- beta M + G, store M, stage the
   // matrix that is orthogonalised: M, or G + beta M with Nesterov momentum.
@@ -252,8 +262,11 @@ __global__ __launch_bounds__(kThreads) void k_skinny_gram(SkinnyLaunch a) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const int c = t * 32 + g * 16 + kh * 8;
-        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(&st[row][c]);
-        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(&st[row][c + 4]);
+        f32x4_t x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};  // rows >= m are zero
+        if (row < m) {
+          x0 = *reinterpret_cast<const f32x4_t*>(&st[row][c]);
+          x1 = *reinterpret_cast<const f32x4_t*>(&st[row][c + 4]);
+        }
         const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         uint32_t hw[4], lw[4];
 #pragma unroll
@@ -271,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny_gram(SkinnyLaunch a) {
     } else {
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        const float x = st[row][t * 32 + 2 * s + kh];
+        const float x = row < m ? st[row][t * 32 + 2 * s + kh] : 0.f;
         acc = mfma_f32(x, x, acc);
       }
     }
@@ -281,33 +294,216 @@ __global__ __launch_bounds__(kThreads) void k_skinny_gram(SkinnyLaunch a) {
   // Output layout: lane l, register r -> row rho(r, l / 32), column l % 32.
   __syncthreads();  // every wave is done reading the staging block
 #pragma unroll
-  for (int r = 0; r < 16; ++r) red[wave][rho(r, kh) * 32 + row] = accd[r];
+  for (int r = 0; r < 16; ++r) {
+    const int i = rho(r, kh);
+    if (i < m && row < m) red[(wave * m + i) * m + row] = accd[r];
+  }
   __syncthreads();
+  // The upper triangle (i <= j), packed row by row.
+  const int nt = m * (m + 1) / 2;
   const int64_t part = (int64_t)z * a.n_chunks + chunk;
-  for (int e = tid; e < m * m; e += kThreads) {  // the m x m block, row-major
-    const int i = e / m, j = e - i * m;
+  for (int e = tid; e < nt; e += kThreads) {
+    int i = 0, r = e;
+    while (r >= m - i) {
+      r -= m - i;
+      ++i;
+    }
+    const int o = i * m + i + r;
     double s = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += red[w][i * 32 + j];
-    a.gram_parts[part * m * m + e] = s;
+    for (int w = 0; w < kWaves; ++w) s += red[w * m * m + o];
+    a.gram_parts[part * nt + e] = s;
   }
   if (tid == 0) a.sq_parts[part] = ((wsq[0] + wsq[1]) + wsq[2]) + wsq[3];
 }
 
-// ------------------------------------------------------------------ apply
-// NEST: Nesterov momentum (X = G + beta M); chosen at launch from the plan so
-// that the plain kernel carries no second code path.
-template <bool BF16, bool NEST>
-__global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
-  __shared__ __attribute__((aligned(16))) float st[32][kStride];
-  __shared__ float qs[32][33];
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void k_skinny_gram(SkinnyLaunch a) {
+  extern __shared__ __attribute__((aligned(16))) float gram_lds[];
+  __shared__ float wsq[kWaves];
+  // The step's first kernel: scalars by value, written out for the later kernels.
+  const DevScalars S = a.sc_out ? a.sv : *a.sc;
+  if (a.sc_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.sc_out = a.sv;
+  gram_chunk<BF16>(a, S, blockIdx.y, blockIdx.x, gram_lds, wsq);
+}
 
-  const int z = blockIdx.y, chunk = blockIdx.x;
+// ------------------------------------------------------------------ poly
+// Per slice: s = 1/(||X||_F + eps) and A0 = s^2 (sum of the Gram partials),
+// then the rounds in the m x m Gram space (A_{t+1} = P_t^2 A_t,
+// Q = P_{k-1} ... P_0), all in float64, and finally s Q as float32.  Products
+// run on the float64 matrix cores: each of the four waves owns one 16 x 16
+// tile of a 32 x 32 result (16x16x4 float64 instruction: lane l supplies
+// X[l % 16][l / 16] and Y[l / 16][l % 16] of each 4-wide k step and receives
+// rows l / 16 + 4 r, r = 0..3, of column l % 16).  Everything outside the
+// leading m x m block stays zero, so k steps past m (KQ = ceil(m / 4) is a
+// template parameter, which keeps each product one straight run of
+// instructions) and tiles past m are skipped: they would add exact zeros.
+// A and Q are double-buffered, so a round needs three barriers.
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr int kPolyLd = 33;                                                  // row stride (doubles)
+constexpr int kPolyLds = (6 * 32 * kPolyLd + 1) * (int)sizeof(double);  // A[2], Q[2], P, S and s
+typedef double PolyRow[kPolyLd];
+
+template <int KQ>
+__device__ __forceinline__ void poly_slice(const SkinnyLaunch& a, const DevScalars& Sc, int z, double* lds) {
+  PolyRow* const base = reinterpret_cast<PolyRow*>(lds);
+  PolyRow* const P = base + 128;
+  PolyRow* const S = base + 160;
+  double* sh_s = lds + 6 * 32 * kPolyLd;
+  auto Abuf = [&](int i) { return base + 32 * i; };
+  auto Qbuf = [&](int i) { return base + 64 + 32 * i; };
+  const int m = a.m, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const double ca = Sc.a, cb = Sc.b, cc = Sc.c;
+  const int ns = Sc.ns_steps;
+  const int nt = m * (m + 1) / 2;
+  const int nch = a.n_chunks;
+
+  // Sum of squares: wave 3, a strided sum per lane and a butterfly.
+  if (wave == 3) {
+    const float* sq = a.sq_parts + (int64_t)z * nch;
+    double v = 0.0;
+    for (int c = lane; c < nch; c += 64) v += (double)sq[c];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) {
+      *sh_s = 1.0 / (sqrt(v) + (double)Sc.eps);
+      if (!isfinite(v)) atomicOr(a.err, kErrNonFinite);
+    }
+  }
+  // Gram sums over the packed upper triangles: entry v = tid + 256 k of the
+  // triangle (kPer = 3 covers m <= 32; KQ <= 5 means m <= 20, nt <= 210, one
+  // entry); the loads of a thread's entries for kBatch chunks are in flight
+  // together, and each entry is summed in chunk order.  Loads past the end
+  // read a valid address and are discarded, so the batch is one straight run.
+  constexpr int kBatch = 20, kPer = KQ <= 5 ? 1 : (KQ <= 7 ? 2 : 3);
+  const double* parts = a.gram_parts + (int64_t)z * nch * nt;
+  double sum[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) sum[k] = 0.0;
+  for (int c0 = 0; c0 < nch; c0 += kBatch) {
+    double part[kPer][kBatch];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int v = tid + kThreads * k, vc = v < nt ? v : 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int c = c0 + u < nch ? c0 + u : nch - 1;
+        part[k][u] = parts[(int64_t)c * nt + vc];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const bool in = tid + kThreads * k < nt;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) sum[k] += (in && c0 + u < nch) ? part[k][u] : 0.0;
+    }
+  }
+  for (int e = tid; e < 6 * 32 * kPolyLd; e += kThreads) lds[e] = 0.0;
+  __syncthreads();  // also publishes s
+  const double s = *sh_s;
+  for (int e = tid; e < m; e += kThreads) Qbuf(0)[e][e] = 1.0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int v = tid + kThreads * k;
+    if (v < nt) {
+      int i = 0, r = v;
+      while (r >= m - i) {
+        r -= m - i;
+        ++i;
+      }
+      const double x = sum[k] * s * s;
+      Abuf(0)[i][i + r] = x;
+      Abuf(0)[i + r][i] = x;
+    }
+  }
+  __syncthreads();
+
+  const int ti = 16 * (wave >> 1), tj = 16 * (wave & 1);
+  const int li = lane & 15, lk = lane >> 4;
+  const bool live = ti < m && tj < m;  // this wave's tile has entries inside m x m
+  // One tile of X Y: the operands of the k steps are read from LDS first,
+  // then the products run in two independent chains (even and odd k steps).
+  auto prod = [&](const PolyRow* X, const PolyRow* Y) {
+    double xv[KQ], yv[KQ];
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+      xv[q] = X[ti + li][4 * q + lk];
+      yv[q] = Y[4 * q + lk][tj + li];
+    }
+    f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int q = 0; q < KQ; q += 2) {
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[q], yv[q], acc0, 0, 0, 0);
+      if (q + 1 < KQ) acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[q + 1], yv[q + 1], acc1, 0, 0, 0);
+    }
+    // Every operand read is issued before the first product, so the LDS
+    // latency is paid once per tile rather than once per k step.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KQ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, KQ, 0);
+    return acc0 + acc1;
+  };
+  int cur = 0;
+  for (int it = 0; it < ns; ++it) {
+    const bool more = it + 1 < ns;
+    PolyRow* const Ac = Abuf(cur);
+    // P = a I + b A + c A^2
+    if (live) {
+      const f64x4_t t = prod(Ac, Ac);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = ti + lk + 4 * r, j = tj + li;
+        P[i][j] = cb * Ac[i][j] + cc * t[r] + ((i == j && i < m) ? ca : 0.0);
+      }
+    }
+    __syncthreads();
+    // Q' = P Q and, unless this is the last round, S = P P
+    if (live) {
+      const f64x4_t q = prod(P, Qbuf(cur));
+      PolyRow* const Qn = Qbuf(cur ^ 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Qn[ti + lk + 4 * r][tj + li] = q[r];
+      if (more) {
+        const f64x4_t sp = prod(P, P);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[ti + lk + 4 * r][tj + li] = sp[r];
+      }
+    }
+    __syncthreads();
+    if (more) {
+      // A' = S A
+      if (live) {
+        const f64x4_t t = prod(S, Ac);
+        PolyRow* const An = Abuf(cur ^ 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) An[ti + lk + 4 * r][tj + li] = t[r];
+      }
+      __syncthreads();
+    }
+    cur ^= 1;
+  }
+  PolyRow* const Qf = Qbuf(cur);
+  for (int e = tid; e < 1024; e += kThreads) a.qs[(int64_t)z * 1024 + e] = (float)(s * Qf[e >> 5][e & 31]);
+}
+
+template <int KQ>
+__global__ __launch_bounds__(kThreads) void k_skinny_poly(SkinnyLaunch a) {
+  __shared__ double poly_lds[kPolyLds / sizeof(double)];
+  poly_slice<KQ>(a, *a.sc, blockIdx.x, poly_lds);
+}
+
+// ------------------------------------------------------------------ apply
+// One 256-column chunk of slice z: O = Qs X (X = M, or G + beta M with
+// Nesterov momentum, NEST), W <- W - decay W - lr f O.  lds: m staged rows;
+// qs: 32 x 33 floats.
+template <bool BF16, bool NEST>
+__device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const DevScalars& S, int z, int chunk,
+                                            float* lds, float (*qs)[33]) {
+  float (*st)[kStride] = reinterpret_cast<float (*)[kStride]>(lds);
   const DevMat d = a.mats[z];
   const PtrEntry pe = a.ptrs[d.param];
-  const float lr = a.sc->lr, decay = a.sc->decay, beta = a.sc->beta;
+  const float lr = S.lr, decay = S.decay, beta = S.beta;
   const int m = a.m, n = a.n;
-  const float lrf = lr * update_factor(a.sc->scale_mode, m, n, d.transposed);
+  const float lrf = lr * update_factor(S.scale_mode, m, n, d.transposed);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   ChunkMap cm;
@@ -318,35 +514,38 @@ __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
 
   for (int e = tid; e < 1024; e += kThreads) qs[e >> 5][e & 31] = a.qs[(int64_t)z * 1024 + e];
 
-  // gmode: 0 = X is M; 1 / 2 = Nesterov, X = G + beta M with G in float32 / bf16.
+
+  // gmode: 0 = G is not read; 1 / 2 = Nesterov, X = G + beta M with G in
+  // float32 / bf16.
   auto run = [&](auto wtype, auto gmode) {
     using WT = decltype(wtype);
     constexpr int GM = decltype(gmode)::value;
     using GT = std::integral_constant<bool, GM == 2>;
-    float lm[kChunks][4], lw[kChunks][4];
+    float lm[kChunks][4], lw[kChunks][4], lg[kChunks][4];
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) {
       const int v = tid + kThreads * k;
       int64_t off = 0;
       int cnt = 0, i0 = 0, j0 = 0;
       if (v < cm.total) cm.piece(v, off, cnt, i0, j0);
-      float lg[4] = {0.f, 0.f, 0.f, 0.f};
       if (cnt == 4 && cm.vec_ok) {
         ld_vec4<F32>(Mb, off, lm[k]);
         ld_vec4<WT>(Wb, off, lw[k]);
-        if constexpr (GM != 0) ld_vec4<GT>(Gb, off, lg);
+        if constexpr (GM != 0) ld_vec4<GT>(Gb, off, lg[k]);
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           lm[k][u] = u < cnt ? ld_elem<F32>(Mb, off + u) : 0.f;
           lw[k][u] = u < cnt ? ld_elem<WT>(Wb, off + u) : 0.f;
-          if constexpr (GM != 0) lg[u] = u < cnt ? ld_elem<GT>(Gb, off + u) : 0.f;
+          if constexpr (GM != 0) lg[k][u] = u < cnt ? ld_elem<GT>(Gb, off + u) : 0.f;
         }
       }
-      if constexpr (GM != 0) {
+    }
+    if constexpr (NEST) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) lm[k][u] = fmaf(beta, lm[k][u], lg[u]);
-      }
+      for (int k = 0; k < kChunks; ++k)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lm[k][u] = fmaf(beta, lm[k][u], lg[k][u]);
     }
     // Stage X (M, or G + beta M) in oriented order.
 #pragma unroll
@@ -396,7 +595,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
       const int j = t * 32 + col;
       float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = st[rho(r, h)][j];  // rows >= m and columns >= cw are zero
+      for (int r = 0; r < 16; ++r) x[r] = rho(r, h) < m ? st[rho(r, h)][j] : 0.f;  // columns >= cw are zero
       f32x16_t o = {};
       if constexpr (BF16) {
 #pragma unroll
@@ -423,7 +622,8 @@ __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[rho(r, h)][j] = o[r];
+      for (int r = 0; r < 16; ++r)
+        if (rho(r, h) < m) st[rho(r, h)][j] = o[r];
     }
     __syncthreads();
 
@@ -457,8 +657,8 @@ __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
       }
     }
   };
-  // Rows >= m and columns >= cw of the staging block read as zero.
-  zero_unfilled(st, m, cm.cw, tid);
+  // Columns >= cw of the staged rows read as zero.
+  zero_unfilled(st, m, m, cm.cw, tid);
   using G0 = std::integral_constant<int, 0>;
   using G1 = std::integral_constant<int, 1>;
   using G2 = std::integral_constant<int, 2>;
@@ -474,23 +674,50 @@ __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
   }
 }
 
+// NEST is chosen at launch from the plan, so the plain kernel carries no
+// second code path.
+template <bool BF16, bool NEST>
+__global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
+  extern __shared__ __attribute__((aligned(16))) float apply_lds[];  // m staged rows
+  __shared__ float qs[32][33];
+  apply_chunk<BF16, NEST>(a, *a.sc, blockIdx.y, blockIdx.x, apply_lds, qs);
+}
+
 }  // namespace
 
 hipError_t launch_skinny_gram(const SkinnyLaunch& a, hipStream_t s) {
   const dim3 grid(a.n_chunks, a.count);
-  if (a.bf16) hipLaunchKernelGGL(k_skinny_gram<true>, grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(k_skinny_gram<false>, grid, dim3(kThreads), 0, s, a);
+  const size_t lds = skinny_gram_lds(a.m);
+  if (a.bf16) hipLaunchKernelGGL(k_skinny_gram<true>, grid, dim3(kThreads), lds, s, a);
+  else hipLaunchKernelGGL(k_skinny_gram<false>, grid, dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny_poly(const SkinnyLaunch& a, hipStream_t s) {
+  const dim3 grid(a.count), block(kThreads);
+  switch ((a.m + 3) >> 2) {
+    case 1: hipLaunchKernelGGL(k_skinny_poly<1>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_skinny_poly<2>, grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL(k_skinny_poly<3>, grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL(k_skinny_poly<4>, grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL(k_skinny_poly<5>, grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL(k_skinny_poly<6>, grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL(k_skinny_poly<7>, grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL(k_skinny_poly<8>, grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_skinny_apply(const SkinnyLaunch& a, hipStream_t s) {
   const dim3 grid(a.n_chunks, a.count);
+  const size_t lds = (size_t)a.m * kStride * sizeof(float);
   if (a.nesterov) {
-    if (a.bf16) hipLaunchKernelGGL((k_skinny_apply<true, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_skinny_apply<false, true>), grid, dim3(kThreads), 0, s, a);
+    if (a.bf16) hipLaunchKernelGGL((k_skinny_apply<true, true>), grid, dim3(kThreads), lds, s, a);
+    else hipLaunchKernelGGL((k_skinny_apply<false, true>), grid, dim3(kThreads), lds, s, a);
   } else {
-    if (a.bf16) hipLaunchKernelGGL((k_skinny_apply<true, false>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_skinny_apply<false, false>), grid, dim3(kThreads), 0, s, a);
+    if (a.bf16) hipLaunchKernelGGL((k_skinny_apply<true, false>), grid, dim3(kThreads), lds, s, a);
+    else hipLaunchKernelGGL((k_skinny_apply<false, false>), grid, dim3(kThreads), lds, s, a);
   }
   return hipGetLastError();
 }
