@@ -106,7 +106,6 @@ hipError_t enqueue_skinny(muon_plan_t plan, const muon::BucketPlan& bp, hipStrea
     L.sc_out = at<muon::DevScalars>(plan, p.off_scalars);
   }
   L.gram_parts = at<double>(plan, bp.off_gram);
-  L.sq_parts = at<float>(plan, bp.off_sqp);
   L.qs = at<float>(plan, bp.off_qs);
   L.err = at<uint32_t>(plan, p.off_err);
   L.m = (int)bp.m;

@@ -21,7 +21,6 @@ struct SkinnyLaunch {
   DevScalars sv;          // scalars by value (used when sc_out is set)
   DevScalars* sc_out;     // null, or the scalar block to fill
   double* gram_parts;     // [count][n_chunks][m(m+1)/2]: upper triangles, packed by rows
-  float* sq_parts;        // [count][n_chunks]
   float* qs;              // [count][32*32]: s * Q
   uint32_t* err;          // device error word
   int m, n, n_chunks, count;

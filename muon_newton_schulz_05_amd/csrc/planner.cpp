@@ -191,7 +191,6 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
     if (bp.path == MUON_PATH_SKINNY) {
       bp.n_chunks = (int)((bp.n + kSkinnyChunk - 1) / kSkinnyChunk);
       bp.off_gram = ws.take(cnt * bp.n_chunks * (bp.m * (bp.m + 1) / 2) * sizeof(double));  // upper triangles
-      bp.off_sqp = ws.take(cnt * bp.n_chunks * sizeof(float));
       bp.off_qs = ws.take(cnt * 1024 * sizeof(float));
       p.launches_fixed += 3;  // momentum + Gram partials, polynomial, apply + update
     } else {

@@ -31,7 +31,7 @@ struct BucketPlan {
 
   // skinny path (m <= 32)
   int n_chunks = 0;         // 256-column chunks per slice
-  uint64_t off_gram = 0, off_sqp = 0, off_qs = 0;
+  uint64_t off_gram = 0, off_qs = 0;
 
   // streamed path
   bool big = false;         // bf16 mode and m >= kBigMinM: 256 x 256 tile products

@@ -146,38 +146,54 @@ __device__ __forceinline__ void zero_unfilled(float (*st)[kStride], int rows, in
 }
 
 // ------------------------------------------------------------------ gram
-// LDS of k_skinny_gram: the m staged rows, or the waves' m x m float64
-// partials that reuse them, whichever is larger.  Holding only m rows (not
-// 32) lets more workgroups share a CU, so one workgroup's arithmetic
-// overlaps another's memory traffic.
-inline size_t skinny_gram_lds(int m) {
+// LDS of k_skinny_gram.  bf16 mode: the m staged rows as two bf16 planes,
+// hi = bf16(x) and lo = bf16(x - hi).  fp32 mode: the m staged float32 rows,
+// or the waves' m x m float64 partials that reuse them, whichever is larger.
+// Holding only m rows (not 32) lets more workgroups share a CU, so one
+// workgroup's arithmetic overlaps another's memory traffic.
+constexpr int kBStride = kCols + 8;  // bf16 plane row stride (elements; rows stay 16-byte aligned)
+inline size_t skinny_gram_lds(int m, bool bf16) {
+  if (bf16) return (size_t)2 * m * kBStride * sizeof(uint16_t);
   const size_t stage = (size_t)m * kStride * sizeof(float);
   const size_t red = (size_t)kWaves * m * m * sizeof(double);
   return stage > red ? stage : red;
 }
 
-// One 256-column chunk of slice z: M <- beta M + G (stored), the chunk's sum
-// of squares and its Gram partial.  lds: skinny_gram_lds(m) bytes; wsq:
-// kWaves floats.
-template <bool BF16>
-__device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const DevScalars& S, int z, int chunk,
-                                           float* lds, float* wsq) {
-  float (*st)[kStride] = reinterpret_cast<float (*)[kStride]>(lds);  // rows 0 .. m-1
-  // The waves' Gram partials (float64, m x m each) reuse the staging block once it has been read.
-  double* red = reinterpret_cast<double*>(lds);
+// Position of (i, j), i <= j, in an m x m upper triangle packed row by row.
+__device__ __forceinline__ int tri_index(int i, int j, int m) { return i * m - (i * (i - 1)) / 2 + (j - i); }
 
+// One 256-column chunk of slice z: M <- beta M + G (stored) and the chunk's
+// Gram partial of X0 (M, or G + beta M with Nesterov momentum), stored as its
+// packed upper triangle in float64.  (The slice's sum of squares is the
+// trace of the summed partials.)  lds: skinny_gram_lds(m, BF16) bytes.
+template <bool BF16>
+__device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const DevScalars& S, int z, int chunk, float* lds) {
+  float (*st)[kStride] = reinterpret_cast<float (*)[kStride]>(lds);         // fp32 mode: rows 0 .. m-1
+  uint16_t (*H)[kBStride] = reinterpret_cast<uint16_t (*)[kBStride]>(lds);  // bf16 mode: hi plane
   const DevMat d = a.mats[z];
   const PtrEntry pe = a.ptrs[d.param];
   const float beta = S.beta;
   const bool nesterov = S.nesterov != 0;
   const int m = a.m, n = a.n;
+  uint16_t (*L)[kBStride] = H + m;                                           // bf16 mode: lo plane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   ChunkMap cm;
   cm.init(m, n, chunk * kCols, min(kCols, n - chunk * kCols), d.transposed != 0, d.slice_off);
   char* const Mb = reinterpret_cast<char*>(pe.m + d.slice_off);
   const char* const Gb = static_cast<const char*>(pe.g) + d.slice_off * (d.gdtype ? 2 : 4);
 
-  zero_unfilled(st, m, m, cm.cw, tid);
+  // Columns >= cw of the staged rows read as zero.
+  if constexpr (BF16) {
+    if (cm.cw < kCols) {
+      const int w = kCols - cm.cw;
+      for (int e = tid; e < m * w; e += kThreads) {
+        H[e / w][cm.cw + e % w] = 0;
+        L[e / w][cm.cw + e % w] = 0;
+      }
+    }
+  } else {
+    zero_unfilled(st, m, m, cm.cw, tid);
+  }
 
   // Issue every load of the chunk, then M <- beta M + G, store M, stage the
   // matrix that is orthogonalised: M, or G + beta M with Nesterov momentum.
@@ -221,15 +237,35 @@ __device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const DevScala
         for (int u = 0; u < 4; ++u)
           if (u < cnt) st_elem<F32>(Mb, off + u, mn[u]);
       }
-      if (!cm.tr && cnt == 4) {
-        *reinterpret_cast<f32x4_t*>(&st[i0][j0]) = f32x4_t{xs[0], xs[1], xs[2], xs[3]};
-      } else {
+      if constexpr (BF16) {
+        if (!cm.tr && cnt == 4) {
+          const uint32_t h0 = pack_bf16x2(xs[0], xs[1]), h1 = pack_bf16x2(xs[2], xs[3]);
+          const uint32_t l0 = pack_bf16x2(xs[0] - bf16_lo(h0), xs[1] - bf16_hi(h0));
+          const uint32_t l1 = pack_bf16x2(xs[2] - bf16_lo(h1), xs[3] - bf16_hi(h1));
+          *reinterpret_cast<u32x2_t*>(&H[i0][j0]) = u32x2_t{h0, h1};
+          *reinterpret_cast<u32x2_t*>(&L[i0][j0]) = u32x2_t{l0, l1};
+        } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (u >= cnt) break;
-          int i, j;
-          cm.pos(i0, j0, u, i, j);
-          st[i][j] = xs[u];
+          for (int u = 0; u < 4; ++u) {
+            if (u >= cnt) break;
+            int i, j;
+            cm.pos(i0, j0, u, i, j);
+            const uint16_t h = to_bf16(xs[u]);
+            H[i][j] = h;
+            L[i][j] = to_bf16(xs[u] - from_bf16(h));
+          }
+        }
+      } else {
+        if (!cm.tr && cnt == 4) {
+          *reinterpret_cast<f32x4_t*>(&st[i0][j0]) = f32x4_t{xs[0], xs[1], xs[2], xs[3]};
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (u >= cnt) break;
+            int i, j;
+            cm.pos(i0, j0, u, i, j);
+            st[i][j] = xs[u];
+          }
         }
       }
     }
@@ -238,99 +274,109 @@ __device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const DevScala
   else pass(F32{});
   __syncthreads();
 
-  // Sum of squares in oriented order: thread t owns columns t, t + 256.
-  float sq = 0.f;
-  for (int j = tid; j < kCols; j += kThreads)
-    for (int i = 0; i < m; ++i) sq = fmaf(st[i][j], st[i][j], sq);
-  sq = wave_sum(sq);
-  if (lane == 0) wsq[wave] = sq;
-
-  // Gram partial: lane l holds row l % 32; both operands are the same rows.
-  // Each 32-column tile is accumulated in float32 on the matrix cores and
-  // added into a float64 running sum, so the partial's rounding does not
-  // grow with the chunk width.
-  double accd[16];
+  const int nt = m * (m + 1) / 2;
+  double* const out = a.gram_parts + ((int64_t)z * a.n_chunks + chunk) * nt;
+  if constexpr (BF16) {
+    // Wave w owns the 16 x 16 output tile (16 (w / 2), 16 (w % 2)) over all
+    // columns of the chunk; the tile below the diagonal mirrors the one above
+    // it and is skipped.  16x16x32 bf16 products (lane l: row l % 16 of the
+    // tile's A rows and of its B rows, k = 8 (l / 16) .. + 7 of each 32-column
+    // step; result rows 4 (l / 16) + r, column l % 16) accumulate
+    // hi hi + hi lo + lo hi + lo lo, about float32 accuracy, in float32 per
+    // 32-column step and in float64 across steps, so the partial's rounding
+    // does not grow with the chunk width.
+    const int ti = 16 * (wave >> 1), tj = 16 * (wave & 1);
+    if (ti <= tj && tj < m) {
+      const int li = lane & 15, kg = lane >> 4;
+      const int ra = ti + li, rb = tj + li;
+      double accd[4] = {0.0, 0.0, 0.0, 0.0};
+      const bf16x8_t zero = as_bf16x8(0u, 0u, 0u, 0u);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) accd[r] = 0.0;
-  const int row = lane & 31, kh = lane >> 5;
-#pragma unroll
-  for (int q = 0; q < kTilesPerWave; ++q) {
-    const int t = wave + kWaves * q;
-    if (t * 32 >= cm.cw) break;
-    f32x16_t acc = {};
-    if constexpr (BF16) {
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int c = t * 32 + g * 16 + kh * 8;
-        f32x4_t x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};  // rows >= m are zero
-        if (row < m) {
-          x0 = *reinterpret_cast<const f32x4_t*>(&st[row][c]);
-          x1 = *reinterpret_cast<const f32x4_t*>(&st[row][c + 4]);
+      for (int t = 0; t < kCols / 32; ++t) {
+        if (t * 32 >= cm.cw) break;
+        const int c = t * 32 + kg * 8;
+        bf16x8_t ah = zero, al = zero, bh = zero, bl = zero;  // rows >= m are zero
+        if (ra < m) {
+          ah = *reinterpret_cast<const bf16x8_t*>(&H[ra][c]);
+          al = *reinterpret_cast<const bf16x8_t*>(&L[ra][c]);
         }
-        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          hw[u] = pack_bf16x2(x[2 * u], x[2 * u + 1]);
-          lw[u] = pack_bf16x2(x[2 * u] - bf16_lo(hw[u]), x[2 * u + 1] - bf16_hi(hw[u]));
+        if (ti == tj) {
+          bh = ah;
+          bl = al;
+        } else if (rb < m) {
+          bh = *reinterpret_cast<const bf16x8_t*>(&H[rb][c]);
+          bl = *reinterpret_cast<const bf16x8_t*>(&L[rb][c]);
         }
-        const bf16x8_t xh = as_bf16x8(hw[0], hw[1], hw[2], hw[3]);
-        const bf16x8_t xl = as_bf16x8(lw[0], lw[1], lw[2], lw[3]);
-        acc = mfma_bf16(xh, xh, acc);
-        acc = mfma_bf16(xh, xl, acc);
-        acc = mfma_bf16(xl, xh, acc);
-        acc = mfma_bf16(xl, xl, acc);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bl, acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accd[r] += (double)acc[r];
       }
-    } else {
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const float x = row < m ? st[row][t * 32 + 2 * s + kh] : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int i = ti + 4 * kg + r, j = tj + li;
+        if (i <= j && j < m) out[tri_index(i, j, m)] = accd[r];
+      }
+    }
+  } else {
+    // fp32: lane l holds row l % 32 and both operands are the same rows; wave
+    // w takes 32-column tiles w, w + 4, ...  Each tile is accumulated in
+    // float32 on the matrix cores and added into a float64 running sum; the
+    // four waves' partials are added through LDS.
+    double* red = reinterpret_cast<double*>(lds);
+    double accd[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accd[r] = 0.0;
+    const int row = lane & 31, kh = lane >> 5;
+#pragma unroll
+    for (int q = 0; q < kTilesPerWave; ++q) {
+      const int t = wave + kWaves * q;
+      if (t * 32 >= cm.cw) break;
+      f32x16_t acc = {};
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) {
+        const float x = row < m ? st[row][t * 32 + 2 * s2 + kh] : 0.f;
         acc = mfma_f32(x, x, acc);
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) accd[r] += (double)acc[r];
     }
+    // Output layout: lane l, register r -> row rho(r, l / 32), column l % 32.
+    __syncthreads();  // every wave is done reading the staging block
 #pragma unroll
-    for (int r = 0; r < 16; ++r) accd[r] += (double)acc[r];
-  }
-  // Output layout: lane l, register r -> row rho(r, l / 32), column l % 32.
-  __syncthreads();  // every wave is done reading the staging block
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = rho(r, kh);
-    if (i < m && row < m) red[(wave * m + i) * m + row] = accd[r];
-  }
-  __syncthreads();
-  // The upper triangle (i <= j), packed row by row.
-  const int nt = m * (m + 1) / 2;
-  const int64_t part = (int64_t)z * a.n_chunks + chunk;
-  for (int e = tid; e < nt; e += kThreads) {
-    int i = 0, r = e;
-    while (r >= m - i) {
-      r -= m - i;
-      ++i;
+    for (int r = 0; r < 16; ++r) {
+      const int i = rho(r, kh);
+      if (i < m && row < m) red[(wave * m + i) * m + row] = accd[r];
     }
-    const int o = i * m + i + r;
-    double s = 0.0;
+    __syncthreads();
+    for (int e = tid; e < m * m; e += kThreads) {
+      const int i = e / m, j = e - i * m;
+      if (i > j) continue;
+      double sum = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += red[w * m * m + o];
-    a.gram_parts[part * nt + e] = s;
+      for (int w = 0; w < kWaves; ++w) sum += red[w * m * m + e];
+      out[tri_index(i, j, m)] = sum;
+    }
   }
-  if (tid == 0) a.sq_parts[part] = ((wsq[0] + wsq[1]) + wsq[2]) + wsq[3];
 }
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void k_skinny_gram(SkinnyLaunch a) {
   extern __shared__ __attribute__((aligned(16))) float gram_lds[];
-  __shared__ float wsq[kWaves];
   // The step's first kernel: scalars by value, written out for the later kernels.
   const DevScalars S = a.sc_out ? a.sv : *a.sc;
   if (a.sc_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.sc_out = a.sv;
-  gram_chunk<BF16>(a, S, blockIdx.y, blockIdx.x, gram_lds, wsq);
+  gram_chunk<BF16>(a, S, blockIdx.y, blockIdx.x, gram_lds);
 }
 
 // ------------------------------------------------------------------ poly
-// Per slice: s = 1/(||X||_F + eps) and A0 = s^2 (sum of the Gram partials),
-// then the rounds in the m x m Gram space (A_{t+1} = P_t^2 A_t,
-// Q = P_{k-1} ... P_0), all in float64, and finally s Q as float32.  Products
+// Per slice: the sum of the Gram partials, s = 1/(||X||_F + eps) from its
+// trace, A0 = s^2 (the sum), then the rounds in the m x m Gram space
+// (A_{t+1} = P_t^2 A_t, Q = P_{k-1} ... P_0), all in float64, and finally
+// s Q as float32.  Products
 // run on the float64 matrix cores: each of the four waves owns one 16 x 16
 // tile of a 32 x 32 result (16x16x4 float64 instruction: lane l supplies
 // X[l % 16][l / 16] and Y[l / 16][l % 16] of each 4-wide k step and receives
@@ -358,18 +404,6 @@ __device__ __forceinline__ void poly_slice(const SkinnyLaunch& a, const DevScala
   const int nt = m * (m + 1) / 2;
   const int nch = a.n_chunks;
 
-  // Sum of squares: wave 3, a strided sum per lane and a butterfly.
-  if (wave == 3) {
-    const float* sq = a.sq_parts + (int64_t)z * nch;
-    double v = 0.0;
-    for (int c = lane; c < nch; c += 64) v += (double)sq[c];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if (lane == 0) {
-      *sh_s = 1.0 / (sqrt(v) + (double)Sc.eps);
-      if (!isfinite(v)) atomicOr(a.err, kErrNonFinite);
-    }
-  }
   // Gram sums over the packed upper triangles: entry v = tid + 256 k of the
   // triangle (kPer = 3 covers m <= 32; KQ <= 5 means m <= 20, nt <= 210, one
   // entry); the loads of a thread's entries for kBatch chunks are in flight
@@ -399,21 +433,47 @@ __device__ __forceinline__ void poly_slice(const SkinnyLaunch& a, const DevScala
     }
   }
   for (int e = tid; e < 6 * 32 * kPolyLd; e += kThreads) lds[e] = 0.0;
-  __syncthreads();  // also publishes s
-  const double s = *sh_s;
-  for (int e = tid; e < m; e += kThreads) Qbuf(0)[e][e] = 1.0;
+  __syncthreads();
+  // The summed Gram matrix, both triangles.
+  int row[kPer], col[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int v = tid + kThreads * k;
-    if (v < nt) {
-      int i = 0, r = v;
+    int i = 0, r = tid + kThreads * k;
+    if (r < nt) {
       while (r >= m - i) {
         r -= m - i;
         ++i;
       }
+    }
+    row[k] = i;
+    col[k] = i + r;
+    if (tid + kThreads * k < nt) {
+      Abuf(0)[i][i + r] = sum[k];
+      Abuf(0)[i + r][i] = sum[k];
+    }
+  }
+  for (int e = tid; e < m; e += kThreads) Qbuf(0)[e][e] = 1.0;
+  __syncthreads();
+  // Sum of squares of X0 = trace of its Gram matrix (wave 0: one diagonal
+  // entry per lane, then a butterfly); s = 1 / (||X0||_F + eps).
+  if (wave == 0) {
+    double v = lane < m ? Abuf(0)[lane][lane] : 0.0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) {
+      *sh_s = 1.0 / (sqrt(v) + (double)Sc.eps);
+      if (!isfinite(v)) atomicOr(a.err, kErrNonFinite);
+    }
+  }
+  __syncthreads();
+  const double s = *sh_s;
+  // A0 = s^2 (X0 X0^T), each thread scaling the entries it wrote.
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    if (tid + kThreads * k < nt) {
       const double x = sum[k] * s * s;
-      Abuf(0)[i][i + r] = x;
-      Abuf(0)[i + r][i] = x;
+      Abuf(0)[row[k]][col[k]] = x;
+      Abuf(0)[col[k]][row[k]] = x;
     }
   }
   __syncthreads();
@@ -687,7 +747,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
 
 hipError_t launch_skinny_gram(const SkinnyLaunch& a, hipStream_t s) {
   const dim3 grid(a.n_chunks, a.count);
-  const size_t lds = skinny_gram_lds(a.m);
+  const size_t lds = skinny_gram_lds(a.m, a.bf16 != 0);
   if (a.bf16) hipLaunchKernelGGL(k_skinny_gram<true>, grid, dim3(kThreads), lds, s, a);
   else hipLaunchKernelGGL(k_skinny_gram<false>, grid, dim3(kThreads), lds, s, a);
   return hipGetLastError();
