@@ -147,13 +147,14 @@ __device__ __forceinline__ void zero_unfilled(float (*st)[kStride], int rows, in
 
 // ------------------------------------------------------------------ gram
 // LDS of k_skinny_gram.  bf16 mode: the m staged rows as two bf16 planes,
-// hi = bf16(x) and lo = bf16(x - hi).  fp32 mode: the m staged float32 rows,
+// hi = bf16(x) and lo = bf16(x - hi), each with one more row of zeros (row
+// m) that stands in for the padding rows m .. 31 of the products.  fp32 mode: the m staged float32 rows,
 // or the waves' m x m float64 partials that reuse them, whichever is larger.
 // Holding only m rows (not 32) lets more workgroups share a CU, so one
 // workgroup's arithmetic overlaps another's memory traffic.
 constexpr int kBStride = kCols + 8;  // bf16 plane row stride (elements; rows stay 16-byte aligned)
 inline size_t skinny_gram_lds(int m, bool bf16) {
-  if (bf16) return (size_t)2 * m * kBStride * sizeof(uint16_t);
+  if (bf16) return (size_t)2 * (m + 1) * kBStride * sizeof(uint16_t);
   const size_t stage = (size_t)m * kStride * sizeof(float);
   const size_t red = (size_t)kWaves * m * m * sizeof(double);
   return stage > red ? stage : red;
@@ -175,15 +176,21 @@ __device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const DevScala
   const float beta = S.beta;
   const bool nesterov = S.nesterov != 0;
   const int m = a.m, n = a.n;
-  uint16_t (*L)[kBStride] = H + m;                                           // bf16 mode: lo plane
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint16_t (*L)[kBStride] = H + m + 1;                                       // bf16 mode: lo plane
+  const int tid = threadIdx.x, lane = tid & 63;
+  // The wave index is uniform over the wave; saying so keeps branches on it scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   ChunkMap cm;
   cm.init(m, n, chunk * kCols, min(kCols, n - chunk * kCols), d.transposed != 0, d.slice_off);
   char* const Mb = reinterpret_cast<char*>(pe.m + d.slice_off);
   const char* const Gb = static_cast<const char*>(pe.g) + d.slice_off * (d.gdtype ? 2 : 4);
 
-  // Columns >= cw of the staged rows read as zero.
+  // Columns >= cw of the staged rows, and the zero row m, read as zero.
   if constexpr (BF16) {
+    for (int e = tid; e < kCols; e += kThreads) {
+      H[m][e] = 0;
+      L[m][e] = 0;
+    }
     if (cm.cw < kCols) {
       const int w = kCols - cm.cw;
       for (int e = tid; e < m * w; e += kThreads) {
@@ -289,29 +296,38 @@ __device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const DevScala
     if (ti <= tj && tj < m) {
       const int li = lane & 15, kg = lane >> 4;
       const int ra = ti + li, rb = tj + li;
+      const bool diag = ti == tj;
       double accd[4] = {0.0, 0.0, 0.0, 0.0};
-      const bf16x8_t zero = as_bf16x8(0u, 0u, 0u, 0u);
+      // Operands of step t (columns 32 t .. 32 t + 31).  Rows >= m read the
+      // zero row m.  All eight steps run: columns >= cw are zero in the
+      // planes, so the steps past the chunk width add exact zeros.  Step
+      // t + 1's operands are read while step t's products run.
+      bf16x8_t ah[2], al[2], bh[2], bl[2];
+      const int rac = min(ra, m), rbc = min(rb, m);
+      auto rd = [](const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); };
+      auto fetch = [&](int t, int buf) {
+        const int c = t * 32 + kg * 8;
+        ah[buf] = rd(&H[rac][c]);
+        al[buf] = rd(&L[rac][c]);
+        if (!diag) {
+          bh[buf] = rd(&H[rbc][c]);
+          bl[buf] = rd(&L[rbc][c]);
+        } else {
+          bh[buf] = ah[buf];
+          bl[buf] = al[buf];
+        }
+      };
+      fetch(0, 0);
 #pragma unroll
       for (int t = 0; t < kCols / 32; ++t) {
-        if (t * 32 >= cm.cw) break;
-        const int c = t * 32 + kg * 8;
-        bf16x8_t ah = zero, al = zero, bh = zero, bl = zero;  // rows >= m are zero
-        if (ra < m) {
-          ah = *reinterpret_cast<const bf16x8_t*>(&H[ra][c]);
-          al = *reinterpret_cast<const bf16x8_t*>(&L[ra][c]);
-        }
-        if (ti == tj) {
-          bh = ah;
-          bl = al;
-        } else if (rb < m) {
-          bh = *reinterpret_cast<const bf16x8_t*>(&H[rb][c]);
-          bl = *reinterpret_cast<const bf16x8_t*>(&L[rb][c]);
-        }
+        const int cb = t & 1;
+        if (t + 1 < kCols / 32) fetch(t + 1, cb ^ 1);
+        const bf16x8_t xh = bh[cb], xl = bl[cb];
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[cb], xh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[cb], xl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[cb], xh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[cb], xl, acc, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) accd[r] += (double)acc[r];
       }
