@@ -569,8 +569,9 @@ __global__ __launch_bounds__(kThreads) void k_skinny_poly(SkinnyLaunch a) {
 
 // ------------------------------------------------------------------ apply
 // One 256-column chunk of slice z: O = Qs X (X = M, or G + beta M with
-// Nesterov momentum, NEST), W <- W - decay W - lr f O.  lds: m staged rows;
-// qs: 32 x 33 floats.
+// Nesterov momentum, NEST), W <- W - decay W - lr f O.  lds: 32 staged
+// rows (rows m .. 31 are zero, so the products read and write them without
+// per-lane guards); qs: 32 x 33 floats.
 template <bool BF16, bool NEST>
 __device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const DevScalars& S, int z, int chunk,
                                             float* lds, float (*qs)[33]) {
@@ -671,7 +672,7 @@ __device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const DevScal
       const int j = t * 32 + col;
       float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = rho(r, h) < m ? st[rho(r, h)][j] : 0.f;  // columns >= cw are zero
+      for (int r = 0; r < 16; ++r) x[r] = st[rho(r, h)][j];  // rows >= m and columns >= cw are zero
       f32x16_t o = {};
       if constexpr (BF16) {
 #pragma unroll
@@ -697,9 +698,9 @@ __device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const DevScal
           o = mfma_f32(qf[r], x[r], o);
         }
       }
+      // Rows >= m of O are zero (so are those rows of Qs).
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (rho(r, h) < m) st[rho(r, h)][j] = o[r];
+      for (int r = 0; r < 16; ++r) st[rho(r, h)][j] = o[r];
     }
     __syncthreads();
 
@@ -733,8 +734,8 @@ __device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const DevScal
       }
     }
   };
-  // Columns >= cw of the staged rows read as zero.
-  zero_unfilled(st, m, m, cm.cw, tid);
+  // Rows m .. 31, and columns >= cw of the staged rows, read as zero.
+  zero_unfilled(st, 32, m, cm.cw, tid);
   using G0 = std::integral_constant<int, 0>;
   using G1 = std::integral_constant<int, 1>;
   using G2 = std::integral_constant<int, 2>;
@@ -754,7 +755,7 @@ __device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const DevScal
 // second code path.
 template <bool BF16, bool NEST>
 __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
-  extern __shared__ __attribute__((aligned(16))) float apply_lds[];  // m staged rows
+  extern __shared__ __attribute__((aligned(16))) float apply_lds[];  // 32 staged rows
   __shared__ float qs[32][33];
   apply_chunk<BF16, NEST>(a, *a.sc, blockIdx.y, blockIdx.x, apply_lds, qs);
 }
@@ -787,7 +788,7 @@ hipError_t launch_skinny_poly(const SkinnyLaunch& a, hipStream_t s) {
 
 hipError_t launch_skinny_apply(const SkinnyLaunch& a, hipStream_t s) {
   const dim3 grid(a.n_chunks, a.count);
-  const size_t lds = (size_t)a.m * kStride * sizeof(float);
+  const size_t lds = (size_t)32 * kStride * sizeof(float);
   if (a.nesterov) {
     if (a.bf16) hipLaunchKernelGGL((k_skinny_apply<true, true>), grid, dim3(kThreads), lds, s, a);
     else hipLaunchKernelGGL((k_skinny_apply<false, true>), grid, dim3(kThreads), lds, s, a);
