@@ -149,14 +149,16 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
     }
   }
 
-  // Bucket by oriented shape, in order of first appearance.
+  // Bucket by oriented shape, in order of first appearance.  Launches put
+  // the slice index of a bucket in a grid dimension that holds at most
+  // kMaxBucketSlices, so a larger group of one shape fills several buckets.
   std::map<std::pair<int64_t, int64_t>, int> index;
   for (int si = 0; si < (int)p.slices.size(); ++si) {
     Slice& s = p.slices[si];
     auto key = std::make_pair(s.m, s.n);
     auto it = index.find(key);
     int b;
-    if (it == index.end()) {
+    if (it == index.end() || (int64_t)p.buckets[it->second].slices.size() >= kMaxBucketSlices) {
       if ((int)p.buckets.size() >= MUON_MAX_BUCKETS) {
         std::snprintf(buf, sizeof buf, "more than %d distinct oriented shapes", MUON_MAX_BUCKETS);
         *err = buf;

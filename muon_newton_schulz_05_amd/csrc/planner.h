@@ -23,6 +23,9 @@ struct Slice {
   int bucket = -1;
 };
 
+// Slices per bucket: the launches index them in a grid dimension.
+constexpr int64_t kMaxBucketSlices = 65535;
+
 struct BucketPlan {
   int64_t m = 0, n = 0;
   int path = MUON_PATH_STREAM;

@@ -121,6 +121,22 @@ def test_fusion_is_bitexact(mode):
         assert np.array_equal(w_f[i], w_1[0]) and np.array_equal(m_f[i], m_1[0]), f"slice {i}"
 
 
+def test_shape_group_larger_than_one_bucket():
+    """70000 slices of [8,16] fill two buckets (a launch indexes at most 65535
+    slices); sampled slices of both, first and last included, match the
+    oracle run on those slices alone."""
+    shape = (70000, 8, 16)
+    params, grads, moms = make_inputs([shape], "bf16", 77, w_std=0.02)
+    w_gpu, m_gpu = gpu_step(params, grads, moms, mode="bf16", lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    picks = [0, 1, 65534, 65535, 65536, 69999] + list(range(1000, 70000, 9973))
+    sub = [a[0][picks] for a in (params, grads, moms)]
+    w_ref, m_ref, o_ref = oracle_step([sub[0]], [sub[1]], [sub[2]], lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    errs = update_errors(w_gpu[0][picks], sub[0], 0.02, o_ref[0])
+    print(f"{shape}: worst {max(errs):.3e} over {len(picks)} sampled slices", flush=True)
+    assert max(errs) <= TOL["bf16"]
+    assert max_ulp_diff(m_gpu[0][picks], m_ref[0]) <= 1
+
+
 @pytest.mark.parametrize("mode", ["bf16", "fp32"])
 def test_3d_equals_2d_slices(mode):
     shapes3 = [(3, 24, 900), (2, 80, 150)]

@@ -132,6 +132,14 @@ def test_chunks_depend_on_shape_not_batch(m):
     assert fp32["buckets"][0]["chunks"] == 40 and fp32["buckets"][0]["path"] == "skinny"
 
 
+def test_large_shape_groups_split_into_buckets_the_grid_can_index(m):
+    """Launches index a bucket's slices in a grid dimension of at most 65535
+    entries, so 70000 slices of one shape become two buckets."""
+    info = m.info_dict(m.muon_plan_describe(m.make_descs([(70000, 8, 16)], ["f32"], ["bf16"]), m.make_opts()))
+    assert bucket_keys(info) == [(8, 16, 65535, 0, "skinny"), (8, 16, 70000 - 65535, 0, "skinny")]
+    assert info["n_matrices"] == 70000
+
+
 def test_skinny_path_can_be_disabled(m):
     info = describe(m, workloads.WORKLOADS["fused_74x24x10240"], skinny_max_m=-1)
     assert info["buckets"][0]["path"] == "stream"
