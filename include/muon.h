@@ -121,7 +121,8 @@ typedef enum {
  *  MUON_PATH_SKINNY: m <= 32.  One pass forms the first Gram matrix (split over
  *    256-column chunks), the rounds run on m x m matrices (each round's P is a
  *    polynomial in A, so A' = P^2 A and X_k = P_{k-1}..P_0 X_0), and one pass
- *    applies X_k = Q X_0 and updates W.  Three launches per bucket.
+ *    applies X_k = Q X_0 and updates W.  Three launches per step cover every
+ *    skinny bucket of the plan.
  *  MUON_PATH_STREAM: every round forms A = X X^T, P = bA + cA^2 and
  *    X <- aX + PX with batched matrix-core products over the bucket. */
 typedef enum { MUON_PATH_SKINNY = 0, MUON_PATH_STREAM = 1 } muon_path_t;

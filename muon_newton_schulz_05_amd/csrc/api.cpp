@@ -50,6 +50,7 @@ struct muon_plan {
   muon::PtrEntry* pinned = nullptr;  // staging for the upload
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
+  muon::SkinnyBucket skinny_b0{};  // first skinny bucket (launch arguments); the table is in the workspace
   // graph of the streamed launches, keyed by ns_steps and stream
   hipGraphExec_t gexec = nullptr;
   int graph_ns = -1;
@@ -94,24 +95,23 @@ hipError_t timed(muon_plan_t plan, int cls, hipStream_t s, bool timing, F&& laun
   return e;
 }
 
-hipError_t enqueue_skinny(muon_plan_t plan, const muon::BucketPlan& bp, hipStream_t s, bool timing,
-                          const muon::DevScalars* first) {
+// All skinny buckets: one launch per stage, each walking the bucket table.
+hipError_t enqueue_skinny(muon_plan_t plan, hipStream_t s, bool timing, const muon::DevScalars* first) {
   const muon::Plan& p = plan->p;
   muon::SkinnyLaunch L{};
-  L.mats = at<muon::DevMat>(plan, bp.off_mats);
+  L.b0 = plan->skinny_b0;
+  L.buckets = at<muon::SkinnyBucket>(plan, p.off_skinny_params);
+  L.n_buckets = (int)p.skinny.size();
   L.ptrs = at<muon::PtrEntry>(plan, p.off_ptrs);
   L.sc = at<muon::DevScalars>(plan, p.off_scalars);
   if (first) {
     L.sv = *first;
     L.sc_out = at<muon::DevScalars>(plan, p.off_scalars);
   }
-  L.gram_parts = at<double>(plan, bp.off_gram);
-  L.qs = at<float>(plan, bp.off_qs);
   L.err = at<uint32_t>(plan, p.off_err);
-  L.m = (int)bp.m;
-  L.n = (int)bp.n;
-  L.n_chunks = bp.n_chunks;
-  L.count = (int)bp.slices.size();
+  L.items = p.skinny_items;
+  L.slices = p.skinny_slices;
+  L.m_max = p.skinny_m_max;
   L.bf16 = p.mode == MUON_MODE_BF16_MFMA;
   L.nesterov = p.nesterov;
   hipError_t e;
@@ -242,9 +242,14 @@ hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, 
 // steps), or null when a prologue kernel has already written them.
 hipError_t enqueue_buckets(muon_plan_t plan, int ns, hipStream_t s, bool timing,
                            const muon::DevScalars* first) {
+  if (!plan->p.skinny.empty()) {
+    hipError_t e = enqueue_skinny(plan, s, timing, first);
+    if (e != hipSuccess) return e;
+    first = nullptr;
+  }
   for (const muon::BucketPlan& bp : plan->p.buckets) {
-    hipError_t e = bp.path == MUON_PATH_SKINNY ? enqueue_skinny(plan, bp, s, timing, first)
-                                               : enqueue_stream(plan, bp, ns, s, timing, first);
+    if (bp.path == MUON_PATH_SKINNY) continue;
+    hipError_t e = enqueue_stream(plan, bp, ns, s, timing, first);
     if (e != hipSuccess) return e;
     first = nullptr;
   }
@@ -334,6 +339,29 @@ int muon_plan_create(const muon_param_desc_t* descs, int32_t n_params, const muo
       table.push_back(d);
     }
     e = hipMemcpy(plan->ws + bp.off_mats, table.data(), sizeof(muon::DevMat) * table.size(),
+                  hipMemcpyHostToDevice);
+  }
+  if (e == hipSuccess && !p.skinny.empty()) {
+    std::vector<muon::SkinnyBucket> sbs;
+    int item0 = 0, slice0 = 0;
+    for (int b : p.skinny) {
+      const muon::BucketPlan& bp = p.buckets[b];
+      muon::SkinnyBucket sb{};
+      sb.mats = at<muon::DevMat>(plan, bp.off_mats);
+      sb.gram_parts = at<double>(plan, bp.off_gram);
+      sb.qs = at<float>(plan, bp.off_qs);
+      sb.m = (int32_t)bp.m;
+      sb.n = (int32_t)bp.n;
+      sb.n_chunks = bp.n_chunks;
+      sb.count = (int32_t)bp.slices.size();
+      sb.item0 = item0;
+      sb.slice0 = slice0;
+      item0 += sb.count * sb.n_chunks;
+      slice0 += sb.count;
+      sbs.push_back(sb);
+    }
+    plan->skinny_b0 = sbs[0];
+    e = hipMemcpy(plan->ws + p.off_skinny_params, sbs.data(), sizeof(muon::SkinnyBucket) * sbs.size(),
                   hipMemcpyHostToDevice);
   }
   if (e == hipSuccess && !p.big.empty()) {

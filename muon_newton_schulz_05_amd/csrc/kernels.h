@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/muon.h"
 #include "layout.h"
 
 namespace muon {
@@ -15,15 +16,17 @@ hipError_t launch_prologue(DevScalars* dst, const DevScalars& v, hipStream_t s);
 // writes them to the plan's scalar block for the kernels after it (sc_out
 // non-null); every other launch reads them from the block (sc).
 struct SkinnyLaunch {
-  const DevMat* mats;     // bucket's slice table
+  SkinnyBucket b0;                // the first skinny bucket, by value
+  const SkinnyBucket* buckets;    // every skinny bucket of the plan (device table)
+  int n_buckets;
   const PtrEntry* ptrs;
   const DevScalars* sc;
   DevScalars sv;          // scalars by value (used when sc_out is set)
   DevScalars* sc_out;     // null, or the scalar block to fill
-  double* gram_parts;     // [count][n_chunks][m(m+1)/2]: upper triangles, packed by rows
-  float* qs;              // [count][32*32]: s * Q
   uint32_t* err;          // device error word
-  int m, n, n_chunks, count;
+  int items;              // (slice, chunk) items over all buckets
+  int slices;             // slices over all buckets
+  int m_max;              // largest m (sizes LDS; the polynomial's k steps)
   int bf16;               // 1: bf16 matrix-core mode, 0: fp32 mode
   int nesterov;           // the plan's Nesterov option (selects the apply kernel)
 };

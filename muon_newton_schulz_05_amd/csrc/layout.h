@@ -47,6 +47,19 @@ struct DevMat {
   int64_t slice_off;   // element offset of the slice inside its parameter
 };
 
+// One skinny bucket as the kernels see it.  The skinny stages run as one
+// launch each over all skinny buckets; a workgroup finds its bucket in a
+// device array of these by its first item or slice (the first bucket also
+// rides in the launch arguments).
+struct SkinnyBucket {
+  const DevMat* mats;  // slice table
+  double* gram_parts;  // [count][n_chunks][m(m+1)/2]: upper triangles, packed by rows
+  float* qs;           // [count][32*32]: s * Q
+  int32_t m, n, n_chunks, count;
+  int32_t item0;       // first (slice, chunk) item of the Gram and apply launches
+  int32_t slice0;      // first slice of the polynomial launch
+};
+
 // Large bf16 buckets run each product phase as one launch over all of
 // them: a tile table entry names the bucket, the slice and the output tile.
 struct BigTile {

@@ -194,7 +194,6 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
       bp.n_chunks = (int)((bp.n + kSkinnyChunk - 1) / kSkinnyChunk);
       bp.off_gram = ws.take(cnt * bp.n_chunks * (bp.m * (bp.m + 1) / 2) * sizeof(double));  // upper triangles
       bp.off_qs = ws.take(cnt * 1024 * sizeof(float));
-      p.launches_fixed += 3;  // momentum + Gram partials, polynomial, apply + update
     } else {
       bp.big = p.mode == MUON_MODE_BF16_MFMA && bp.m >= kBigMinM;
       const int64_t pad = bp.big ? kBigTile : kStreamPad;
@@ -219,6 +218,25 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
       if (!bp.big) p.launches_per_ns += 3;  // gram, poly, apply (the last apply also updates W)
     }
     bp.ws_bytes = ws.take(0) - bp.ws_begin;
+  }
+  // Skinny buckets share one launch per stage: momentum + Gram partials,
+  // polynomial, apply + update.
+  for (int b = 0; b < (int)p.buckets.size(); ++b) {
+    const BucketPlan& bp = p.buckets[b];
+    if (bp.path != MUON_PATH_SKINNY) continue;
+    p.skinny.push_back(b);
+    const int64_t items = (int64_t)p.skinny_items + (int64_t)bp.slices.size() * bp.n_chunks;
+    if (items >= (int64_t(1) << 31)) {
+      *err = "too many skinny column chunks in one plan";
+      return MUON_ERR_UNSUPPORTED;
+    }
+    p.skinny_items = (int)items;
+    p.skinny_slices += (int)bp.slices.size();
+    p.skinny_m_max = std::max(p.skinny_m_max, (int)bp.m);
+  }
+  if (!p.skinny.empty()) {
+    p.launches_fixed += 3;
+    p.off_skinny_params = ws.take(p.skinny.size() * sizeof(SkinnyBucket));
   }
   // Large buckets share one launch per product phase.
   for (int b = 0; b < (int)p.buckets.size(); ++b)

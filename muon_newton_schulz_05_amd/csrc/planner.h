@@ -71,6 +71,11 @@ struct Plan {
   // tile table per product phase (kBigGram, kBigPoly, kBigApply).
   std::vector<int> big;
   uint64_t off_big_params = 0;
+  // Skinny buckets: their indices, the device SkinnyBucket array and the
+  // totals of the grouped launches.
+  std::vector<int> skinny;
+  uint64_t off_skinny_params = 0;
+  int skinny_items = 0, skinny_slices = 0, skinny_m_max = 0;
   std::vector<BigTile> big_tab[3];
   uint64_t off_big_tab[3] = {0, 0, 0};
   uint64_t ws_total = 0;

@@ -15,13 +15,15 @@
 // recomputed every round, normalisation by the whole-matrix sum of squares);
 // only the order of the floating-point operations differs.
 //
-// Three kernels per bucket, all batched over the bucket's slices:
+// Three launches per step, each over every skinny bucket of the plan (a
+// workgroup finds its bucket in a table by its flat item or slice index):
 //   k_skinny_gram   momentum M <- beta M + G (stored), and per 256-column
-//                   chunk the sum of squares and the Gram partial of X0 (M,
-//                   or G + beta M with Nesterov momentum) on the matrix cores
-//                   (split-K over the long dimension);
-//   k_skinny_poly   per slice: s = 1/(||X0||_F + eps), A0 = s^2 sum of the
-//                   partials, the k-round recurrence in float64, Qs = s Q;
+//                   chunk the Gram partial of X0 (M, or G + beta M with
+//                   Nesterov momentum) on the matrix cores (split-K over the
+//                   long dimension);
+//   k_skinny_poly   per slice: the sum of the partials, s = 1/(||X0||_F +
+//                   eps) from its trace, A0 = s^2 (the sum), the k-round
+//                   recurrence in float64, Qs = s Q;
 //   k_skinny_apply  O = Qs X0 (matrix cores), W <- W - decay W - lr f O.
 // Chunks are fixed by n alone, so a slice's arithmetic does not depend on the
 // batch it is fused into.  Both memory passes stream 16-byte accesses in
@@ -145,6 +147,40 @@ __device__ __forceinline__ void zero_unfilled(float (*st)[kStride], int rows, in
   }
 }
 
+// The bucket of a flat (slice, chunk) item, or of a flat slice (by_slice):
+// the last bucket whose first item (slice) is at or before it, by binary
+// search over the table (uniform over the workgroup).
+__device__ __forceinline__ int bucket_of(const SkinnyLaunch& a, int idx, bool by_slice) {
+  int lo = 0, hi = a.n_buckets - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((by_slice ? a.buckets[mid].slice0 : a.buckets[mid].item0) <= idx) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+// The bucket itself (the first one from the launch arguments).
+__device__ __forceinline__ SkinnyBucket find_bucket(const SkinnyLaunch& a, int idx, bool by_slice) {
+  if (a.n_buckets == 1) return a.b0;
+  return a.buckets[bucket_of(a, idx, by_slice)];
+}
+// Slice and chunk of this workgroup in the Gram and apply launches: a plan
+// with one skinny shape launches a (chunk, slice) grid, several shapes one
+// flat grid over all items.
+__device__ __forceinline__ SkinnyBucket chunk_of(const SkinnyLaunch& a, int& z, int& chunk) {
+  if (gridDim.y > 1 || a.n_buckets == 1) {
+    z = blockIdx.y;
+    chunk = blockIdx.x;
+    return a.b0;
+  }
+  const int item = blockIdx.x;
+  const SkinnyBucket bk = find_bucket(a, item, false);
+  const int r = item - bk.item0;
+  z = r / bk.n_chunks;
+  chunk = r - z * bk.n_chunks;
+  return bk;
+}
+
 // ------------------------------------------------------------------ gram
 // LDS of k_skinny_gram.  bf16 mode: the m staged rows as two bf16 planes,
 // hi = bf16(x) and lo = bf16(x - hi), each with one more row of zeros (row
@@ -168,14 +204,15 @@ __device__ __forceinline__ int tri_index(int i, int j, int m) { return i * m - (
 // packed upper triangle in float64.  (The slice's sum of squares is the
 // trace of the summed partials.)  lds: skinny_gram_lds(m, BF16) bytes.
 template <bool BF16>
-__device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const DevScalars& S, int z, int chunk, float* lds) {
+__device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const SkinnyBucket& bk, const DevScalars& S, int z,
+                                           int chunk, float* lds) {
   float (*st)[kStride] = reinterpret_cast<float (*)[kStride]>(lds);         // fp32 mode: rows 0 .. m-1
   uint16_t (*H)[kBStride] = reinterpret_cast<uint16_t (*)[kBStride]>(lds);  // bf16 mode: hi plane
-  const DevMat d = a.mats[z];
+  const DevMat d = bk.mats[z];
   const PtrEntry pe = a.ptrs[d.param];
   const float beta = S.beta;
   const bool nesterov = S.nesterov != 0;
-  const int m = a.m, n = a.n;
+  const int m = bk.m, n = bk.n;
   uint16_t (*L)[kBStride] = H + m + 1;                                       // bf16 mode: lo plane
   const int tid = threadIdx.x, lane = tid & 63;
   // The wave index is uniform over the wave; saying so keeps branches on it scalar.
@@ -282,7 +319,7 @@ __device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const DevScala
   __syncthreads();
 
   const int nt = m * (m + 1) / 2;
-  double* const out = a.gram_parts + ((int64_t)z * a.n_chunks + chunk) * nt;
+  double* const out = bk.gram_parts + ((int64_t)z * bk.n_chunks + chunk) * nt;
   if constexpr (BF16) {
     // Wave w owns the 16 x 16 output tile (16 (w / 2), 16 (w % 2)) over all
     // columns of the chunk; the tile below the diagonal mirrors the one above
@@ -384,8 +421,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
   extern __shared__ __attribute__((aligned(16))) float gram_lds[];
   // The step's first kernel: scalars by value, written out for the later kernels.
   const DevScalars S = a.sc_out ? a.sv : *a.sc;
-  if (a.sc_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.sc_out = a.sv;
-  gram_chunk<BF16>(a, S, blockIdx.y, blockIdx.x, gram_lds);
+  if (a.sc_out && blockIdx.x == 0 && threadIdx.x == 0) *a.sc_out = a.sv;
+  int z, chunk;
+  const SkinnyBucket bk = chunk_of(a, z, chunk);
+  gram_chunk<BF16>(a, bk, S, z, chunk, gram_lds);
 }
 
 // ------------------------------------------------------------------ poly
@@ -407,18 +446,19 @@ constexpr int kPolyLds = (6 * 32 * kPolyLd + 1) * (int)sizeof(double);  // A[2],
 typedef double PolyRow[kPolyLd];
 
 template <int KQ>
-__device__ __forceinline__ void poly_slice(const SkinnyLaunch& a, const DevScalars& Sc, int z, double* lds) {
+__device__ __forceinline__ void poly_slice(const SkinnyLaunch& a, const SkinnyBucket& bk, const DevScalars& Sc, int z,
+                                           double* lds) {
   PolyRow* const base = reinterpret_cast<PolyRow*>(lds);
   PolyRow* const P = base + 128;
   PolyRow* const S = base + 160;
   double* sh_s = lds + 6 * 32 * kPolyLd;
   auto Abuf = [&](int i) { return base + 32 * i; };
   auto Qbuf = [&](int i) { return base + 64 + 32 * i; };
-  const int m = a.m, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = bk.m, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const double ca = Sc.a, cb = Sc.b, cc = Sc.c;
   const int ns = Sc.ns_steps;
   const int nt = m * (m + 1) / 2;
-  const int nch = a.n_chunks;
+  const int nch = bk.n_chunks;
 
   // Gram sums over the packed upper triangles: entry v = tid + 256 k of the
   // triangle (kPer = 3 covers m <= 32; KQ <= 5 means m <= 20, nt <= 210, one
@@ -426,7 +466,7 @@ __device__ __forceinline__ void poly_slice(const SkinnyLaunch& a, const DevScala
   // together, and each entry is summed in chunk order.  Loads past the end
   // read a valid address and are discarded, so the batch is one straight run.
   constexpr int kBatch = 20, kPer = KQ <= 5 ? 1 : (KQ <= 7 ? 2 : 3);
-  const double* parts = a.gram_parts + (int64_t)z * nch * nt;
+  const double* parts = bk.gram_parts + (int64_t)z * nch * nt;
   double sum[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) sum[k] = 0.0;
@@ -558,13 +598,15 @@ __device__ __forceinline__ void poly_slice(const SkinnyLaunch& a, const DevScala
     cur ^= 1;
   }
   PolyRow* const Qf = Qbuf(cur);
-  for (int e = tid; e < 1024; e += kThreads) a.qs[(int64_t)z * 1024 + e] = (float)(s * Qf[e >> 5][e & 31]);
+  for (int e = tid; e < 1024; e += kThreads) bk.qs[(int64_t)z * 1024 + e] = (float)(s * Qf[e >> 5][e & 31]);
 }
 
 template <int KQ>
 __global__ __launch_bounds__(kThreads) void k_skinny_poly(SkinnyLaunch a) {
   __shared__ double poly_lds[kPolyLds / sizeof(double)];
-  poly_slice<KQ>(a, *a.sc, blockIdx.x, poly_lds);
+  const int slice = blockIdx.x;
+  const SkinnyBucket bk = find_bucket(a, slice, true);
+  poly_slice<KQ>(a, bk, *a.sc, slice - bk.slice0, poly_lds);
 }
 
 // ------------------------------------------------------------------ apply
@@ -573,13 +615,13 @@ __global__ __launch_bounds__(kThreads) void k_skinny_poly(SkinnyLaunch a) {
 // rows (rows m .. 31 are zero, so the products read and write them without
 // per-lane guards); qs: 32 x 33 floats.
 template <bool BF16, bool NEST>
-__device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const DevScalars& S, int z, int chunk,
-                                            float* lds, float (*qs)[33]) {
+__device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const SkinnyBucket& bk, const DevScalars& S, int z,
+                                            int chunk, float* lds, float (*qs)[33]) {
   float (*st)[kStride] = reinterpret_cast<float (*)[kStride]>(lds);
-  const DevMat d = a.mats[z];
+  const DevMat d = bk.mats[z];
   const PtrEntry pe = a.ptrs[d.param];
   const float lr = S.lr, decay = S.decay, beta = S.beta;
-  const int m = a.m, n = a.n;
+  const int m = bk.m, n = bk.n;
   const float lrf = lr * update_factor(S.scale_mode, m, n, d.transposed);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
@@ -589,7 +631,7 @@ __device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const DevScal
   const char* const Gb = static_cast<const char*>(pe.g) + d.slice_off * (d.gdtype ? 2 : 4);
   char* const Wb = static_cast<char*>(pe.w) + d.slice_off * (d.pdtype ? 2 : 4);
 
-  for (int e = tid; e < 1024; e += kThreads) qs[e >> 5][e & 31] = a.qs[(int64_t)z * 1024 + e];
+  for (int e = tid; e < 1024; e += kThreads) qs[e >> 5][e & 31] = bk.qs[(int64_t)z * 1024 + e];
 
 
   // gmode: 0 = G is not read; 1 / 2 = Nesterov, X = G + beta M with G in
@@ -757,22 +799,30 @@ template <bool BF16, bool NEST>
 __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
   extern __shared__ __attribute__((aligned(16))) float apply_lds[];  // 32 staged rows
   __shared__ float qs[32][33];
-  apply_chunk<BF16, NEST>(a, *a.sc, blockIdx.y, blockIdx.x, apply_lds, qs);
+  int z, chunk;
+  const SkinnyBucket bk = chunk_of(a, z, chunk);
+  apply_chunk<BF16, NEST>(a, bk, *a.sc, z, chunk, apply_lds, qs);
 }
 
 }  // namespace
 
+// One skinny shape: a (chunk, slice) grid; several: one flat grid over all items.
+inline dim3 chunk_grid(const SkinnyLaunch& a) {
+  return a.n_buckets == 1 ? dim3(a.b0.n_chunks, a.b0.count) : dim3(a.items);
+}
+
 hipError_t launch_skinny_gram(const SkinnyLaunch& a, hipStream_t s) {
-  const dim3 grid(a.n_chunks, a.count);
-  const size_t lds = skinny_gram_lds(a.m, a.bf16 != 0);
+  const dim3 grid = chunk_grid(a);
+  const size_t lds = skinny_gram_lds(a.m_max, a.bf16 != 0);
   if (a.bf16) hipLaunchKernelGGL(k_skinny_gram<true>, grid, dim3(kThreads), lds, s, a);
   else hipLaunchKernelGGL(k_skinny_gram<false>, grid, dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_skinny_poly(const SkinnyLaunch& a, hipStream_t s) {
-  const dim3 grid(a.count), block(kThreads);
-  switch ((a.m + 3) >> 2) {
+  // Buckets with a smaller m run the largest m's k steps over zero padding.
+  const dim3 grid(a.slices), block(kThreads);
+  switch ((a.m_max + 3) >> 2) {
     case 1: hipLaunchKernelGGL(k_skinny_poly<1>, grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL(k_skinny_poly<2>, grid, block, 0, s, a); break;
     case 3: hipLaunchKernelGGL(k_skinny_poly<3>, grid, block, 0, s, a); break;
@@ -787,7 +837,7 @@ hipError_t launch_skinny_poly(const SkinnyLaunch& a, hipStream_t s) {
 }
 
 hipError_t launch_skinny_apply(const SkinnyLaunch& a, hipStream_t s) {
-  const dim3 grid(a.n_chunks, a.count);
+  const dim3 grid = chunk_grid(a);
   const size_t lds = (size_t)32 * kStride * sizeof(float);
   if (a.nesterov) {
     if (a.bf16) hipLaunchKernelGGL((k_skinny_apply<true, true>), grid, dim3(kThreads), lds, s, a);

@@ -111,14 +111,22 @@ def test_ns_steps(ns, mode):
 
 @pytest.mark.parametrize("mode", ["bf16", "fp32"])
 def test_fusion_is_bitexact(mode):
-    """A fused bucket gives bitwise the same W and M as one plan per matrix."""
-    shapes = [(24, 2500)] * 5 + [(96, 200)] * 3 + [(2500, 24)]
+    """A fused bucket gives bitwise the same W and M as one plan per matrix,
+    also when skinny shapes of different m share the grouped launches."""
+    shapes = [(24, 2500)] * 5 + [(96, 200)] * 3 + [(2500, 24), (32, 300), (7, 900), (16, 256)]
     params, grads, moms = make_inputs(shapes, "bf16", 21)
     w_f, m_f = gpu_step(params, grads, moms, mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
     for i in range(len(shapes)):
         w_1, m_1 = gpu_step([params[i]], [grads[i]], [moms[i]], mode=mode, lr=0.02, beta=0.95,
                             ns_steps=5, coeffs=Q)
         assert np.array_equal(w_f[i], w_1[0]) and np.array_equal(m_f[i], m_1[0]), f"slice {i}"
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+def test_several_skinny_shapes_share_the_launches(mode):
+    """Skinny shapes with different m and n (and ragged chunks) run in one
+    launch per stage, each finding its bucket in the table."""
+    check([(24, 3000), (16, 700), (7, 100), (32, 33), (3, 2, 500), (100, 8), (1, 300), (29, 257)], mode)
 
 
 def test_shape_group_larger_than_one_bucket():

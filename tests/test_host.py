@@ -140,6 +140,15 @@ def test_large_shape_groups_split_into_buckets_the_grid_can_index(m):
     assert info["n_matrices"] == 70000
 
 
+def test_skinny_buckets_share_three_launches(m):
+    """Every skinny shape of a plan runs in the same three launches."""
+    shapes = [(24, 10240), (16, 4096), (4, 32, 700), (100, 8), (24, 10240)]
+    d = m.make_descs(shapes, ["f32"] * 5, ["bf16"] * 5)
+    info = m.info_dict(m.muon_plan_describe(d, m.make_opts()))
+    assert [b["path"] for b in info["buckets"]] == ["skinny"] * 4
+    assert info["launches_fixed"] == 3 and info["launches_per_ns"] == 0
+
+
 def test_skinny_path_can_be_disabled(m):
     info = describe(m, workloads.WORKLOADS["fused_74x24x10240"], skinny_max_m=-1)
     assert info["buckets"][0]["path"] == "stream"
