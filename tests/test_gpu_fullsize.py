@@ -1,5 +1,6 @@
 """Parity at full workload sizes, in the launch configuration the benchmark
-times (one fused plan over every parameter of the workload, bf16 mode, eager).
+times (one fused plan over every parameter of the workload, eager), in bf16
+mode and in fp32 mode.
 
 The float64 oracle cannot run whole workloads in a test, so one slice of every
 large oriented shape was run through it by tests/golden/make_golden.py; the
@@ -10,7 +11,7 @@ start at zero and lr = 1, so the new weights are exactly -O.
 
 Checked per case:
   * the sampled entries: ||O_gpu[s] - O_ref[s]|| / ||O_ref[s]|| <= 2e-2
-    (the bf16-mode bar);
+    in bf16 mode, 1e-4 in fp32 mode;
   * ||O_gpu||_F of the sampled slice against the stored norm, same bar;
   * every other slice of the same oriented shape is finite and has a
     Frobenius norm within 5% of the sampled slice's (Gaussian matrices of one
@@ -44,8 +45,9 @@ def _oriented(shape):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
 @pytest.mark.parametrize("workload", ["moe_experts", "dense_h4096_l8", "large_share"])
-def test_full_workload_sampled(workload):
+def test_full_workload_sampled(workload, mode):
     import torch
 
     from muon_newton_schulz_05_amd import MuonPlan
@@ -54,7 +56,7 @@ def test_full_workload_sampled(workload):
     assert cases
     wl = workloads.WORKLOADS[workload]
     dev = torch.device("cuda:0")
-    print(f"full-size parity: {workload}", flush=True)
+    print(f"full-size parity: {workload} ({mode} mode)", flush=True)
 
     golden_params = {c["param"] for c in cases}
     gen = torch.Generator(device=dev)
@@ -68,7 +70,7 @@ def test_full_workload_sampled(workload):
         grads.append(g)
         params.append(torch.zeros(spec.shape, dtype=torch.float32, device=dev))
         moms.append(torch.zeros(spec.shape, dtype=torch.float32, device=dev))
-    plan = MuonPlan(params, grad_dtypes=[g.dtype for g in grads], mode="bf16")
+    plan = MuonPlan(params, grad_dtypes=[g.dtype for g in grads], mode=mode)
     plan.step(grads, moms, lr=1.0, beta=wl.beta, ns_steps=wl.ns_steps, coeffs=wl.coeffs)
     torch.cuda.synchronize()
     assert plan.status() == 0, "device error word set"
@@ -78,7 +80,7 @@ def test_full_workload_sampled(workload):
     def slice_of(t, s):
         return t[s] if t.dim() == 3 else t
 
-    tol = TOL["bf16"]
+    tol = TOL[mode]
     for c in cases:
         o_gpu = -slice_of(params[c["param"]], c["slice"])
         assert list(o_gpu.shape) == c["shape"]

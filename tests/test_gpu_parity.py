@@ -123,6 +123,22 @@ def test_fusion_is_bitexact(mode):
 
 
 @pytest.mark.parametrize("mode", ["bf16", "fp32"])
+def test_resume_from_host_copies_is_bitexact(mode):
+    """The plan holds no numeric state: one step, W and M copied to the host,
+    the plan destroyed and a new one created for two more steps gives bitwise
+    the W and M of three continuous steps (skinny, small streamed and large
+    shapes in one plan)."""
+    shapes = [(24, 3000), (96, 200), (600, 700), (2, 40, 520)]
+    params, grads, moms = make_inputs(shapes, "bf16", 53, w_std=0.02, m_std=1e-3)
+    kw = dict(mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    w3, m3 = gpu_step(params, grads, moms, steps=3, **kw)
+    w1, m1 = gpu_step(params, grads, moms, steps=1, **kw)
+    w3b, m3b = gpu_step(w1, grads, m1, steps=2, **kw)
+    for i in range(len(shapes)):
+        assert np.array_equal(w3[i], w3b[i]) and np.array_equal(m3[i], m3b[i]), f"parameter {i}"
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
 def test_several_skinny_shapes_share_the_launches(mode):
     """Skinny shapes with different m and n (and ragged chunks) run in one
     launch per stage, each finding its bucket in the table."""
@@ -162,7 +178,7 @@ def test_3d_equals_2d_slices(mode):
 
 
 @pytest.mark.parametrize("mode", ["bf16", "fp32"])
-@pytest.mark.parametrize("shape", [(24, 1800), (96, 230)])
+@pytest.mark.parametrize("shape", [(24, 1800), (96, 230), (600, 700)])
 def test_transposed_input_gives_transposed_output(shape, mode):
     params, grads, moms = make_inputs([shape], "bf16", 41)
     w_a, _ = gpu_step(params, grads, moms, mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
