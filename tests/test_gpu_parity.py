@@ -244,9 +244,11 @@ def test_graph_replay_matches_eager():
         m = [to_device(x, dev) for x in moms]
         plan = MuonPlan(p, grad_dtypes=[x.dtype for x in g], mode="bf16", use_graph=use_graph)
         s = torch.cuda.Stream()
+        # lr, beta and the coefficients change between replays and must take effect.
+        cubic = (1.5, -0.5, 0.0)
         with torch.cuda.stream(s):
-            for k, lr in enumerate([0.02, 0.01, 0.03, 0.03]):
-                plan.step(g, m, lr=lr, beta=0.9, ns_steps=5, coeffs=Q)
+            for lr, beta, co in [(0.02, 0.9, Q), (0.01, 0.95, Q), (0.03, 0.9, cubic), (0.03, 0.8, Q)]:
+                plan.step(g, m, lr=lr, beta=beta, ns_steps=5, coeffs=co)
                 s.synchronize()  # eager host work between replays
         torch.cuda.synchronize()
         outs.append([to_host(x) for x in p + m])
