@@ -20,8 +20,12 @@
 // This is an arithmetic arrangement of the same iteration, not a different
 // method.
 //
-// The kernel: 256 x 256 output tile per 256-thread workgroup, each of the
-// four waves owning 128 x 128 (4 x 4 blocks of v_mfma_f32_32x32x16_bf16).
+// The kernel: 256 x 256 output tile per 512-thread workgroup, eight waves
+// in a 2 x 4 grid each owning 128 x 64 (4 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16).  Two waves share each SIMD, so one wave's
+// matrix-core products run while the other waits on LDS or the barrier;
+// with one wave per SIMD (four waves of 128 x 128) the products ran about
+// 12% slower.
 // Operand k-slices of kBK elements go from HBM straight into LDS with
 // gfx950's global_load_lds_dwordx4, kNS stages deep with one barrier per
 // slice; lane l of a load lands at byte 16 l of its 1 KB destination, and
@@ -54,7 +58,9 @@ constexpr int kRB = 2 * kBK;                 // bytes of one tile row per slice
 constexpr int kCPR = kRB / 16;               // 16-byte chunks per row
 constexpr int kRPI = 1024 / kRB;             // rows filled by one 1 KB load instruction
 constexpr int kRW = 256 / kRB;               // rows per 256-byte span of the LDS banks
-constexpr int kLI = kBigTile / kRPI / 4;     // load instructions per wave, operand and slice
+constexpr int kWavesBig = 8;                 // waves per workgroup: 2 along i, 4 along j
+constexpr int kThreadsBig = 64 * kWavesBig;
+constexpr int kLI = kBigTile / kRPI / kWavesBig;  // load instructions per wave, operand and slice
 constexpr int kStage = 2 * kBigTile * kRB;   // bytes per stage (A and B tiles)
 constexpr int kStageBytes = 128 * 256 * 4;   // epilogue staging: 128 rows of 256 floats
 constexpr int kLds = kNS * kStage > kStageBytes ? kNS * kStage : kStageBytes;
@@ -102,8 +108,8 @@ __device__ __forceinline__ void st_f32x4(float* p, f32x4_t v) {
 }
 
 template <class Epi>
-__global__ __launch_bounds__(256) void k_gemm_big(BigArgs g) {
-  constexpr int FM = 4, FN = 4;    // 32x32 blocks per wave along i and j
+__global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
+  constexpr int FM = 4, FN = 2;    // 32x32 blocks per wave along i and j
   __shared__ __attribute__((aligned(1024))) char lds[kLds];
 
   int b = blockIdx.x;
@@ -118,7 +124,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(BigArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   // The wave index is uniform over the wave; saying so keeps branches on it scalar.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;  // 128 rows x 64 columns per wave
   const char* A = op.a + (int64_t)tm * kBigTile * op.lda * 2;
   const char* B = op.b + (int64_t)tn * kBigTile * op.ldb * 2;
   const int nk = (int)(op.K / kBK);
@@ -129,7 +135,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(BigArgs g) {
   uint32_t oa[kLI], ob[kLI];
 #pragma unroll
   for (int u = 0; u < kLI; ++u) {
-    const int row = kRPI * (wave + 4 * u) + lane / kCPR;
+    const int row = kRPI * (wave + kWavesBig * u) + lane / kCPR;
     const int chunk = (lane % kCPR) ^ swz(row);
     oa[u] = (uint32_t)(row * op.lda * 2 + chunk * 16);
     ob[u] = (uint32_t)(row * op.ldb * 2 + chunk * 16);
@@ -139,11 +145,11 @@ __global__ __launch_bounds__(256) void k_gemm_big(BigArgs g) {
 #pragma unroll
     for (int u = 0; u < kLI; ++u)
       __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(A + (int64_t)kt * kRB + oa[u]),
-                                       (void LDS_PTR*)(base + (wave + 4 * u) * 1024), 16, 0, 0);
+                                       (void LDS_PTR*)(base + (wave + kWavesBig * u) * 1024), 16, 0, 0);
 #pragma unroll
     for (int u = 0; u < kLI; ++u)
       __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(B + (int64_t)kt * kRB + ob[u]),
-                                       (void LDS_PTR*)(base + kBigTile * kRB + (wave + 4 * u) * 1024), 16, 0, 0);
+                                       (void LDS_PTR*)(base + kBigTile * kRB + (wave + kWavesBig * u) * 1024), 16, 0, 0);
   };
 
   f32x16_t acc[FM][FN];
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(BigArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
-  const int ra = wm * 128 + (lane & 31), rb = kBigTile + wn * 128 + (lane & 31);
+  const int ra = wm * 128 + (lane & 31), rb = kBigTile + wn * 64 + (lane & 31);
   // Multiply one resident slice.  The fragments of k-substep s + 1 are read
   // from LDS while the 16 products of substep s run (two fragment sets), and
   // the scheduling hints interleave one fragment read with every two
@@ -182,16 +188,19 @@ __global__ __launch_bounds__(256) void k_gemm_big(BigArgs g) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(af[s & 1][i], bfr[s & 1][j], acc[i][j]);
     }
-    // Order: the first substep's 8 reads, then (2 products, 1 read) x 8 per
-    // following substep, then the last substep's 16 products.
+    // Order: the first substep's 6 reads, then (1 product, 1 read) x 6 and
+    // 2 more products per following substep, then the last substep's 8
+    // products.
     __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
 #pragma unroll
-    for (int s = 0; s + 1 < kSub; ++s)
+    for (int s = 0; s + 1 < kSub; ++s) {
 #pragma unroll
       for (int q = 0; q < FM + FN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+    }
     __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
   };
 
@@ -227,14 +236,15 @@ __global__ __launch_bounds__(256) void k_gemm_big(BigArgs g) {
   float* stg = reinterpret_cast<float*>(lds);
   auto pass = [&](auto view_tag, int h) {
     constexpr int V = decltype(view_tag)::value;
-    constexpr int NB = Epi::kBatch;
+    constexpr int kPieces = 128 * 64 / kThreadsBig;  // 16-byte pieces of a half tile per thread
+    constexpr int NB = Epi::kBatch < kPieces ? Epi::kBatch : kPieces;
     const int row0 = (V == kViewRow ? tm : tn) * kBigTile + h * 128;
     const int col0 = (V == kViewRow ? tn : tm) * kBigTile;
     typename Epi::Aux aux[NB];
     auto load_batch = [&](int b0) {
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-        const int idx = (b0 + u) * 256 + tid;
+        const int idx = (b0 + u) * kThreadsBig + tid;
         aux[u] = Epi::load(cx, V, row0 + (idx >> 6), col0 + 4 * (idx & 63));
       }
     };
@@ -251,7 +261,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(BigArgs g) {
 #pragma unroll
               for (int u = 0; u < 4; ++u) {
                 const int r = i * 32 + 8 * q + 4 * (lane >> 5) + u;
-                const int col = wn * 128 + j * 32 + (lane & 31);
+                const int col = wn * 64 + j * 32 + (lane & 31);
                 const int ps = (col >> 2) ^ (((r >> 2) & 1) << 3);
                 stg[r * 256 + ps * 4 + (col & 3)] = pre * acc[i][j][4 * q + u];
               }
@@ -259,14 +269,14 @@ __global__ __launch_bounds__(256) void k_gemm_big(BigArgs g) {
     } else {
       // Staged [j][i] (four consecutive i per lane are one 16-byte slot);
       // slot s of row r sits at s ^ (r mod 16).
-      if (wn == h) {
+      if ((wn >> 1) == h) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int rc = j * 32 + (lane & 31);
+              const int rc = (wn & 1) * 64 + j * 32 + (lane & 31);
               const int ci = wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
               const int ps = (ci >> 2) ^ (rc & 15);
               f32x4_t v;
@@ -280,11 +290,11 @@ __global__ __launch_bounds__(256) void k_gemm_big(BigArgs g) {
     }
     __syncthreads();
 #pragma unroll
-    for (int b0 = 0; b0 < 32; b0 += NB) {
+    for (int b0 = 0; b0 < kPieces; b0 += NB) {
       if (b0 > 0) load_batch(b0);
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-        const int idx = (b0 + u) * 256 + tid;
+        const int idx = (b0 + u) * kThreadsBig + tid;
         const int r = idx >> 6, sl = idx & 63;
         const int ps = V == kViewRow ? sl ^ (((r >> 2) & 1) << 3) : sl ^ (r & 15);
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + r * 256 + ps * 4);
@@ -375,7 +385,7 @@ struct PolyPhase {
     f32x4_t a, dc;  // A (r, c .. c+3) and d (c .. c+3)
     float dr;       // d (r)
   };
-  static constexpr int kBatch = 8;
+  static constexpr int kBatch = 2;
   static __device__ Aux load(const Ctx& x, int, int r, int c) {
     return Aux{ld_f32x4(x.a32 + (int64_t)r * x.mp + c), ld_f32x4(x.dg + c),
                *reinterpret_cast<const MUON_GLOBAL float*>(as_global(x.dg + r))};
@@ -430,7 +440,7 @@ struct ApplyPhase {
   static __device__ float prescale(const Ctx&) { return 1.f; }
   static __device__ int views(const Ctx&, bool) { return kViewRow | kViewCol; }
   using Aux = u32x2_t;  // old X (r, c .. c+3), bf16
-  static constexpr int kBatch = 16;
+  static constexpr int kBatch = 8;
   static __device__ Aux load(const Ctx& x, int view, int r, int c) {
     const uint16_t* p = view == kViewRow ? x.x_old + (int64_t)r * x.np + c : x.xt_old + (int64_t)r * x.mp + c;
     return *reinterpret_cast<const MUON_GLOBAL u32x2_t*>(as_global(p));
@@ -482,7 +492,7 @@ struct FinalPhase {
     f32x4_t w;   // W (r, c .. c+3) as float32 (entries past the row end unused)
     u32x2_t xo;  // old X in this view, bf16
   };
-  static constexpr int kBatch = 8;
+  static constexpr int kBatch = 4;
   static __device__ Aux load(const Ctx& x, int, int r, int c) {
     Aux q{};
     if (r >= x.rows || c >= x.len) return q;
@@ -529,7 +539,7 @@ struct FinalPhase {
 }  // namespace
 
 hipError_t launch_big(BigKind kind, const BigArgs& a, hipStream_t s) {
-  const dim3 grid(a.t8), block(256);
+  const dim3 grid(a.t8), block(kThreadsBig);
   switch (kind) {
     case kBigGram: hipLaunchKernelGGL(k_gemm_big<GramPhase>, grid, block, 0, s, a); break;
     case kBigPoly: hipLaunchKernelGGL(k_gemm_big<PolyPhase>, grid, block, 0, s, a); break;
