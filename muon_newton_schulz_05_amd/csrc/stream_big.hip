@@ -52,7 +52,7 @@
 namespace muon {
 namespace {
 
-constexpr int kBK = 64;                      // bf16 elements of k per slice
+constexpr int kBK = kBigKStep;               // bf16 elements of k per slice
 constexpr int kNS = 2;                       // LDS stages (slices in flight: kNS - 1)
 constexpr int kRB = 2 * kBK;                 // bytes of one tile row per slice
 constexpr int kCPR = kRB / 16;               // 16-byte chunks per row
@@ -366,7 +366,7 @@ struct GramPhase {
 struct PolyPhase {
   static __device__ Operands operands(const BigArgs&, const BigBucket& bb, int z) {
     const char* e = reinterpret_cast<const char*>(bb.e16 + (int64_t)z * bb.mp * bb.mp);
-    return Operands{e, e, bb.mp, bb.mp, bb.mp};
+    return Operands{e, e, bb.mp, bb.mp, big_k_over_m(bb.m)};
   }
   struct Ctx {
     const float* a32;
@@ -413,7 +413,7 @@ struct PolyPhase {
 // Operands of R X: rows of R and rows of X^T (both contiguous along k = m).
 __device__ __forceinline__ Operands apply_operands(const BigArgs& g, const BigBucket& bb, int z) {
   return Operands{reinterpret_cast<const char*>(bb.r16 + (int64_t)z * bb.mp * bb.mp),
-                  bb.xt[g.src] + (int64_t)z * bb.np * bb.mp * 2, bb.mp, bb.mp, bb.mp};
+                  bb.xt[g.src] + (int64_t)z * bb.np * bb.mp * 2, bb.mp, bb.mp, big_k_over_m(bb.m)};
 }
 
 // X' = s (X + R X): X' [mp][np] from the row view, X'^T [np][mp] from the column view.
