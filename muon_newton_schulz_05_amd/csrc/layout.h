@@ -13,9 +13,10 @@ constexpr int kStreamPad = 128;       // streamed workspace dims are padded to t
 constexpr int kBigTile = 256;         // large bf16 buckets: product tile, and their padding
 constexpr int kBigMinM = 513;         // bf16 buckets with m >= this take the large-tile products
 constexpr int kBigKStep = 64;         // large-tile products: k elements per slice
-// Contraction length over m of the large-tile products: rows and columns of
-// the operands past m are zero, so the k loop stops at m rounded up to a slice.
-inline constexpr int64_t big_k_over_m(int64_t m) { return (m + kBigKStep - 1) / kBigKStep * kBigKStep; }
+// Contraction length of the large-tile products over a dimension of d (m, or
+// n for the Gram): operand entries past d are zero, so the k loop stops at d
+// rounded up to a slice.
+inline constexpr int64_t big_k_over_m(int64_t d) { return (d + kBigKStep - 1) / kBigKStep * kBigKStep; }
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;  // tile-table padding entry
 constexpr int kMomTile = 64;          // momentum kernel tile (oriented 64 x 64)
 

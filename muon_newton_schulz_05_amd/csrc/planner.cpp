@@ -276,7 +276,7 @@ std::vector<BigTile> big_table(const Plan& p, int phase) {
     const int tm = (int)(bp.mp / kBigTile);
     const int tn = phase == 2 ? (int)(bp.np / kBigTile) : tm;
     const bool sym = phase != 2;
-    const int64_t k = phase == 0 ? bp.np : big_k_over_m(bp.m);
+    const int64_t k = big_k_over_m(phase == 0 ? bp.n : bp.m);
     for (int z = 0; z < (int)bp.slices.size(); ++z)
       for (int i0 = 0; i0 < tm; i0 += kRows)
         for (int j0 = sym ? (i0 / kCols) * kCols : 0; j0 < tn; j0 += kCols) {

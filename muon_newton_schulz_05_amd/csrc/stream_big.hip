@@ -328,7 +328,7 @@ __device__ __forceinline__ f32x4_t ld_bf16x4(const uint16_t* p) {
 struct GramPhase {
   static __device__ Operands operands(const BigArgs& g, const BigBucket& bb, int z) {
     const char* x = bb.x[g.src] + (int64_t)z * bb.mp * bb.np * 2;
-    return Operands{x, x, bb.np, bb.np, bb.np};
+    return Operands{x, x, bb.np, bb.np, big_k_over_m(bb.n)};
   }
   struct Ctx {
     float* a32;
