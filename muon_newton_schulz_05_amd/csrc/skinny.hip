@@ -49,9 +49,6 @@ using B16 = std::integral_constant<bool, true>;
 
 __device__ __forceinline__ int rho(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-__device__ __forceinline__ f32x16_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
@@ -610,29 +607,165 @@ __global__ __launch_bounds__(kThreads) void k_skinny_poly(SkinnyLaunch a) {
 }
 
 // ------------------------------------------------------------------ apply
-// One 256-column chunk of slice z: O = Qs X (X = M, or G + beta M with
-// Nesterov momentum, NEST), W <- W - decay W - lr f O.  lds: 32 staged
-// rows (rows m .. 31 are zero, so the products read and write them without
-// per-lane guards); qs: 32 x 33 floats.
-template <bool BF16, bool NEST>
+// O = Qs X0 per 256-column chunk, then W <- W - decay W - lr f O.  Wave w
+// takes columns [64 w, 64 w + 64) of the chunk; lane l owns the 4-column
+// piece at 4 (l % 16) of them, rows R (l / 16) + q, q < R, of X0
+// (R = 2 ceil(m / 8), so 4 R >= m) and rows 16 t + 4 (l / 16) + r of O.  16x16x4 float32
+// products (lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and
+// receives rows 4 (l / 16) + r of column l % 16): product (t, u) of k step q
+// takes the contraction indices q, R + q, 2 R + q, 3 R + q, multiplies rows
+// 16 t .. + 15 of Qs by element u of every lane's X0 piece, so its column j
+// is column 4 j + u of the wave's 64, and the result lands in the lanes that
+// hold the matching W piece.  A lane's Qs operands are then R consecutive
+// entries of a row, read as 8-byte pieces.  Operands and accumulation are
+// float32 in both modes.  The Qs operands and X0 are loaded before W, so the
+// products start while the W loads are still in flight.  RM, the largest R
+// of the launch, sizes the registers; R itself depends only on the slice.
+// Two forms share this arithmetic, so a slice gives the same bits whichever
+// way it is stored: slices stored [m, n] with n % 4 == 0 read their pieces
+// straight from memory (no LDS, no barrier); the others are turned around in
+// LDS first.
+
+__device__ __forceinline__ int apply_rows(int m) { return 2 * ((m + 7) >> 3); }
+template <int RM>
+constexpr int apply_tiles() { return RM > 4 ? 2 : 1; }
+
+// Qs operands: Qs[16 t + l % 16][R (l / 16) + q] (zero outside m x m).
+template <int RM>
+__device__ __forceinline__ void load_qs_operands(const float* Q, int p, int g, int R, int nt,
+                                                 float (&qa)[apply_tiles<RM>()][RM]) {
+#pragma unroll
+  for (int t = 0; t < apply_tiles<RM>(); ++t)
+#pragma unroll
+    for (int h = 0; h < RM / 2; ++h) {
+      f32x2_t v = {0.f, 0.f};
+      if (t < nt && 2 * h < R) v = *reinterpret_cast<const MUON_GLOBAL f32x2_t*>(as_global(Q + (16 * t + p) * 32 + R * g + 2 * h));
+      qa[t][2 * h] = v.x;
+      qa[t][2 * h + 1] = v.y;
+    }
+}
+template <int RM>
+__device__ __forceinline__ void apply_products(const f32x4_t (&x)[RM], const float (&qa)[apply_tiles<RM>()][RM], int R,
+                                               int nt, f32x4_t (&acc)[apply_tiles<RM>()][4]) {
+#pragma unroll
+  for (int t = 0; t < apply_tiles<RM>(); ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < RM; ++q) {
+    if (q >= R) break;
+#pragma unroll
+    for (int t = 0; t < apply_tiles<RM>(); ++t) {
+      if (t >= nt) break;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[t][q], x[q][u], acc[t][u], 0, 0, 0);
+    }
+  }
+}
+// The update of one element: (W - decay W) - lr f O.
+__device__ __forceinline__ float w_update(float w, float decay, float lrf, float o) {
+  return fmaf(-lrf, o, fmaf(-decay, w, w));
+}
+
+// Direct form (slice stored [m, n], n % 4 == 0: every 4-column piece lies
+// whole inside or outside the slice and is 16-byte aligned).
+template <int RM, bool NEST>
+__device__ __forceinline__ void apply_direct(const SkinnyLaunch& a, const SkinnyBucket& bk, const DevScalars& S, int z,
+                                             int chunk) {
+  const DevMat d = bk.mats[z];
+  const PtrEntry pe = a.ptrs[d.param];
+  const int m = bk.m, n = bk.n;
+  const float lrf = S.lr * update_factor(S.scale_mode, m, n, 0), decay = S.decay, beta = S.beta;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p = lane & 15, g = lane >> 4;
+  const int c = chunk * kCols + wave * 64 + 4 * p;  // first column of this lane's piece
+  const bool in = c < n;
+  const int R = apply_rows(m), nt = (m + 15) >> 4;
+  constexpr int NT = apply_tiles<RM>();
+  const float* const Mb = pe.m + d.slice_off;
+  char* const Wb = static_cast<char*>(pe.w) + d.slice_off * (d.pdtype ? 2 : 4);
+
+  // Every load first: the Qs operands, the X0 pieces, then the W pieces of
+  // the lane's O rows.
+  float qa[NT][RM];
+  load_qs_operands<RM>(bk.qs + (int64_t)z * 1024, p, g, R, nt, qa);
+  f32x4_t x[RM];
+#pragma unroll
+  for (int q = 0; q < RM; ++q) {
+    const int row = R * g + q;
+    x[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (q < R && in && row < m) x[q] = *reinterpret_cast<const MUON_GLOBAL f32x4_t*>(as_global(Mb + (int64_t)row * n + c));
+  }
+  float gx[NEST ? RM : 1][4];
+  if constexpr (NEST) {
+    const char* const Gb = static_cast<const char*>(pe.g) + d.slice_off * (d.gdtype ? 2 : 4);
+#pragma unroll
+    for (int q = 0; q < RM; ++q) {
+      const int row = R * g + q;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) gx[q][u] = 0.f;
+      if (q < R && in && row < m) {
+        if (d.gdtype) ld_vec4<B16>(Gb, (int64_t)row * n + c, gx[q]);
+        else ld_vec4<F32>(Gb, (int64_t)row * n + c, gx[q]);
+      }
+    }
+  }
+  float w[NT][4][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * t + 4 * g + r;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[t][r][u] = 0.f;
+      if (t < nt && in && row < m) {
+        if (d.pdtype) ld_vec4<B16>(Wb, (int64_t)row * n + c, w[t][r]);
+        else ld_vec4<F32>(Wb, (int64_t)row * n + c, w[t][r]);
+      }
+    }
+  if constexpr (NEST) {
+#pragma unroll
+    for (int q = 0; q < RM; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[q][u] = fmaf(beta, x[q][u], gx[q][u]);
+  }
+  f32x4_t acc[NT][4];
+  apply_products<RM>(x, qa, R, nt, acc);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * t + 4 * g + r;
+      if (t >= nt || !in || row >= m) continue;
+      float o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[u] = w_update(w[t][r][u], decay, lrf, acc[t][u][r]);
+      if (d.pdtype) st_vec4<B16>(Wb, (int64_t)row * n + c, o);
+      else st_vec4<F32>(Wb, (int64_t)row * n + c, o);
+    }
+}
+
+// Staged form (any slice): the chunk's X0 is turned around in LDS, the
+// products read their pieces from there and write O back over them, and W is
+// updated in storage order.  lds: 32 staged rows (rows m .. 31 and columns
+// past the chunk are zero).
+template <int RM, bool NEST>
 __device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const SkinnyBucket& bk, const DevScalars& S, int z,
-                                            int chunk, float* lds, float (*qs)[33]) {
+                                            int chunk, float* lds) {
   float (*st)[kStride] = reinterpret_cast<float (*)[kStride]>(lds);
   const DevMat d = bk.mats[z];
   const PtrEntry pe = a.ptrs[d.param];
   const float lr = S.lr, decay = S.decay, beta = S.beta;
   const int m = bk.m, n = bk.n;
   const float lrf = lr * update_factor(S.scale_mode, m, n, d.transposed);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   ChunkMap cm;
   cm.init(m, n, chunk * kCols, min(kCols, n - chunk * kCols), d.transposed != 0, d.slice_off);
   const char* const Mb = reinterpret_cast<const char*>(pe.m + d.slice_off);
   const char* const Gb = static_cast<const char*>(pe.g) + d.slice_off * (d.gdtype ? 2 : 4);
   char* const Wb = static_cast<char*>(pe.w) + d.slice_off * (d.pdtype ? 2 : 4);
-
-  for (int e = tid; e < 1024; e += kThreads) qs[e >> 5][e & 31] = bk.qs[(int64_t)z * 1024 + e];
-
 
   // gmode: 0 = G is not read; 1 / 2 = Nesterov, X = G + beta M with G in
   // float32 / bf16.
@@ -688,61 +821,27 @@ __device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const SkinnyB
     }
     __syncthreads();
 
-    // Qs as the A operand; the contraction index runs over rows rho of X.
-    bf16x8_t qh[2], ql[2];
-    float qf[BF16 ? 1 : 16];
-    if constexpr (BF16) {
+    // The products on the wave's own 64 columns; O replaces X in place.
+    {
+      const int p = lane & 15, g = lane >> 4, c = wave * 64 + 4 * p;
+      const int R = apply_rows(m), nt = (m + 15) >> 4;
+      constexpr int NT = apply_tiles<RM>();
+      float qa[NT][RM];
+      load_qs_operands<RM>(bk.qs + (int64_t)z * 1024, p, g, R, nt, qa);
+      f32x4_t x[RM];
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int q = 0; q < RM; ++q)
+        x[q] = q < R ? *reinterpret_cast<const f32x4_t*>(&st[R * g + q][c]) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      f32x4_t acc[NT][4];
+      apply_products<RM>(x, qa, R, nt, acc);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float v = qs[col][rho(8 * g + t, h)];
-          const __bf16 hi = (__bf16)v;
-          qh[g][t] = hi;
-          ql[g][t] = (__bf16)(v - (float)hi);
-        }
-    } else {
+      for (int t = 0; t < NT; ++t) {
+        if (t >= nt) break;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) qf[r] = qs[col][rho(r, h)];
-    }
-    // O = Qs X per 32-column tile; X read in the column layout, O written
-    // back over it (each wave owns its tiles).
-#pragma unroll
-    for (int q = 0; q < kTilesPerWave; ++q) {
-      const int t = wave + kWaves * q;
-      if (t * 32 >= cm.cw) break;
-      const int j = t * 32 + col;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = st[rho(r, h)][j];  // rows >= m and columns >= cw are zero
-      f32x16_t o = {};
-      if constexpr (BF16) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          if (g == 1 && m <= 16) break;
-          uint32_t hw[4], lw2[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float x0 = x[8 * g + 2 * u], x1 = x[8 * g + 2 * u + 1];
-            hw[u] = pack_bf16x2(x0, x1);
-            lw2[u] = pack_bf16x2(x0 - bf16_lo(hw[u]), x1 - bf16_hi(hw[u]));
-          }
-          const bf16x8_t xh = as_bf16x8(hw[0], hw[1], hw[2], hw[3]);
-          const bf16x8_t xl = as_bf16x8(lw2[0], lw2[1], lw2[2], lw2[3]);
-          o = mfma_bf16(qh[g], xh, o);
-          o = mfma_bf16(qh[g], xl, o);
-          o = mfma_bf16(ql[g], xh, o);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (rho(r, 0) >= m) continue;
-          o = mfma_f32(qf[r], x[r], o);
-        }
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<f32x4_t*>(&st[16 * t + 4 * g + r][c]) =
+              f32x4_t{acc[t][0][r], acc[t][1][r], acc[t][2][r], acc[t][3][r]};
       }
-      // Rows >= m of O are zero (so are those rows of Qs).
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[rho(r, h)][j] = o[r];
     }
     __syncthreads();
 
@@ -758,13 +857,13 @@ __device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const SkinnyB
       if (!cm.tr && cnt == 4) {
         const f32x4_t o4 = *reinterpret_cast<const f32x4_t*>(&st[i0][j0]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = lw[k][u] - decay * lw[k][u] - lrf * o4[u];
+        for (int u = 0; u < 4; ++u) w[u] = w_update(lw[k][u], decay, lrf, o4[u]);
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           int i = 0, j = 0;
           if (u < cnt) cm.pos(i0, j0, u, i, j);
-          w[u] = lw[k][u] - decay * lw[k][u] - lrf * (u < cnt ? st[i][j] : 0.f);
+          w[u] = w_update(lw[k][u], decay, lrf, u < cnt ? st[i][j] : 0.f);
         }
       }
       if (cnt == 4 && cm.vec_ok) {
@@ -795,13 +894,14 @@ __device__ __forceinline__ void apply_chunk(const SkinnyLaunch& a, const SkinnyB
 
 // NEST is chosen at launch from the plan, so the plain kernel carries no
 // second code path.
-template <bool BF16, bool NEST>
+template <int RM, bool NEST>
 __global__ __launch_bounds__(kThreads) void k_skinny_apply(SkinnyLaunch a) {
   extern __shared__ __attribute__((aligned(16))) float apply_lds[];  // 32 staged rows
-  __shared__ float qs[32][33];
   int z, chunk;
   const SkinnyBucket bk = chunk_of(a, z, chunk);
-  apply_chunk<BF16, NEST>(a, bk, *a.sc, z, chunk, apply_lds, qs);
+  // The form depends only on the slice's own layout (uniform per workgroup).
+  if (!bk.mats[z].transposed && (bk.n & 3) == 0) apply_direct<RM, NEST>(a, bk, *a.sc, z, chunk);
+  else apply_chunk<RM, NEST>(a, bk, *a.sc, z, chunk, apply_lds);
 }
 
 }  // namespace
@@ -839,13 +939,20 @@ hipError_t launch_skinny_poly(const SkinnyLaunch& a, hipStream_t s) {
 hipError_t launch_skinny_apply(const SkinnyLaunch& a, hipStream_t s) {
   const dim3 grid = chunk_grid(a);
   const size_t lds = (size_t)32 * kStride * sizeof(float);
-  if (a.nesterov) {
-    if (a.bf16) hipLaunchKernelGGL((k_skinny_apply<true, true>), grid, dim3(kThreads), lds, s, a);
-    else hipLaunchKernelGGL((k_skinny_apply<false, true>), grid, dim3(kThreads), lds, s, a);
-  } else {
-    if (a.bf16) hipLaunchKernelGGL((k_skinny_apply<true, false>), grid, dim3(kThreads), lds, s, a);
-    else hipLaunchKernelGGL((k_skinny_apply<false, false>), grid, dim3(kThreads), lds, s, a);
+  // RM = 2 ceil(m_max / 8): registers for the largest slice of the launch.
+#define MUON_APPLY_CASE(RM)                                                                     \
+  case RM:                                                                                      \
+    if (a.nesterov) hipLaunchKernelGGL((k_skinny_apply<RM, true>), grid, dim3(kThreads), lds, s, a); \
+    else hipLaunchKernelGGL((k_skinny_apply<RM, false>), grid, dim3(kThreads), lds, s, a);           \
+    break;
+  switch (2 * ((a.m_max + 7) >> 3)) {
+    MUON_APPLY_CASE(2)
+    MUON_APPLY_CASE(4)
+    MUON_APPLY_CASE(6)
+    MUON_APPLY_CASE(8)
+    default: return hipErrorInvalidValue;
   }
+#undef MUON_APPLY_CASE
   return hipGetLastError();
 }
 
