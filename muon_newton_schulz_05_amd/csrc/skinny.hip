@@ -219,13 +219,65 @@ __device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const SkinnyBu
   char* const Mb = reinterpret_cast<char*>(pe.m + d.slice_off);
   const char* const Gb = static_cast<const char*>(pe.g) + d.slice_off * (d.gdtype ? 2 : 4);
 
+  // bf16 mode, slice stored [m, n] with n % 4 == 0: each wave stages only
+  // its own 64 columns (coalesced 16-byte pieces, four rows of 256 bytes per
+  // load instruction), so its products need no barrier.
+  const bool direct = BF16 && !cm.tr && cm.vec_ok;
+  auto pass_direct = [&](auto gtype) {
+    using GT = decltype(gtype);
+    const int cb = wave * 64;
+    float lm[kChunks][4], lg[kChunks][4];
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      const int v = lane + 64 * k, row = v >> 4, cc = cb + 4 * (v & 15);
+      if (row < m && cc < cm.cw) {
+        const int64_t off = (int64_t)row * n + cm.c0 + cc;
+        ld_vec4<F32>(Mb, off, lm[k]);
+        ld_vec4<GT>(Gb, off, lg[k]);
+      }
+    }
+    if (lane < 16) {
+      *reinterpret_cast<u32x2_t*>(&H[m][cb + 4 * lane]) = u32x2_t{0u, 0u};
+      *reinterpret_cast<u32x2_t*>(&L[m][cb + 4 * lane]) = u32x2_t{0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      const int v = lane + 64 * k, row = v >> 4, cc = cb + 4 * (v & 15);
+      if (row >= m) continue;
+      u32x2_t hv = {0u, 0u}, lv = {0u, 0u};
+      if (cc < cm.cw) {
+        float mn[4], xs[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          mn[u] = fmaf(beta, lm[k][u], lg[k][u]);
+          xs[u] = nesterov ? fmaf(beta, mn[u], lg[k][u]) : mn[u];
+        }
+        st_vec4<F32>(Mb, (int64_t)row * n + cm.c0 + cc, mn);
+        hv = u32x2_t{pack_bf16x2(xs[0], xs[1]), pack_bf16x2(xs[2], xs[3])};
+        lv = u32x2_t{pack_bf16x2(xs[0] - bf16_lo(hv.x), xs[1] - bf16_hi(hv.x)),
+                     pack_bf16x2(xs[2] - bf16_lo(hv.y), xs[3] - bf16_hi(hv.y))};
+      }
+      *reinterpret_cast<u32x2_t*>(&H[row][cc]) = hv;
+      *reinterpret_cast<u32x2_t*>(&L[row][cc]) = lv;
+    }
+    // This wave reads back only what it wrote; LDS accesses of one wave are
+    // performed in order, so no barrier is needed, only that the compiler
+    // keeps the order.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  if (direct) {
+    if (d.gdtype) pass_direct(B16{});
+    else pass_direct(F32{});
+  }
+
   // Columns >= cw of the staged rows, and the zero row m, read as zero.
   if constexpr (BF16) {
-    for (int e = tid; e < kCols; e += kThreads) {
+    if (!direct) for (int e = tid; e < kCols; e += kThreads) {
       H[m][e] = 0;
       L[m][e] = 0;
     }
-    if (cm.cw < kCols) {
+    if (!direct && cm.cw < kCols) {
       const int w = kCols - cm.cw;
       for (int e = tid; e < m * w; e += kThreads) {
         H[e / w][cm.cw + e % w] = 0;
@@ -311,66 +363,63 @@ __device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const SkinnyBu
       }
     }
   };
-  if (d.gdtype) pass(B16{});
-  else pass(F32{});
-  __syncthreads();
+  if (!direct) {
+    if (d.gdtype) pass(B16{});
+    else pass(F32{});
+    __syncthreads();
+  }
 
   const int nt = m * (m + 1) / 2;
   double* const out = bk.gram_parts + ((int64_t)z * bk.n_chunks + chunk) * nt;
   if constexpr (BF16) {
-    // Wave w owns the 16 x 16 output tile (16 (w / 2), 16 (w % 2)) over all
-    // columns of the chunk; the tile below the diagonal mirrors the one above
-    // it and is skipped.  16x16x32 bf16 products (lane l: row l % 16 of the
-    // tile's A rows and of its B rows, k = 8 (l / 16) .. + 7 of each 32-column
-    // step; result rows 4 (l / 16) + r, column l % 16) accumulate
-    // hi hi + hi lo + lo hi + lo lo, about float32 accuracy, in float32 per
-    // 32-column step and in float64 across steps, so the partial's rounding
-    // does not grow with the chunk width.
-    const int ti = 16 * (wave >> 1), tj = 16 * (wave & 1);
-    if (ti <= tj && tj < m) {
-      const int li = lane & 15, kg = lane >> 4;
-      const int ra = ti + li, rb = tj + li;
-      const bool diag = ti == tj;
-      double accd[4] = {0.0, 0.0, 0.0, 0.0};
-      // Operands of step t (columns 32 t .. 32 t + 31).  Rows >= m read the
-      // zero row m.  All eight steps run: columns >= cw are zero in the
-      // planes, so the steps past the chunk width add exact zeros.  Step
-      // t + 1's operands are read while step t's products run.
-      bf16x8_t ah[2], al[2], bh[2], bl[2];
-      const int rac = min(ra, m), rbc = min(rb, m);
-      auto rd = [](const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); };
-      auto fetch = [&](int t, int buf) {
-        const int c = t * 32 + kg * 8;
-        ah[buf] = rd(&H[rac][c]);
-        al[buf] = rd(&L[rac][c]);
-        if (!diag) {
-          bh[buf] = rd(&H[rbc][c]);
-          bl[buf] = rd(&L[rbc][c]);
-        } else {
-          bh[buf] = ah[buf];
-          bl[buf] = al[buf];
-        }
-      };
-      fetch(0, 0);
+    // Wave w multiplies its own 64 columns for the upper 16 x 16 tiles
+    // (0, 0), (0, 16) and (16, 16) (only the first for m <= 16).  16x16x32
+    // bf16 products (lane l: row l % 16 of the tile's A rows and of its B
+    // rows, k = 8 (l / 16) .. + 7 of each 32-column step; result rows
+    // 4 (l / 16) + r, column l % 16) accumulate hi hi + hi lo + lo hi + lo lo,
+    // about float32 accuracy, in float32 per 32-column step and in float64
+    // across steps; the four waves' sums are then added in wave order through
+    // LDS, so the partial's rounding does not grow with the chunk width.
+    // Rows >= m read the zero row m; columns >= cw are zero in the planes.
+    const int li = lane & 15, kg = lane >> 4;
+    const int ntile = m > 16 ? 3 : 1;
+    auto rd = [](const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); };
+    double accd[3][4];
 #pragma unroll
-      for (int t = 0; t < kCols / 32; ++t) {
-        const int cb = t & 1;
-        if (t + 1 < kCols / 32) fetch(t + 1, cb ^ 1);
-        const bf16x8_t xh = bh[cb], xl = bl[cb];
+    for (int tl = 0; tl < 3; ++tl) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accd[tl][r] = 0.0;
+      if (tl >= ntile) continue;
+      const int ti = tl == 2 ? 16 : 0, tj = tl == 0 ? 0 : 16;
+      const int rac = min(ti + li, m), rbc = min(tj + li, m);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int c = wave * 64 + t * 32 + kg * 8;
+        const bf16x8_t ah = rd(&H[rac][c]), al = rd(&L[rac][c]);
+        const bf16x8_t bh = ti == tj ? ah : rd(&H[rbc][c]), bl = ti == tj ? al : rd(&L[rbc][c]);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[cb], xh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[cb], xl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[cb], xh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[cb], xl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bl, acc, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accd[r] += (double)acc[r];
+        for (int r = 0; r < 4; ++r) accd[tl][r] += (double)acc[r];
       }
+    }
+    __syncthreads();  // every wave is done with the planes, which now hold the sums
+    double* const red = reinterpret_cast<double*>(lds);  // [4][nt]
+#pragma unroll
+    for (int tl = 0; tl < 3; ++tl) {
+      if (tl >= ntile) continue;
+      const int ti = tl == 2 ? 16 : 0, tj = tl == 0 ? 0 : 16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = ti + 4 * kg + r, j = tj + li;
-        if (i <= j && j < m) out[tri_index(i, j, m)] = accd[r];
+        if (i <= j && j < m) red[wave * nt + tri_index(i, j, m)] = accd[tl][r];
       }
     }
+    __syncthreads();
+    for (int e = tid; e < nt; e += kThreads) out[e] = ((red[e] + red[nt + e]) + red[2 * nt + e]) + red[3 * nt + e];
   } else {
     // fp32: lane l holds row l % 32 and both operands are the same rows; wave
     // w takes 32-column tiles w, w + 4, ...  Each tile is accumulated in
