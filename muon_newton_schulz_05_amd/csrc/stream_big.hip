@@ -5,9 +5,9 @@
 // matrix is recomputed each round; "MindSpore HyperParallel X 盘古,Muon优化器实现
 // 6倍性能跃升", 三大性能挑战: the round is matrix products and additions):
 //
-//   gram   A = s2 X X^T, stored three ways: float32 A, the diagonal d = diag(A)
-//          in float32, and E = A - diag(d) rounded to bf16 (the operand of
-//          the next product);
+//   gram   A = s2 X X^T, stored three ways: float32 A (tiles on and above
+//          the diagonal), the diagonal d = diag(A) in float32, and
+//          E = A - diag(d) rounded to bf16 (the operand of the next product);
 //   poly   R = (a - 1) I + b A + c A^2 with
 //            A^2 = E E + diag(d) A + A diag(d) - diag(d)^2,
 //          where only E E runs on the matrix cores; R is rounded to bf16;
@@ -41,9 +41,11 @@
 // (the 32 workgroups an XCD runs at once share 4 row and 8 column panels in
 // its L2), longest contraction first, with the work balanced over the XCDs.
 // Symmetric products (X X^T, E E) list only tiles on or above the diagonal;
-// an off-diagonal tile is also written to its mirror position.  The epilogue
-// turns the accumulators around in LDS and writes whole rows of 16-byte
-// pieces, in the tile's own orientation and, where needed, transposed.
+// the bf16 result of an off-diagonal tile is also written to its mirror
+// position.  The epilogue turns the accumulators around in LDS and writes
+// whole rows of 16-byte pieces.  Where a transposed copy holds the same values
+// (the mirror tiles, and X'^T next to X'), it is read out of LDS after the
+// row-view results, so the side inputs of the epilogue are read only once.
 #include <type_traits>
 
 #include "device_common.h"
@@ -230,8 +232,15 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   // written as whole rows of 16-byte pieces.  What an epilogue reads besides
   // the product (old X, W, A, the diagonal) is loaded kBatch pieces at a
   // time, the first batch before the staging so its latency is hidden.
+  // A phase whose transposed output holds the same values as its own
+  // (Epi::kMirror: the symmetric products, and X' next to X'^T) computes
+  // them once, in the row view: each thread puts its results back into the
+  // staging slots it read them from, and the transposed rows are then read
+  // out of LDS down the columns, 8 values (16 bytes of bf16) per thread.
+  // Such a phase reads its side inputs in one layout only.
   const auto cx = Epi::context(g, bb, z);
   const int views = Epi::views(cx, tm == tn);
+  const bool mirror = Epi::kMirror && (views & kViewCol);
   const float pre = Epi::prescale(cx);
   float* stg = reinterpret_cast<float*>(lds);
   auto pass = [&](auto view_tag, int h) {
@@ -297,17 +306,41 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
         const int idx = (b0 + u) * kThreadsBig + tid;
         const int r = idx >> 6, sl = idx & 63;
         const int ps = V == kViewRow ? sl ^ (((r >> 2) & 1) << 3) : sl ^ (r & 15);
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + r * 256 + ps * 4);
-        Epi::store(cx, V, row0 + r, col0 + 4 * sl, v, aux[u]);
+        f32x4_t* slot = reinterpret_cast<f32x4_t*>(stg + r * 256 + ps * 4);
+        const f32x4_t res = Epi::store(cx, V, row0 + r, col0 + 4 * sl, *slot, aux[u]);
+        if constexpr (V == kViewRow && Epi::kMirror) {
+          if (mirror) *slot = res;
+        }
       }
     }
     __syncthreads();
+    if constexpr (V == kViewRow && Epi::kMirror) {
+      if (!mirror) return;
+      // Transposed rows: wave w takes tile columns 32 w .. 32 w + 31 (one per
+      // lane of each half-wave) and, in step t, rows 16 t + 8 (l / 32) .. + 7
+      // of this half, written as one 16-byte piece of row (column) c.
+      const int c = 32 * wave + (lane & 31);
+#pragma unroll 2
+      for (int t = 0; t < 8; ++t) {
+        const int r0 = 16 * t + 8 * (lane >> 5);
+        float e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int r = r0 + u;
+          e[u] = stg[r * 256 + 4 * ((c >> 2) ^ (((r >> 2) & 1) << 3)) + (c & 3)];
+        }
+        Epi::store_t(cx, tn * kBigTile + c, tm * kBigTile + h * 128 + r0,
+                     u32x4_t{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                             pack_bf16x2(e[6], e[7])});
+      }
+      __syncthreads();
+    }
   };
   if (views & kViewRow) {
     pass(std::integral_constant<int, kViewRow>{}, 0);
     pass(std::integral_constant<int, kViewRow>{}, 1);
   }
-  if (views & kViewCol) {
+  if ((views & kViewCol) && !mirror) {
     pass(std::integral_constant<int, kViewCol>{}, 0);
     pass(std::integral_constant<int, kViewCol>{}, 1);
   }
@@ -343,10 +376,16 @@ struct GramPhase {
   }
   static __device__ float prescale(const Ctx& x) { return x.pre; }
   static __device__ int views(const Ctx&, bool diag) { return diag ? kViewRow : kViewRow | kViewCol; }
+  // The transposed tile of E comes from LDS; A itself is stored only for
+  // tiles on or above the diagonal, the only ones the polynomial reads.
+  static constexpr bool kMirror = true;
   struct Aux {};
   static constexpr int kBatch = 32;
   static __device__ Aux load(const Ctx&, int, int, int) { return Aux{}; }
-  static __device__ void store(const Ctx& x, int, int r, int c, f32x4_t v, Aux) {
+  static __device__ void store_t(const Ctx& x, int r, int c, u32x4_t v) {
+    *reinterpret_cast<MUON_GLOBAL u32x4_t*>(as_global(x.e16 + (int64_t)r * x.mp + c)) = v;
+  }
+  static __device__ f32x4_t store(const Ctx& x, int, int r, int c, f32x4_t v, Aux) {
     const int64_t idx = (int64_t)r * x.mp + c;
     st_f32x4(x.a32 + idx, v);
     const int d = r - c;  // position of the diagonal in this piece, if any
@@ -359,6 +398,7 @@ struct GramPhase {
       v.w = d == 3 ? 0.f : v.w;
     }
     st_bf16x4(x.e16 + idx, v);
+    return v;
   }
 };
 
@@ -381,6 +421,12 @@ struct PolyPhase {
   }
   static __device__ float prescale(const Ctx&) { return 1.f; }
   static __device__ int views(const Ctx&, bool diag) { return diag ? kViewRow : kViewRow | kViewCol; }
+  // R is symmetric: its transposed tile comes from LDS, so A is read only
+  // on and above the diagonal.
+  static constexpr bool kMirror = true;
+  static __device__ void store_t(const Ctx& x, int r, int c, u32x4_t v) {
+    *reinterpret_cast<MUON_GLOBAL u32x4_t*>(as_global(x.r16 + (int64_t)r * x.mp + c)) = v;
+  }
   struct Aux {
     f32x4_t a, dc;  // A (r, c .. c+3) and d (c .. c+3)
     float dr;       // d (r)
@@ -390,7 +436,7 @@ struct PolyPhase {
     return Aux{ld_f32x4(x.a32 + (int64_t)r * x.mp + c), ld_f32x4(x.dg + c),
                *reinterpret_cast<const MUON_GLOBAL float*>(as_global(x.dg + r))};
   }
-  static __device__ void store(const Ctx& x, int, int r, int c, f32x4_t ee, const Aux& q) {
+  static __device__ f32x4_t store(const Ctx& x, int, int r, int c, f32x4_t ee, const Aux& q) {
     const int64_t idx = (int64_t)r * x.mp + c;
     const f32x4_t a = q.a, dc = q.dc;
     const float dr = q.dr;
@@ -407,6 +453,7 @@ struct PolyPhase {
     MUON_POLY_ONE(w, 3)
 #undef MUON_POLY_ONE
     st_bf16x4(x.r16 + idx, o);
+    return o;
   }
 };
 
@@ -416,14 +463,14 @@ __device__ __forceinline__ Operands apply_operands(const BigArgs& g, const BigBu
                   bb.xt[g.src] + (int64_t)z * bb.np * bb.mp * 2, bb.mp, bb.mp, big_k_over_m(bb.m)};
 }
 
-// X' = s (X + R X): X' [mp][np] from the row view, X'^T [np][mp] from the column view.
+// X' = s (X + R X): X' [mp][np] from the row view, X'^T [np][mp] written
+// from LDS (the same values), so only the old X is read.
 struct ApplyPhase {
   static __device__ Operands operands(const BigArgs& g, const BigBucket& bb, int z) {
     return apply_operands(g, bb, z);
   }
   struct Ctx {
     const uint16_t* x_old;
-    const uint16_t* xt_old;
     uint16_t* x_new;
     uint16_t* xt_new;
     int64_t mp, np;
@@ -432,24 +479,26 @@ struct ApplyPhase {
   static __device__ Ctx context(const BigArgs& g, const BigBucket& bb, int z) {
     const int64_t o = (int64_t)z * bb.mp * bb.np * 2;
     return Ctx{reinterpret_cast<const uint16_t*>(bb.x[g.src] + o),
-               reinterpret_cast<const uint16_t*>(bb.xt[g.src] + o),
                reinterpret_cast<uint16_t*>(bb.x[g.src ^ 1] + o),
                reinterpret_cast<uint16_t*>(bb.xt[g.src ^ 1] + o), bb.mp, bb.np,
                g.first ? bb.scale[2 * z] : 1.f};
   }
   static __device__ float prescale(const Ctx&) { return 1.f; }
   static __device__ int views(const Ctx&, bool) { return kViewRow | kViewCol; }
+  static constexpr bool kMirror = true;
   using Aux = u32x2_t;  // old X (r, c .. c+3), bf16
   static constexpr int kBatch = 8;
-  static __device__ Aux load(const Ctx& x, int view, int r, int c) {
-    const uint16_t* p = view == kViewRow ? x.x_old + (int64_t)r * x.np + c : x.xt_old + (int64_t)r * x.mp + c;
-    return *reinterpret_cast<const MUON_GLOBAL u32x2_t*>(as_global(p));
+  static __device__ Aux load(const Ctx& x, int, int r, int c) {
+    return *reinterpret_cast<const MUON_GLOBAL u32x2_t*>(as_global(x.x_old + (int64_t)r * x.np + c));
   }
-  static __device__ void store(const Ctx& x, int view, int r, int c, f32x4_t v, Aux o) {
-    const int64_t idx = view == kViewRow ? (int64_t)r * x.np + c : (int64_t)r * x.mp + c;
+  static __device__ f32x4_t store(const Ctx& x, int, int r, int c, f32x4_t v, Aux o) {
     const f32x4_t y{x.pre * (v.x + bf16_lo(o.x)), x.pre * (v.y + bf16_hi(o.x)), x.pre * (v.z + bf16_lo(o.y)),
                     x.pre * (v.w + bf16_hi(o.y))};
-    st_bf16x4((view == kViewRow ? x.x_new : x.xt_new) + idx, y);
+    st_bf16x4(x.x_new + (int64_t)r * x.np + c, y);
+    return y;
+  }
+  static __device__ void store_t(const Ctx& x, int r, int c, u32x4_t v) {
+    *reinterpret_cast<MUON_GLOBAL u32x4_t*>(as_global(x.xt_new + (int64_t)r * x.mp + c)) = v;
   }
 };
 
@@ -488,6 +537,8 @@ struct FinalPhase {
   }
   static __device__ float prescale(const Ctx&) { return 1.f; }
   static __device__ int views(const Ctx& x, bool) { return x.view; }
+  static constexpr bool kMirror = false;
+  static __device__ void store_t(const Ctx&, int, int, u32x4_t) {}  // no transposed copy
   struct Aux {
     f32x4_t w;   // W (r, c .. c+3) as float32 (entries past the row end unused)
     u32x2_t xo;  // old X in this view, bf16
@@ -513,8 +564,8 @@ struct FinalPhase {
     }
     return q;
   }
-  static __device__ void store(const Ctx& x, int, int r, int c, f32x4_t v, const Aux& q) {
-    if (r >= x.rows || c >= x.len) return;
+  static __device__ f32x4_t store(const Ctx& x, int, int r, int c, f32x4_t v, const Aux& q) {
+    if (r >= x.rows || c >= x.len) return v;
     const f32x4_t n{q.w.x - x.decay * q.w.x - x.k * (v.x + bf16_lo(q.xo.x)),
                     q.w.y - x.decay * q.w.y - x.k * (v.y + bf16_hi(q.xo.x)),
                     q.w.z - x.decay * q.w.z - x.k * (v.z + bf16_lo(q.xo.y)),
@@ -527,12 +578,13 @@ struct FinalPhase {
       } else {
         *reinterpret_cast<MUON_GLOBAL f32x4_t*>(as_global(x.w) + 4 * idx) = n;
       }
-      return;
+      return n;
     }
     store_from_f32(x.w, idx, x.pdtype, n.x);
     if (c + 1 < x.len) store_from_f32(x.w, idx + 1, x.pdtype, n.y);
     if (c + 2 < x.len) store_from_f32(x.w, idx + 2, x.pdtype, n.z);
     if (c + 3 < x.len) store_from_f32(x.w, idx + 3, x.pdtype, n.w);
+    return n;
   }
 };
 
