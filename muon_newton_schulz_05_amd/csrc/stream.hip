@@ -29,6 +29,15 @@ __global__ void k_prologue(DevScalars* dst, DevScalars v) {
 }
 
 // ------------------------------------------------------------------ momentum
+// Four consecutive workspace entries of X (float32, or bf16 rounded to
+// nearest even) in one store.
+__device__ __forceinline__ void store_x4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<MUON_GLOBAL f32x4_t*>(as_global(p)) = f32x4_t{a, b, c, d};
+}
+__device__ __forceinline__ void store_x4(uint16_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<MUON_GLOBAL u32x2_t*>(as_global(p)) = u32x2_t{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+
 template <typename XT>
 __global__ __launch_bounds__(256) void k_momentum(MomentumLaunch a) {
   __shared__ float tile[kMomTile][kMomTile + 1];
@@ -45,38 +54,80 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumLaunch a) {
   const int tid = threadIdx.x;
 
   // Load along the stored rows (coalesced), keep X0 in LDS in oriented order:
-  // M_new, or G + beta M_new with Nesterov momentum.
-  for (int q = 0; q < 16; ++q) {
-    const int fast = tid & 63, slow = (tid >> 6) + 4 * q;
-    const int ii = d.transposed ? fast : slow;
-    const int jj = d.transposed ? slow : fast;
-    const int64_t i = i0 + ii, j = j0 + jj;
-    float v = 0.f;
-    if (i < a.m && j < a.n) {
-      const int64_t idx = d.slice_off + (d.transposed ? j * a.m + i : i * a.n + j);
-      const float g = load_as_f32(pe.g, idx, d.gdtype);
-      const float mn = fmaf(beta, pe.m[idx], g);
-      pe.m[idx] = mn;
-      v = nesterov ? fmaf(beta, mn, g) : mn;
+  // M_new, or G + beta M_new with Nesterov momentum.  A whole tile whose
+  // stored rows start on 4-element boundaries moves 4 consecutive elements
+  // per access (16 bytes of M); any other tile goes element by element.
+  const int64_t len = d.transposed ? a.m : a.n;  // stored row length
+  const bool whole = i0 + kMomTile <= a.m && j0 + kMomTile <= a.n && (len & 3) == 0 && (d.slice_off & 3) == 0;
+  if (whole) {
+    const int64_t s0 = d.transposed ? j0 : i0, c0 = d.transposed ? i0 : j0;  // stored tile origin
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int sr = (tid >> 4) + 16 * q, sc = 4 * (tid & 15);
+      const int64_t idx = d.slice_off + (s0 + sr) * len + c0 + sc;
+      f32x4_t g;
+      if (d.gdtype == 1) {
+        const u32x2_t w = *reinterpret_cast<const MUON_GLOBAL u32x2_t*>(as_global(static_cast<const uint16_t*>(pe.g) + idx));
+        g = f32x4_t{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+      } else {
+        g = *reinterpret_cast<const MUON_GLOBAL f32x4_t*>(as_global(static_cast<const float*>(pe.g) + idx));
+      }
+      MUON_GLOBAL f32x4_t* mp4 = reinterpret_cast<MUON_GLOBAL f32x4_t*>(as_global(pe.m + idx));
+      const f32x4_t m0 = *mp4;
+      const f32x4_t mn{fmaf(beta, m0.x, g.x), fmaf(beta, m0.y, g.y), fmaf(beta, m0.z, g.z), fmaf(beta, m0.w, g.w)};
+      *mp4 = mn;
+      const f32x4_t v = nesterov ? f32x4_t{fmaf(beta, mn.x, g.x), fmaf(beta, mn.y, g.y), fmaf(beta, mn.z, g.z),
+                                           fmaf(beta, mn.w, g.w)}
+                                 : mn;
+      if (d.transposed) {
+        tile[sc + 0][sr] = v.x;
+        tile[sc + 1][sr] = v.y;
+        tile[sc + 2][sr] = v.z;
+        tile[sc + 3][sr] = v.w;
+      } else {
+        tile[sr][sc + 0] = v.x;
+        tile[sr][sc + 1] = v.y;
+        tile[sr][sc + 2] = v.z;
+        tile[sr][sc + 3] = v.w;
+      }
     }
-    tile[ii][jj] = v;
+  } else {
+    for (int q = 0; q < 16; ++q) {
+      const int fast = tid & 63, slow = (tid >> 6) + 4 * q;
+      const int ii = d.transposed ? fast : slow;
+      const int jj = d.transposed ? slow : fast;
+      const int64_t i = i0 + ii, j = j0 + jj;
+      float v = 0.f;
+      if (i < a.m && j < a.n) {
+        const int64_t idx = d.slice_off + (d.transposed ? j * a.m + i : i * a.n + j);
+        const float g = load_as_f32(pe.g, idx, d.gdtype);
+        const float mn = fmaf(beta, pe.m[idx], g);
+        pe.m[idx] = mn;
+        v = nesterov ? fmaf(beta, mn, g) : mn;
+      }
+      tile[ii][jj] = v;
+    }
   }
   __syncthreads();
 
-  XT* x = static_cast<XT*>(a.x) + (int64_t)z * a.mp * a.np;
-  XT* xt = static_cast<XT*>(a.xt) + (int64_t)z * a.mp * a.np;
+  // Sum of squares in a fixed order over the oriented tile (entries outside
+  // the slice are zero).
   float sq = 0.f;
   for (int q = 0; q < 16; ++q) {
     const int e = tid + 256 * q;
-    const int ii = e >> 6, jj = e & 63;
-    const float v = tile[ii][jj];
+    const float v = tile[e >> 6][e & 63];
     sq = fmaf(v, v, sq);
-    if (i0 + ii < a.m && j0 + jj < a.n) x[(i0 + ii) * a.np + j0 + jj] = cvt_x<XT>(v);
   }
-  for (int q = 0; q < 16; ++q) {
-    const int e = tid + 256 * q;
-    const int jj = e >> 6, ii = e & 63;
-    if (i0 + ii < a.m && j0 + jj < a.n) xt[(j0 + jj) * a.mp + i0 + ii] = cvt_x<XT>(tile[ii][jj]);
+  // X and X^T in 4-element pieces.  The workspace is padded to whole tiles
+  // and entries outside the slice are zero in the tile, so whole pieces stay
+  // inside the buffers and leave the padding zero.
+  XT* x = static_cast<XT*>(a.x) + (int64_t)z * a.mp * a.np;
+  XT* xt = static_cast<XT*>(a.xt) + (int64_t)z * a.mp * a.np;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = (tid >> 4) + 16 * q, c = 4 * (tid & 15);
+    store_x4(x + (i0 + r) * a.np + j0 + c, tile[r][c], tile[r][c + 1], tile[r][c + 2], tile[r][c + 3]);
+    store_x4(xt + (j0 + r) * a.mp + i0 + c, tile[c][r], tile[c + 1][r], tile[c + 2][r], tile[c + 3][r]);
   }
   sq = wave_sum(sq);
   if ((tid & 63) == 0) wsum[tid >> 6] = sq;
