@@ -243,10 +243,17 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   const bool mirror = Epi::kMirror && (views & kViewCol);
   const float pre = Epi::prescale(cx);
   float* stg = reinterpret_cast<float*>(lds);
-  auto pass = [&](auto view_tag, int h) {
+  auto pass = [&](auto view_tag, auto half_tag) {
     constexpr int V = decltype(view_tag)::value;
+    constexpr int h = decltype(half_tag)::value;
     constexpr int kPieces = 128 * 64 / kThreadsBig;  // 16-byte pieces of a half tile per thread
-    constexpr int NB = Epi::kBatch < kPieces ? Epi::kBatch : kPieces;
+    // In the second half every wave has staged its accumulators before the
+    // side inputs are loaded, so their registers can hold a larger batch
+    // (Epi::kBatchLast) of those loads; the first half loads its first batch
+    // ahead of the staging, to hide its latency.
+    constexpr bool late = h == 1 && Epi::kBatchLast > Epi::kBatch;
+    constexpr int kB = late ? Epi::kBatchLast : Epi::kBatch;
+    constexpr int NB = kB < kPieces ? kB : kPieces;
     const int row0 = (V == kViewRow ? tm : tn) * kBigTile + h * 128;
     const int col0 = (V == kViewRow ? tn : tm) * kBigTile;
     typename Epi::Aux aux[NB];
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
         aux[u] = Epi::load(cx, V, row0 + (idx >> 6), col0 + 4 * (idx & 63));
       }
     };
-    load_batch(0);
+    if constexpr (!late) load_batch(0);
     if constexpr (V == kViewRow) {
       // Staged [i][j]; 16-byte slot s of row r sits at s ^ (8 ((r / 4) mod 2)).
       if (wm == h) {
@@ -298,6 +305,7 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
       }
     }
     __syncthreads();
+    if constexpr (late) load_batch(0);
 #pragma unroll
     for (int b0 = 0; b0 < kPieces; b0 += NB) {
       if (b0 > 0) load_batch(b0);
@@ -336,13 +344,15 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
       __syncthreads();
     }
   };
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
   if (views & kViewRow) {
-    pass(std::integral_constant<int, kViewRow>{}, 0);
-    pass(std::integral_constant<int, kViewRow>{}, 1);
+    pass(std::integral_constant<int, kViewRow>{}, H0{});
+    pass(std::integral_constant<int, kViewRow>{}, H1{});
   }
   if ((views & kViewCol) && !mirror) {
-    pass(std::integral_constant<int, kViewCol>{}, 0);
-    pass(std::integral_constant<int, kViewCol>{}, 1);
+    pass(std::integral_constant<int, kViewCol>{}, H0{});
+    pass(std::integral_constant<int, kViewCol>{}, H1{});
   }
 }
 
@@ -380,7 +390,7 @@ struct GramPhase {
   // tiles on or above the diagonal, the only ones the polynomial reads.
   static constexpr bool kMirror = true;
   struct Aux {};
-  static constexpr int kBatch = 32;
+  static constexpr int kBatch = 32, kBatchLast = 0;
   static __device__ Aux load(const Ctx&, int, int, int) { return Aux{}; }
   static __device__ void store_t(const Ctx& x, int r, int c, u32x4_t v) {
     *reinterpret_cast<MUON_GLOBAL u32x4_t*>(as_global(x.e16 + (int64_t)r * x.mp + c)) = v;
@@ -431,7 +441,7 @@ struct PolyPhase {
     f32x4_t a, dc;  // A (r, c .. c+3) and d (c .. c+3)
     float dr;       // d (r)
   };
-  static constexpr int kBatch = 2;
+  static constexpr int kBatch = 4, kBatchLast = 16;
   static __device__ Aux load(const Ctx& x, int, int r, int c) {
     return Aux{ld_f32x4(x.a32 + (int64_t)r * x.mp + c), ld_f32x4(x.dg + c),
                *reinterpret_cast<const MUON_GLOBAL float*>(as_global(x.dg + r))};
@@ -487,7 +497,7 @@ struct ApplyPhase {
   static __device__ int views(const Ctx&, bool) { return kViewRow | kViewCol; }
   static constexpr bool kMirror = true;
   using Aux = u32x2_t;  // old X (r, c .. c+3), bf16
-  static constexpr int kBatch = 8;
+  static constexpr int kBatch = 8, kBatchLast = 0;
   static __device__ Aux load(const Ctx& x, int, int r, int c) {
     return *reinterpret_cast<const MUON_GLOBAL u32x2_t*>(as_global(x.x_old + (int64_t)r * x.np + c));
   }
@@ -543,7 +553,7 @@ struct FinalPhase {
     f32x4_t w;   // W (r, c .. c+3) as float32 (entries past the row end unused)
     u32x2_t xo;  // old X in this view, bf16
   };
-  static constexpr int kBatch = 4;
+  static constexpr int kBatch = 4, kBatchLast = 0;
   static __device__ Aux load(const Ctx& x, int, int r, int c) {
     Aux q{};
     if (r >= x.rows || c >= x.len) return q;
