@@ -155,10 +155,12 @@ __global__ __launch_bounds__(256) void k_norm(NormLaunch a) {
 }
 
 // ------------------------------------------------------------------ GEMM core
-// 128 x 128 output tile per 256-thread workgroup; 4 waves in a 2 x 2 grid,
-// each computing 64 x 64 with 32x32 matrix-core instructions.  k-slices of
-// 64 bytes per row are staged through LDS, double buffered.
-constexpr int kBM = 128, kBN = 128;
+// BT x BT output tile per 256-thread workgroup (BT = 128, or 64 where a
+// launch would have fewer 128-tiles than the chip has CUs); 4 waves in a
+// 2 x 2 grid, each computing BT/2 x BT/2 with 32x32 matrix-core instructions.
+// k-slices of 64 bytes per row are staged through LDS, double buffered.
+// Every output entry takes its k steps in the same order whatever BT is, so
+// the tile size does not change a single bit of the result.
 constexpr int kRowBytes = 64;       // bytes of k per operand row per stage
 constexpr int kLdsRow = kRowBytes + 16;
 
@@ -169,7 +171,7 @@ struct GemmCore {
   int64_t lda, ldb;          // row strides in elements
   int64_t sa, sb;            // matrix strides in elements
   int64_t K;                 // contraction length (multiple of the k-slice)
-  int tiles_n;               // output tiles along j
+  int tiles_n;               // output tiles along j (set by run_gemm)
 };
 
 __device__ __forceinline__ f32x16_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -179,27 +181,30 @@ __device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <typename T, class Epi>
+template <typename T, class Epi, int BT>
 __global__ __launch_bounds__(256) void k_gemm(GemmCore c, Epi epi) {
   constexpr int BK = kRowBytes / (int)sizeof(T);
-  __shared__ __attribute__((aligned(16))) char lds[2][2][kBM * kLdsRow];
+  constexpr int X = BT / 64;  // 32x32 blocks per wave along i and along j
+  constexpr int H = BT / 64;  // 16-byte loads per thread, operand and slice
+  constexpr int WT = BT / 2;  // rows (columns) per wave
+  __shared__ __attribute__((aligned(16))) char lds[2][2][BT * kLdsRow];
   const int z = blockIdx.z;
   const int tm = blockIdx.x / c.tiles_n, tn = blockIdx.x % c.tiles_n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const char* A = c.a + ((int64_t)z * c.sa + (int64_t)tm * kBM * c.lda) * (int64_t)sizeof(T);
-  const char* A2 = c.a2 ? c.a2 + ((int64_t)z * c.sa + (int64_t)tm * kBM * c.lda) * (int64_t)sizeof(T)
+  const char* A = c.a + ((int64_t)z * c.sa + (int64_t)tm * BT * c.lda) * (int64_t)sizeof(T);
+  const char* A2 = c.a2 ? c.a2 + ((int64_t)z * c.sa + (int64_t)tm * BT * c.lda) * (int64_t)sizeof(T)
                         : nullptr;
-  const char* B = c.b + ((int64_t)z * c.sb + (int64_t)tn * kBN * c.ldb) * (int64_t)sizeof(T);
+  const char* B = c.b + ((int64_t)z * c.sb + (int64_t)tn * BT * c.ldb) * (int64_t)sizeof(T);
 
-  int row[2], c16[2];
+  int row[H], c16[H];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < H; ++h) {
     const int idx = tid + 256 * h;
     row[h] = idx >> 2;
     c16[h] = idx & 3;
   }
-  u32x4_t ra[2], rb[2];
+  u32x4_t ra[H], rb[H];
   const int nk = (int)(c.K / BK);
   const int total = A2 ? 2 * nk : nk;
 
@@ -207,24 +212,24 @@ __global__ __launch_bounds__(256) void k_gemm(GemmCore c, Epi epi) {
     const int kt = it % nk;
     const char* Ab = it >= nk ? A2 : A;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < H; ++h) {
       ra[h] = *reinterpret_cast<const u32x4_t*>(Ab + ((int64_t)row[h] * c.lda + (int64_t)kt * BK) * (int64_t)sizeof(T) + c16[h] * 16);
       rb[h] = *reinterpret_cast<const u32x4_t*>(B + ((int64_t)row[h] * c.ldb + (int64_t)kt * BK) * (int64_t)sizeof(T) + c16[h] * 16);
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < H; ++h) {
       *reinterpret_cast<u32x4_t*>(&lds[buf][0][row[h] * kLdsRow + c16[h] * 16]) = ra[h];
       *reinterpret_cast<u32x4_t*>(&lds[buf][1][row[h] * kLdsRow + c16[h] * 16]) = rb[h];
     }
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[X][X];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < X; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16_t{};
+    for (int y = 0; y < X; ++y) acc[x][y] = f32x16_t{};
 
   gload(0);
   sstore(0);
@@ -237,32 +242,32 @@ __global__ __launch_bounds__(256) void k_gemm(GemmCore c, Epi epi) {
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        bf16x8_t af[2], bf[2];
+        bf16x8_t af[X], bf[X];
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
-          af[x] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + x * 32 + (lane & 31)) * kLdsRow + s * 32 + (lane >> 5) * 16);
+        for (int x = 0; x < X; ++x)
+          af[x] = *reinterpret_cast<const bf16x8_t*>(As + (wm * WT + x * 32 + (lane & 31)) * kLdsRow + s * 32 + (lane >> 5) * 16);
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
-          bf[y] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 64 + y * 32 + (lane & 31)) * kLdsRow + s * 32 + (lane >> 5) * 16);
+        for (int y = 0; y < X; ++y)
+          bf[y] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WT + y * 32 + (lane & 31)) * kLdsRow + s * 32 + (lane >> 5) * 16);
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < X; ++x)
 #pragma unroll
-          for (int y = 0; y < 2; ++y) acc[x][y] = mfma_bf16(af[x], bf[y], acc[x][y]);
+          for (int y = 0; y < X; ++y) acc[x][y] = mfma_bf16(af[x], bf[y], acc[x][y]);
       }
     } else {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        float af[2], bf[2];
+        float af[X], bf[X];
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
-          af[x] = *reinterpret_cast<const float*>(As + (wm * 64 + x * 32 + (lane & 31)) * kLdsRow + (s * 2 + (lane >> 5)) * 4);
+        for (int x = 0; x < X; ++x)
+          af[x] = *reinterpret_cast<const float*>(As + (wm * WT + x * 32 + (lane & 31)) * kLdsRow + (s * 2 + (lane >> 5)) * 4);
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
-          bf[y] = *reinterpret_cast<const float*>(Bs + (wn * 64 + y * 32 + (lane & 31)) * kLdsRow + (s * 2 + (lane >> 5)) * 4);
+        for (int y = 0; y < X; ++y)
+          bf[y] = *reinterpret_cast<const float*>(Bs + (wn * WT + y * 32 + (lane & 31)) * kLdsRow + (s * 2 + (lane >> 5)) * 4);
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < X; ++x)
 #pragma unroll
-          for (int y = 0; y < 2; ++y) acc[x][y] = mfma_f32(af[x], bf[y], acc[x][y]);
+          for (int y = 0; y < X; ++y) acc[x][y] = mfma_f32(af[x], bf[y], acc[x][y]);
       }
     }
     if (it + 1 < total) sstore(cur ^ 1);
@@ -271,13 +276,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmCore c, Epi epi) {
 
   // Output layout of a 32x32 block: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32.
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < X; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < X; ++y)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int i0 = tm * kBM + wm * 64 + x * 32 + 8 * g + 4 * (lane >> 5);
-        const int j = tn * kBN + wn * 64 + y * 32 + (lane & 31);
+        const int i0 = tm * BT + wm * WT + x * 32 + 8 * g + 4 * (lane >> 5);
+        const int j = tn * BT + wn * WT + y * 32 + (lane & 31);
         float v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) v[u] = acc[x][y][4 * g + u];
@@ -411,9 +416,15 @@ __global__ __launch_bounds__(256) void k_update0(Update0Launch a) {
 }
 
 template <typename T, class Epi>
-hipError_t run_gemm(const GemmCore& c, const Epi& e, int64_t rows, int count, hipStream_t s) {
-  const int tiles = (int)(rows / kBM) * c.tiles_n;
-  hipLaunchKernelGGL((k_gemm<T, Epi>), dim3(tiles, 1, count), dim3(256), 0, s, c, e);
+hipError_t run_gemm(GemmCore c, const Epi& e, int64_t rows, int64_t cols, int count, hipStream_t s) {
+  // rows and cols are multiples of 128 (the workspace padding).
+  if ((rows / 128) * (cols / 128) * count < 256) {
+    c.tiles_n = (int)(cols / 64);
+    hipLaunchKernelGGL((k_gemm<T, Epi, 64>), dim3((int)(rows / 64) * c.tiles_n, 1, count), dim3(256), 0, s, c, e);
+  } else {
+    c.tiles_n = (int)(cols / 128);
+    hipLaunchKernelGGL((k_gemm<T, Epi, 128>), dim3((int)(rows / 128) * c.tiles_n, 1, count), dim3(256), 0, s, c, e);
+  }
   return hipGetLastError();
 }
 
@@ -443,10 +454,9 @@ hipError_t launch_gram(const GramLaunch& a, hipStream_t s) {
   c.lda = c.ldb = a.np;
   c.sa = c.sb = a.mp * a.np;
   c.K = a.np;
-  c.tiles_n = (int)(a.mp / kBN);
   GramEpi e{a.a32, a.a16, a.scale, a.mp};
-  return a.x_bytes == 2 ? run_gemm<uint16_t>(c, e, a.mp, a.count, s)
-                        : run_gemm<float>(c, e, a.mp, a.count, s);
+  return a.x_bytes == 2 ? run_gemm<uint16_t>(c, e, a.mp, a.mp, a.count, s)
+                        : run_gemm<float>(c, e, a.mp, a.mp, a.count, s);
 }
 
 hipError_t launch_poly(const PolyLaunch& a, hipStream_t s) {
@@ -457,10 +467,9 @@ hipError_t launch_poly(const PolyLaunch& a, hipStream_t s) {
   c.lda = c.ldb = a.mp;
   c.sa = c.sb = a.mp * a.mp;
   c.K = a.mp;
-  c.tiles_n = (int)(a.mp / kBN);
   PolyEpi e{a.a32, a.phi, a.plo, a.p_bytes == 4, a.sc, a.mp};
-  return a.op_bytes == 2 ? run_gemm<uint16_t>(c, e, a.mp, a.count, s)
-                         : run_gemm<float>(c, e, a.mp, a.count, s);
+  return a.op_bytes == 2 ? run_gemm<uint16_t>(c, e, a.mp, a.mp, a.count, s)
+                         : run_gemm<float>(c, e, a.mp, a.mp, a.count, s);
 }
 
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
@@ -473,25 +482,24 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   c.sa = a.mp * a.mp;
   c.sb = a.np * a.mp;
   c.K = a.mp;
-  c.tiles_n = (int)(a.np / kBN);
   if (a.x_bytes == 2) {
     if (a.final_round) {
       FinalEpi<uint16_t> e{static_cast<const uint16_t*>(a.x_old), a.scale, a.sc, a.mats, a.ptrs,
                            a.mp, a.np, a.m, a.n};
-      return run_gemm<uint16_t>(c, e, a.mp, a.count, s);
+      return run_gemm<uint16_t>(c, e, a.mp, a.np, a.count, s);
     }
     ApplyEpi<uint16_t> e{static_cast<const uint16_t*>(a.x_old), static_cast<uint16_t*>(a.x_new),
                          static_cast<uint16_t*>(a.xt_new), a.scale, a.sc, a.mp, a.np};
-    return run_gemm<uint16_t>(c, e, a.mp, a.count, s);
+    return run_gemm<uint16_t>(c, e, a.mp, a.np, a.count, s);
   }
   if (a.final_round) {
     FinalEpi<float> e{static_cast<const float*>(a.x_old), a.scale, a.sc, a.mats, a.ptrs,
                       a.mp, a.np, a.m, a.n};
-    return run_gemm<float>(c, e, a.mp, a.count, s);
+    return run_gemm<float>(c, e, a.mp, a.np, a.count, s);
   }
   ApplyEpi<float> e{static_cast<const float*>(a.x_old), static_cast<float*>(a.x_new),
                     static_cast<float*>(a.xt_new), a.scale, a.sc, a.mp, a.np};
-  return run_gemm<float>(c, e, a.mp, a.count, s);
+  return run_gemm<float>(c, e, a.mp, a.np, a.count, s);
 }
 
 hipError_t launch_update0(const Update0Launch& a, hipStream_t s) {
