@@ -509,9 +509,10 @@ __device__ __forceinline__ void poly_slice(const SkinnyLaunch& a, const SkinnyBu
   // Gram sums over the packed upper triangles: entry v = tid + 256 k of the
   // triangle (kPer = 3 covers m <= 32; KQ <= 5 means m <= 20, nt <= 210, one
   // entry); the loads of a thread's entries for kBatch chunks are in flight
-  // together, and each entry is summed in chunk order.  Loads past the end
-  // read a valid address and are discarded, so the batch is one straight run.
-  constexpr int kBatch = 20, kPer = KQ <= 5 ? 1 : (KQ <= 7 ? 2 : 3);
+  // together (40 chunks, n = 10240, in one batch where the registers allow),
+  // and each entry is summed in chunk order.  Loads past the end read a valid
+  // address and are discarded, so the batch is one straight run.
+  constexpr int kPer = KQ <= 5 ? 1 : (KQ <= 7 ? 2 : 3), kBatch = kPer <= 2 ? 40 : 20;
   const double* parts = bk.gram_parts + (int64_t)z * nch * nt;
   double sum[kPer];
 #pragma unroll
