@@ -122,6 +122,9 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   const int z = (int)(t.bz & 0xFFFFFFu);
   const int tm = (int)(t.mn & 0xFFFFu), tn = (int)(t.mn >> 16);
   const Operands op = Epi::operands(g, bb, z);
+  // The epilogue's context (table reads for the final phase) is fetched
+  // here, so its loads complete during the products.
+  const auto cx = Epi::context(g, bb, z);
 
   const int tid = threadIdx.x, lane = tid & 63;
   // The wave index is uniform over the wave; saying so keeps branches on it scalar.
@@ -238,7 +241,6 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   // staging slots it read them from, and the transposed rows are then read
   // out of LDS down the columns, 8 values (16 bytes of bf16) per thread.
   // Such a phase reads its side inputs in one layout only.
-  const auto cx = Epi::context(g, bb, z);
   const int views = Epi::views(cx, tm == tn);
   const bool mirror = Epi::kMirror && (views & kViewCol);
   const float pre = Epi::prescale(cx);
