@@ -65,6 +65,8 @@ def make_gpu_inputs(wl: workloads.Workload, dev):
 KERNEL_SOURCES = {
     "k_skinny_gram": ("skinny.hip", "device_common.h", "kernels.h", "layout.h"),
     "k_skinny_apply": ("skinny.hip", "device_common.h", "kernels.h", "layout.h"),
+    # apply and final launches of the large-tile products (the "apply" timing class)
+    "apply": ("stream_big.hip", "device_common.h", "kernels.h", "layout.h"),
 }
 
 
@@ -95,6 +97,24 @@ def measured_traffic(kernel: str, workload: str):
                 if len(f) == 5 and f[0] == "traffic" and f[1] == kernel and f[2] == workload and f[3] == want:
                     return float(f[4])
     return None
+
+
+def big_apply_bytes(wl: workloads.Workload) -> float:
+    """Compulsory HBM bytes per launch of the large-tile apply class (k - 1
+    apply launches and one final launch per step), over the slices with
+    m > 512 in their padded workspace layout (multiples of 256): an apply
+    reads R (2 mp^2) and X^T, reads the old X and writes X' and X'^T (2 mp np
+    each); the final launch reads R, X^T and the old X and reads and writes W
+    (float32, 8 m n)."""
+    k = wl.ns_steps
+    apply = final = 0.0
+    for m, n in wl.oriented_matrices():
+        if m <= 512:
+            continue
+        mp, np_ = -(-m // 256) * 256, -(-n // 256) * 256
+        apply += 2 * mp * mp + 8 * mp * np_
+        final += 2 * mp * mp + 4 * mp * np_ + 8 * m * n
+    return ((k - 1) * apply + final) / k if k > 0 else 0.0
 
 
 def measure_ceilings(dev, copy_mib: int = 1024, reps: int = 20, gemm: bool = True):
@@ -282,6 +302,9 @@ def main():
         roof = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
                 "algorithmic_flops_per_launch": per_launch, "avg_launch_ms": round(dom_ms_per_launch, 5)}
+        if dominant == "apply" and mode == "bf16":
+            roof["traffic"] = measured_traffic("apply", wl.name)
+            roof["algorithmic_bytes_per_launch"] = big_apply_bytes(wl)
     if skinny_elems and "skinny_gram" in kernel_ms and "skinny_apply" in kernel_ms:
         sk_ms = kernel_ms["skinny_gram"][0] + kernel_ms["skinny_apply"][0]
         roof["skinny_pair_gbs"] = round((skinny_gram_b + skinny_apply_b) / (sk_ms * 1e-3) / 1e9, 1)
