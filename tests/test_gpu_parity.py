@@ -56,6 +56,13 @@ def test_single_fp32_128x256():
     check([(128, 256)], "fp32", grad_dtype="f32", std=1.0, lr=0.02)
 
 
+@pytest.mark.parametrize("ns", [0, 1, 2, 3, 4])
+def test_single_fp32_128x256_after_each_round(ns):
+    """The same matrix after 0 .. 4 rounds, so every round's Gram, polynomial
+    and apply product meets the fp32 bar on its own (5 rounds above)."""
+    check([(128, 256)], "fp32", grad_dtype="f32", std=1.0, lr=0.02, ns=ns)
+
+
 @pytest.mark.parametrize("mode", ["bf16", "fp32"])
 @pytest.mark.parametrize("shape", [(24, 10240), (10240, 24), (24, 1000), (7, 100), (32, 33),
                                    (1, 64), (16, 5000), (3, 24, 777), (17, 4099)])
