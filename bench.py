@@ -243,6 +243,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / steps
+    # Distribution of single steps: a separate pass, each step between its
+    # own pair of events on the launch stream (kept out of the timed region).
+    n_dist = max(1, min(steps, 100))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dist)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        plan.step(grads, moms, **kw)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    pct = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
+    step_pct = {"p10": round(pct(0.1), 5), "p50": round(pct(0.5), 5), "p90": round(pct(0.9), 5),
+                "steps": n_dist}
     status = plan.status()
     plan.close()
 
@@ -318,6 +331,7 @@ def main():
         "warmup": warmup,
         "ms_per_step": round(ms, 5),
         "wall_ms_per_step": round(wall * 1e3 / steps, 5),
+        "step_ms_percentiles": step_pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
