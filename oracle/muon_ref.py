@@ -32,7 +32,7 @@ Sources (cited by page title and section):
     [E, M, N] only the last two dimensions take part; the E slices are
     mathematically independent.
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
 
 * Newton-Schulz round: ``A = X X^T``, ``B = b A + c A^2``, ``X <- a X + B X``
   with (a, b, c) given by the caller; the standard quintic Muon form.
