@@ -206,7 +206,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
 
     import torch

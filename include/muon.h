@@ -67,7 +67,7 @@ extern "C" {
 typedef enum {
   MUON_OK = 0,
   MUON_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad shape, non-finite scalar ... */
-  MUON_ERR_UNSUPPORTED = 2,      /* valid request this build does not support            */
+  MUON_ERR_UNSUPPORTED = 2,      /* valid request this library does not support          */
   MUON_ERR_HIP = 3,              /* a HIP runtime call failed                             */
   MUON_ERR_OOM = 4,              /* workspace allocation failed or exceeds workspace_limit */
   MUON_ERR_DEVICE_MISMATCH = 5,  /* current device differs from the plan's device         */
