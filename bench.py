@@ -65,8 +65,9 @@ def make_gpu_inputs(wl: workloads.Workload, dev):
 KERNEL_SOURCES = {
     "k_skinny_gram": ("skinny.hip", "device_common.h", "kernels.h", "layout.h"),
     "k_skinny_apply": ("skinny.hip", "device_common.h", "kernels.h", "layout.h"),
-    # apply and final launches of the large-tile products (the "apply" timing class)
-    "apply": ("stream_big.hip", "device_common.h", "kernels.h", "layout.h"),
+    # apply and final launches of the large-tile products (the "apply" timing class);
+    # the planner's tile order decides their operand reuse in the L2
+    "apply": ("stream_big.hip", "device_common.h", "kernels.h", "layout.h", "planner.cpp"),
 }
 
 
