@@ -277,10 +277,12 @@ std::vector<BigTile> big_table(const Plan& p, int phase) {
     const int tn = phase == 2 ? (int)(bp.np / kBigTile) : tm;
     const bool sym = phase != 2;
     const int64_t k = big_k_over_m(phase == 0 ? bp.n : bp.m);
-    // Blocks of 32 tiles, 4 rows x 8 columns; an apply over a slice of at
-    // most 8 row tiles takes all of them x 4 columns instead (a 4-row block
-    // would leave a ragged remainder there; measured 5% faster on 6 x 8).
-    const int kRows = (phase == 2 && tm <= 8) ? 8 : 4, kCols = 32 / kRows;
+    // Blocks of 32 tiles, 4 rows x 8 columns.  A slice of at most 8 row tiles
+    // is cut whole along its rows instead, where a 4-row block would leave a
+    // ragged remainder: an apply takes all its row tiles x 4 columns, a
+    // symmetric product its whole upper triangle as one block (measured on
+    // the 6 x 8 and 6 x 6 grids of [1408,2048]: 5% and 2% faster phases).
+    const int kRows = tm <= 8 ? 8 : 4, kCols = sym && tm <= 8 ? 8 : 32 / kRows;
     for (int z = 0; z < (int)bp.slices.size(); ++z)
       for (int i0 = 0; i0 < tm; i0 += kRows)
         for (int j0 = sym ? (i0 / kCols) * kCols : 0; j0 < tn; j0 += kCols) {
