@@ -52,7 +52,7 @@
  *    on error nothing is enqueued and no memory is modified.
  *  - muon_step is asynchronous on `stream`: device faults surface at the
  *    caller's next synchronisation.  muon_plan_status() reports the plan's
- *    device-side error word (it synchronises).
+ *    device-side error word (it waits for the plan's last step only).
  */
 #ifndef MUON_H
 #define MUON_H
@@ -178,15 +178,17 @@ int muon_plan_query(muon_plan_t plan, muon_plan_info_t* info);
 /* Enqueue one Muon step on `stream` (a hipStream_t; NULL = the null stream).
  * params/grads/momentum: host arrays of n_params device pointers (see above).
  * ns_steps in [0, max_ns_steps]; lr, beta, a, b, c finite.  ns_steps = 0 steps
- * along the normalised momentum.  Does not synchronise the host. */
+ * along the normalised momentum.  Does not synchronise the host and
+ * allocates no memory, host or device.  A step on another stream than the
+ * plan's previous step is ordered after that step (stream wait on an event). */
 int muon_step(muon_plan_t plan, void* const* params, const void* const* grads,
               void* const* momentum, float lr, float beta, int32_t ns_steps,
               float a, float b, float c, void* stream);
 
-/* Synchronise the plan's device and read its device-side error word, then
- * clear it.  Bit 0: some slice's momentum had a non-finite norm (its update
- * is then not finite either).  Returns MUON_ERR_DEVICE when the word was
- * nonzero. */
+/* Wait for the plan's last step (not for other work on the device), read the
+ * plan's device-side error word and clear it.  Bit 0: some slice's momentum
+ * had a non-finite norm (its update is then not finite either); every path
+ * sets it.  Returns MUON_ERR_DEVICE when the word was nonzero. */
 int muon_plan_status(muon_plan_t plan, uint32_t* device_error);
 
 /* Kernel-class timings collected since the last call (opts.timing = 1):
@@ -196,7 +198,8 @@ int muon_plan_status(muon_plan_t plan, uint32_t* device_error);
  * number of classes. */
 int muon_plan_timings(muon_plan_t plan, double* out_ms, int64_t* out_count, int32_t n_out);
 
-/* Release the plan and its device memory.  NULL is a no-op. */
+/* Wait for the plan's last step, then release the plan and its device
+ * memory.  NULL is a no-op. */
 int muon_plan_destroy(muon_plan_t plan);
 
 /* Message of the last failed call on this thread ("" if none). */

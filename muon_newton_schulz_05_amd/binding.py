@@ -225,8 +225,6 @@ def info_dict(info: PlanInfo) -> dict:
 
 # --------------------------------------------------------------------- torch
 
-_TORCH_DTYPE_CODE = None
-
 
 def _dtype_code(t) -> int:
     import torch
@@ -266,9 +264,17 @@ class MuonPlan:
             if p.device != dev or not p.is_contiguous():
                 raise ValueError("parameters must be contiguous and on one device")
         gd = grad_dtypes or [p.dtype for p in self.params]
+        if len(gd) != len(self.params):
+            raise ValueError("grad_dtypes must match the parameter list")
+        codes = {torch.bfloat16: MUON_BF16, "bf16": MUON_BF16, MUON_BF16: MUON_BF16,
+                 torch.float32: MUON_F32, "f32": MUON_F32, MUON_F32: MUON_F32}
+        if any(g not in codes for g in gd):
+            raise TypeError("grad dtypes must be float32 or bfloat16")
+        # The kernels read gradients in the storage type given here, so
+        # step() checks every gradient against it.
+        self.grad_torch_dtypes = [torch.bfloat16 if codes[g] == MUON_BF16 else torch.float32 for g in gd]
         self.descs = make_descs([tuple(p.shape) for p in self.params],
-                                [_dtype_code(p) for p in self.params],
-                                [MUON_BF16 if g == torch.bfloat16 or g == "bf16" else MUON_F32 for g in gd])
+                                [_dtype_code(p) for p in self.params], [codes[g] for g in gd])
         self.opts = make_opts(mode=mode, use_graph=use_graph, eps=eps, timing=timing,
                               skinny_max_m=skinny_max_m, workspace_limit=workspace_limit,
                               max_ns_steps=max_ns_steps, nesterov=nesterov, update_scale=update_scale,
@@ -285,13 +291,18 @@ class MuonPlan:
         import torch
         if len(grads) != len(self.params) or len(momentum) != len(self.params):
             raise ValueError("grads/momentum must match the parameter list")
-        for p, g, m in zip(self.params, grads, momentum):
+        for i, (p, g, m) in enumerate(zip(self.params, grads, momentum)):
             if g.shape != p.shape or m.shape != p.shape:
-                raise ValueError("shape mismatch")
+                raise ValueError(f"parameter {i}: shape mismatch")
+            if g.device != self.device or m.device != self.device:
+                raise ValueError(f"parameter {i}: grads and momentum must be on {self.device}")
+            if g.dtype != self.grad_torch_dtypes[i]:
+                raise TypeError(f"parameter {i}: gradient is {g.dtype}, the plan expects "
+                                f"{self.grad_torch_dtypes[i]}")
             if m.dtype != torch.float32:
-                raise TypeError("momentum must be float32")
+                raise TypeError(f"parameter {i}: momentum must be float32")
             if not (g.is_contiguous() and m.is_contiguous()):
-                raise ValueError("grads and momentum must be contiguous")
+                raise ValueError(f"parameter {i}: grads and momentum must be contiguous")
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
         muon_step(self.handle, [p.data_ptr() for p in self.params], [g.data_ptr() for g in grads],
                   [m.data_ptr() for m in momentum], lr, beta, ns_steps, *coeffs, s.cuda_stream)

@@ -45,11 +45,16 @@ struct muon_plan {
   muon::Plan p;
   int device = 0;
   char* ws = nullptr;
-  std::vector<muon::PtrEntry> ptrs;  // last table uploaded
+  std::vector<muon::PtrEntry> ptrs;  // last table uploaded (n_params entries, sized at creation)
   bool ptrs_valid = false;
   muon::PtrEntry* pinned = nullptr;  // staging for the upload
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
+  // End of the last enqueued step: muon_plan_status and muon_plan_destroy
+  // wait on it, and a step on another stream is ordered after it.
+  hipEvent_t step_done = nullptr;
+  hipStream_t step_stream = nullptr;
+  bool step_recorded = false;
   muon::SkinnyBucket skinny_b0{};  // first skinny bucket (launch arguments); the table is in the workspace
   // graph of the streamed launches, keyed by ns_steps and stream
   hipGraphExec_t gexec = nullptr;
@@ -182,7 +187,7 @@ hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, 
   mo.x_bytes = bp.x_bytes;
   if ((e = timed(plan, muon::kClsMomentum, s, timing, [&] { return muon::launch_momentum(mo, s); })) != hipSuccess)
     return e;
-  muon::NormLaunch no{at<float>(plan, bp.off_sq), scale, sc, cnt, bp.km_tiles};
+  muon::NormLaunch no{at<float>(plan, bp.off_sq), scale, sc, at<uint32_t>(plan, p.off_err), cnt, bp.km_tiles};
   if ((e = timed(plan, muon::kClsNorm, s, timing, [&] { return muon::launch_norm(no, s); })) != hipSuccess)
     return e;
   if (ns == 0) {
@@ -255,6 +260,20 @@ hipError_t enqueue_buckets(muon_plan_t plan, int ns, hipStream_t s, bool timing,
   }
   if (!plan->p.big.empty() && ns > 0) return enqueue_big_rounds(plan, ns, s, timing);
   return hipSuccess;
+}
+
+// Mark the end of the step just enqueued on s.
+int record_step(muon_plan_t plan, hipStream_t s) {
+  const hipError_t e = hipEventRecord(plan->step_done, s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  plan->step_stream = s;
+  plan->step_recorded = true;
+  return MUON_OK;
+}
+
+// Wait for the plan's last step (not for other work on the device).
+hipError_t wait_plan(muon_plan_t plan) {
+  return plan->step_recorded ? hipEventSynchronize(plan->step_done) : hipSuccess;
 }
 
 void drop_graph(muon_plan_t plan) {
@@ -395,6 +414,14 @@ int muon_plan_create(const muon_param_desc_t* descs, int32_t n_params, const muo
   if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&plan->pinned),
                                          sizeof(muon::PtrEntry) * p.n_params, hipHostMallocDefault);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->upload_done, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->step_done, hipEventDisableTiming);
+  if (e == hipSuccess) {
+    try {
+      plan->ptrs.resize(p.n_params);
+    } catch (const std::bad_alloc&) {
+      e = hipErrorOutOfMemory;
+    }
+  }
   if (e != hipSuccess) {
     muon_plan_destroy(plan);
     return hip_fail(e, "plan setup");
@@ -438,28 +465,41 @@ int muon_step(muon_plan_t plan, void* const* params, const void* const* grads, v
     return fail(MUON_ERR_DEVICE_MISMATCH, "plan lives on device %d, current device is %d", plan->device, dev);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  // Pointer table: upload only when it changed.
-  std::vector<muon::PtrEntry> now(p.n_params);
-  for (int i = 0; i < p.n_params; ++i) {
-    now[i].w = params[i];
-    now[i].g = grads[i];
-    now[i].m = static_cast<float*>(momentum[i]);
+  // A step enqueued on another stream than the previous one waits for it:
+  // both use the plan's workspace.
+  if (plan->step_recorded && s != plan->step_stream) {
+    e = hipStreamWaitEvent(s, plan->step_done, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   }
-  const bool same = plan->ptrs_valid &&
-                    std::memcmp(now.data(), plan->ptrs.data(), sizeof(muon::PtrEntry) * p.n_params) == 0;
+
+  // Pointer table: upload only when it changed (compared in place, so a step
+  // allocates no host memory).
+  bool same = plan->ptrs_valid;
+  for (int i = 0; same && i < p.n_params; ++i) {
+    const muon::PtrEntry& o = plan->ptrs[i];
+    same = o.w == params[i] && o.g == grads[i] && o.m == momentum[i];
+  }
   if (!same) {
     if (plan->upload_pending) {
       e = hipEventSynchronize(plan->upload_done);  // the staging buffer is still being read
       if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
     }
-    std::memcpy(plan->pinned, now.data(), sizeof(muon::PtrEntry) * p.n_params);
+    for (int i = 0; i < p.n_params; ++i) {
+      muon::PtrEntry& o = plan->ptrs[i];
+      o.w = params[i];
+      o.g = grads[i];
+      o.m = static_cast<float*>(momentum[i]);
+      plan->pinned[i] = o;
+    }
     e = hipMemcpyAsync(plan->ws + p.off_ptrs, plan->pinned, sizeof(muon::PtrEntry) * p.n_params,
                        hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "pointer table upload");
+    if (e != hipSuccess) {
+      plan->ptrs_valid = false;
+      return hip_fail(e, "pointer table upload");
+    }
     e = hipEventRecord(plan->upload_done, s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     plan->upload_pending = true;
-    plan->ptrs = now;
     plan->ptrs_valid = true;
   }
 
@@ -480,7 +520,7 @@ int muon_step(muon_plan_t plan, void* const* params, const void* const* grads, v
     // Eager: the first kernel writes the scalar block itself.
     e = enqueue_buckets(plan, ns_steps, s, timing, &v);
     if (e != hipSuccess) return hip_fail(e, "launch");
-    return MUON_OK;
+    return record_step(plan, s);
   }
   // Graph replay: kernel arguments are frozen in the graph, so a prologue
   // outside it writes this step's scalars first.
@@ -509,17 +549,24 @@ int muon_step(muon_plan_t plan, void* const* params, const void* const* grads, v
   }
   e = hipGraphLaunch(plan->gexec, s);
   if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
-  return MUON_OK;
+  return record_step(plan, s);
 }
 
 int muon_plan_status(muon_plan_t plan, uint32_t* device_error) {
   if (!plan_ok(plan)) return fail(MUON_ERR_INVALID_ARGUMENT, "invalid plan handle");
-  hipError_t e = hipSetDevice(plan->device);
-  if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e == hipSuccess && cur != plan->device) e = hipSetDevice(plan->device);
+  if (e == hipSuccess) e = wait_plan(plan);
+  if (e != hipSuccess) return hip_fail(e, "waiting for the plan's last step");
+  // Blocking copies: the word is read after the step, and cleared before
+  // this call returns.
   uint32_t word = 0;
+  const uint32_t zero = 0;
   e = hipMemcpy(&word, plan->ws + plan->p.off_err, sizeof word, hipMemcpyDeviceToHost);
-  if (e == hipSuccess && word != 0) e = hipMemset(plan->ws + plan->p.off_err, 0, sizeof word);
+  if (e == hipSuccess && word != 0)
+    e = hipMemcpy(plan->ws + plan->p.off_err, &zero, sizeof zero, hipMemcpyHostToDevice);
+  if (cur >= 0 && cur != plan->device) hipSetDevice(cur);
   if (e != hipSuccess) return hip_fail(e, "reading the device error word");
   if (device_error) *device_error = word;
   if (word != 0) return fail(MUON_ERR_DEVICE, "device error word 0x%x (bit 0: non-finite momentum norm)", word);
@@ -554,7 +601,8 @@ int muon_plan_destroy(muon_plan_t plan) {
   int cur = -1;
   hipGetDevice(&cur);
   if (cur != plan->device) hipSetDevice(plan->device);
-  hipDeviceSynchronize();
+  wait_plan(plan);  // the plan's last step (its timing events and uploads precede it)
+  if (plan->upload_pending) hipEventSynchronize(plan->upload_done);
   drop_graph(plan);
   for (TimedLaunch& t : plan->timed) {
     hipEventDestroy(t.start);
@@ -562,6 +610,7 @@ int muon_plan_destroy(muon_plan_t plan) {
   }
   for (hipEvent_t ev : plan->event_pool) hipEventDestroy(ev);
   if (plan->upload_done) hipEventDestroy(plan->upload_done);
+  if (plan->step_done) hipEventDestroy(plan->step_done);
   if (plan->pinned) hipHostFree(plan->pinned);
   if (plan->ws) hipFree(plan->ws);
   if (cur >= 0 && cur != plan->device) hipSetDevice(cur);

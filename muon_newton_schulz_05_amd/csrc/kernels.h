@@ -53,6 +53,7 @@ struct NormLaunch {
   const float* sq;
   float* scale;           // [count][2] = {s, s*s}
   const DevScalars* sc;
+  uint32_t* err;          // device error word: kErrNonFinite when a sum is not finite
   int count, km_tiles;
 };
 hipError_t launch_norm(const NormLaunch& a, hipStream_t s);

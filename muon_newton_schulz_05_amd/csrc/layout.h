@@ -13,6 +13,9 @@ constexpr int kStreamPad = 128;       // streamed workspace dims are padded to t
 constexpr int kBigTile = 256;         // large bf16 buckets: product tile, and their padding
 constexpr int kBigMinM = 513;         // bf16 buckets with m >= this take the large-tile products
 constexpr int kBigKStep = 64;         // large-tile products: k elements per slice
+// Longest padded n of the large-tile products: 255 rows of n bf16 plus a
+// 16-byte chunk offset stay below 2^32 bytes.
+constexpr int64_t kBigMaxN = int64_t(1) << 23;
 // Contraction length of the large-tile products over a dimension of d (m, or
 // n for the Gram): operand entries past d are zero, so the k loop stops at d
 // rounded up to a slice.

@@ -195,7 +195,10 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
       bp.off_gram = ws.take(cnt * bp.n_chunks * (bp.m * (bp.m + 1) / 2) * sizeof(double));  // upper triangles
       bp.off_qs = ws.take(cnt * 1024 * sizeof(float));
     } else {
-      bp.big = p.mode == MUON_MODE_BF16_MFMA && bp.m >= kBigMinM;
+      // The large-tile products address a 256-row operand panel with 32-bit
+      // lane offsets and a tile column in 16 bits, so slices longer than
+      // kBigMaxN take the general products instead.
+      bp.big = p.mode == MUON_MODE_BF16_MFMA && bp.m >= kBigMinM && round_up(bp.n, kBigTile) <= kBigMaxN;
       const int64_t pad = bp.big ? kBigTile : kStreamPad;
       bp.mp = round_up(bp.m, pad);
       bp.np = round_up(bp.n, pad);

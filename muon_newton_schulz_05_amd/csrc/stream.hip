@@ -151,6 +151,9 @@ __global__ __launch_bounds__(256) void k_norm(NormLaunch a) {
     const double sc = 1.0 / (sqrt(red[0]) + (double)a.sc->eps);
     a.scale[2 * z] = (float)sc;
     a.scale[2 * z + 1] = (float)(sc * sc);
+    // A non-finite momentum entry makes the sum non-finite; the update of
+    // this slice is then not finite either, and the plan's error word says so.
+    if (!isfinite(red[0])) atomicOr(a.err, kErrNonFinite);
   }
 }
 

@@ -336,3 +336,17 @@ def test_large_tile_tables_cover_every_tile_once():
             work.append(w)
         biggest_block = 32 * max((b[3] if ph == 0 else b[2]) for b in buckets)
         assert max(work) - min(work) <= biggest_block
+
+
+def test_overlong_slices_leave_the_large_tile_products(m):
+    """The large-tile products address a 256-row operand panel with 32-bit
+    lane offsets (255 rows of n bf16 must stay below 2^32 bytes), so a slice
+    whose padded n exceeds 2^23 takes the general products; its neighbours
+    keep the large tiles."""
+    buckets, tables = _tables([(600, 9_000_000, 1), (600, 700, 1)])
+    assert [b[:2] for b in buckets] == [(600, 700)]
+    d = m.make_descs([(600, 9_000_000), (600, 700)], ["f32"] * 2, ["bf16"] * 2)
+    info = m.info_dict(m.muon_plan_describe(d, m.make_opts(mode="bf16")))
+    assert info["launches_per_ns"] == 3 + 3  # its own three launches + the grouped large launches
+    buckets, _ = _tables([(600, (1 << 23) - 256, 1)])
+    assert [b[:2] for b in buckets] == [(600, (1 << 23) - 256)]
