@@ -66,25 +66,69 @@ def oracle_step(params, grads, moms, *, lr, beta, ns_steps, coeffs, steps=1, nes
     return w, m, o
 
 
-def slice_rel_errors(got: np.ndarray, ref: np.ndarray):
-    """Relative Frobenius error of every 2-D slice."""
+BLOCK = 64          # side of the blocks of the block-local check
+BLOCK_SHARE = 3.0   # a block may carry this many times its fair share of the allowed error
+
+
+def block_ratios(diff: np.ndarray, ref_norm: float, tol: float, full_shape=None) -> np.ndarray:
+    """Block-local check of one 2-D error matrix.
+
+    ``diff`` is split into BLOCK x BLOCK blocks (ragged edge blocks included).
+    A block b of |b| entries may carry at most BLOCK_SHARE times its share of
+    the slice's allowed error: ||diff_b||_F <= BLOCK_SHARE * tol * ref_norm *
+    sqrt(|b| / (m n)), with m n the size of the whole slice (``full_shape``,
+    default diff.shape) and ref_norm the slice's ||O_ref||_F.  Returns each
+    block's error divided by its bound; a value above 1 fails.  A defect
+    confined to a few blocks (one tile, a mirror write, a ragged edge) stays
+    small in the slice's Frobenius error but not in its own block.
+    """
+    rows, cols = diff.shape
+    mn = float(np.prod(full_shape if full_shape is not None else diff.shape))
+    nbr, nbc = -(-rows // BLOCK), -(-cols // BLOCK)
+    pad = np.zeros((nbr * BLOCK, nbc * BLOCK))
+    pad[:rows, :cols] = diff
+    sq = (pad.reshape(nbr, BLOCK, nbc, BLOCK) ** 2).sum(axis=(1, 3))
+    r_sz = np.full(nbr, BLOCK, np.float64)
+    r_sz[-1] = rows - (nbr - 1) * BLOCK
+    c_sz = np.full(nbc, BLOCK, np.float64)
+    c_sz[-1] = cols - (nbc - 1) * BLOCK
+    size = np.outer(r_sz, c_sz)
+    bound = BLOCK_SHARE * tol * ref_norm * np.sqrt(size / mn)
+    if ref_norm == 0:
+        return np.where(sq > 0, np.inf, 0.0)
+    return np.sqrt(sq) / bound
+
+
+def slice_rel_errors(got: np.ndarray, ref: np.ndarray, tol: float | None = None):
+    """Relative Frobenius error of every 2-D slice.  With ``tol`` every slice
+    must also pass the block-local check at that tolerance."""
     g = oracle.decode(got) if got.dtype == np.uint16 else got.astype(np.float64)
     r = ref.astype(np.float64)
     if r.ndim == 2:
         g, r = g[None], r[None]
     out = []
-    for gs, rs in zip(g, r):
+    for z, (gs, rs) in enumerate(zip(g, r)):
         den = np.linalg.norm(rs)
         out.append(np.linalg.norm(gs - rs) / den if den > 0 else np.linalg.norm(gs))
+        if tol is not None:
+            ratios = block_ratios(gs - rs, den, tol)
+            worst = float(ratios.max())
+            if worst > 1.0:
+                bi, bj = np.unravel_index(int(np.argmax(ratios)), ratios.shape)
+                raise AssertionError(
+                    f"slice {z} {rs.shape}: block ({bi * BLOCK}, {bj * BLOCK}) carries {worst:.2f} times "
+                    f"the allowed {BLOCK_SHARE} x fair share of the error (relative error of the whole "
+                    f"slice {out[-1]:.3e}, tolerance {tol})")
     return out
 
 
-def update_errors(w_new_gpu, w_old, lr, o_ref):
-    """Relative Frobenius error of the applied update O = (W_old - W_new) / lr per slice."""
+def update_errors(w_new_gpu, w_old, lr, o_ref, tol: float | None = None):
+    """Relative Frobenius error of the applied update O = (W_old - W_new) / lr
+    per slice (with ``tol``: plus the block-local check)."""
     w_old64 = oracle.decode(w_old) if w_old.dtype == np.uint16 else w_old.astype(np.float64)
     w_new64 = oracle.decode(w_new_gpu) if w_new_gpu.dtype == np.uint16 else w_new_gpu.astype(np.float64)
     o_gpu = (w_old64 - w_new64) / np.float64(np.float32(lr))
-    return slice_rel_errors(o_gpu, o_ref)
+    return slice_rel_errors(o_gpu, o_ref, tol)
 
 
 def max_ulp_diff(a: np.ndarray, b: np.ndarray) -> int:

@@ -17,6 +17,15 @@ Checked per case:
     Frobenius norm within 5% of the sampled slice's (Gaussian matrices of one
     shape have near-identical singular-value spectra, so the Newton-Schulz
     output norm concentrates tightly).
+
+The LAST slice of every large bucket also gets its seeded gradient, and its
+contiguous bottom-right output tile (256 x 256, or the ragged remainder) is
+compared entry by entry with the stored oracle tile
+(tests/golden/large_last_tiles.*): relative error of the tile within the
+bar, and every 64 x 64 block of it within 3 times its share of the slice's
+allowed error (the block-local check of gpu_helpers).  The 32 skinny
+[24,10240] expert slices of the MoE workload are compared whole against the
+oracle, run here.
 """
 
 from __future__ import annotations
@@ -27,15 +36,23 @@ import os
 import numpy as np
 import pytest
 
+import oracle
 import workloads
-from gpu_helpers import TOL, to_device
+from gpu_helpers import TOL, block_ratios, to_device, to_host, update_errors
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 GOLDEN = os.path.join(HERE, "golden", "large_slices.json")
+TILES = os.path.join(HERE, "golden", "large_last_tiles.json")
+TILE_VALUES = os.path.join(HERE, "golden", "large_last_tiles.npz")
 
 
 def _cases():
     with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+def _tile_cases():
+    with open(TILES) as f:
         return json.load(f)["cases"]
 
 
@@ -53,12 +70,14 @@ def test_full_workload_sampled(workload, mode):
     from muon_newton_schulz_05_amd import MuonPlan
 
     cases = [c for c in _cases() if c["workload"] == workload]
-    assert cases
+    tiles = [c for c in _tile_cases() if c["workload"] == workload]
+    assert cases and tiles
     wl = workloads.WORKLOADS[workload]
     dev = torch.device("cuda:0")
     print(f"full-size parity: {workload} ({mode} mode)", flush=True)
 
-    golden_params = {c["param"] for c in cases}
+    skinny_params = [i for i, spec in enumerate(wl.params) if min(spec.shape[-2:]) <= 32]
+    golden_params = {c["param"] for c in cases} | {c["param"] for c in tiles} | set(skinny_params)
     gen = torch.Generator(device=dev)
     grads, params, moms = [], [], []
     for i, spec in enumerate(wl.params):
@@ -81,6 +100,29 @@ def test_full_workload_sampled(workload, mode):
         return t[s] if t.dim() == 3 else t
 
     tol = TOL[mode]
+    values = np.load(TILE_VALUES)
+    for c in tiles:
+        o_gpu = -slice_of(params[c["param"]], c["slice"])
+        assert list(o_gpu.shape) == c["shape"]
+        got = o_gpu[c["row0"]:, c["col0"]:].double().cpu().numpy()
+        ref = values[c["array"]].astype(np.float64)
+        assert got.shape == ref.shape
+        err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        worst_block = float(block_ratios(got - ref, c["frobenius"], tol, full_shape=c["shape"]).max())
+        print(f"  {workload} param {c['param']} slice {c['slice']} {c['shape']}: last tile "
+              f"[{c['row0']}:, {c['col0']}:] rel err {err:.3e}, worst block {worst_block:.3f} of its bound",
+              flush=True)
+        assert err <= tol, (c["shape"], err)
+        assert worst_block <= 1.0, (c["shape"], worst_block)
+
+    for i in skinny_params:
+        g = workloads.gradient(wl, i)
+        zeros = np.zeros(wl.params[i].shape, np.float32)
+        _, _, o_ref = oracle.muon_step([zeros], [g], [zeros], lr=1.0, beta=wl.beta, ns_steps=wl.ns_steps,
+                                       a=wl.coeffs[0], b=wl.coeffs[1], c=wl.coeffs[2])
+        errs = update_errors(to_host(params[i]), zeros, 1.0, o_ref[0], tol)
+        print(f"  {workload} param {i} {wl.params[i].shape}: whole, worst slice {max(errs):.3e}", flush=True)
+        assert max(errs) <= tol
     for c in cases:
         o_gpu = -slice_of(params[c["param"]], c["slice"])
         assert list(o_gpu.shape) == c["shape"]

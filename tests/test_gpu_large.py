@@ -31,20 +31,43 @@ def _check(shapes, *, ns=5, steps=1, param_dtypes=None, w_std=0.0, m_std=0.0, se
     worst = 0.0
     for i in range(len(shapes)):
         if steps == 1:
-            errs = update_errors(w_gpu[i], params[i], lr, o_ref[i])
+            errs = update_errors(w_gpu[i], params[i], lr, o_ref[i], BAR)
         else:  # compare the accumulated change of W, which the initial W would swamp
             w0 = params[i].astype(np.float64)
-            errs = slice_rel_errors(w_gpu[i].astype(np.float64) - w0, w_ref[i] - w0)
+            errs = slice_rel_errors(w_gpu[i].astype(np.float64) - w0, w_ref[i] - w0, BAR)
         worst = max(worst, max(errs))
-        assert max(slice_rel_errors(m_gpu[i], m_ref[i])) <= 1e-6
+        assert max(slice_rel_errors(m_gpu[i], m_ref[i], 1e-6)) <= 1e-6
     print(f"{shapes} ns={ns} steps={steps}: worst {worst:.3e}", flush=True)
     assert worst <= BAR, worst
     return worst
 
 
-@pytest.mark.parametrize("shape", [(600, 700), (700, 600), (1024, 1280), (514, 517), (2, 520, 1030)])
+@pytest.mark.parametrize("shape", [(600, 700), (700, 600), (1024, 1280), (514, 517), (2, 520, 1030),
+                                   (2100, 2200)])
 def test_large_shapes(shape):
+    """(2100, 2200) has 9 row tiles of 256, so its tile table takes the
+    4 x 8 blocks; the others have at most 8 and take whole-height blocks."""
     _check([shape])
+
+
+def test_large_fusion_is_bitexact():
+    """Fused large buckets give bitwise the W and M of one plan per slice:
+    three [600,700] slices fused, the two slices of a [2,520,1030] stack,
+    and two [2100,2200] slices (9 row tiles: the 4 x 8 block branch of the
+    tile table) next to a transposed [700,600].  A slice's products do not
+    depend on which table entries or workgroups computed its tiles."""
+    shapes = [(600, 700)] * 3 + [(2, 520, 1030), (2100, 2200), (2100, 2200), (700, 600)]
+    params, grads, moms = make_inputs(shapes, "bf16", 83, w_std=0.02, m_std=1e-3)
+    kw = dict(mode="bf16", lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    w_f, m_f = gpu_step(params, grads, moms, **kw)
+    for i, shp in enumerate(shapes):
+        if len(shp) == 3:
+            for e in range(shp[0]):
+                w_1, m_1 = gpu_step([params[i][e]], [grads[i][e]], [moms[i][e]], **kw)
+                assert np.array_equal(w_f[i][e], w_1[0]) and np.array_equal(m_f[i][e], m_1[0]), (i, e)
+        else:
+            w_1, m_1 = gpu_step([params[i]], [grads[i]], [moms[i]], **kw)
+            assert np.array_equal(w_f[i], w_1[0]) and np.array_equal(m_f[i], m_1[0]), i
 
 
 @pytest.mark.parametrize("ns", [0, 1, 2])
