@@ -120,9 +120,13 @@ def newton_schulz(x: np.ndarray, steps: int, a: float, b: float, c: float) -> np
 
 
 def orthogonalize(m: np.ndarray, steps: int, a: float, b: float, c: float,
-                  eps: float = DEFAULT_EPS) -> np.ndarray:
-    """O for one 2-D momentum slice: orient, normalise, iterate, un-orient."""
-    x, transposed = orient(decode(m))
+                  eps: float = DEFAULT_EPS, dtype=np.float64) -> np.ndarray:
+    """O for one 2-D momentum slice: orient, normalise, iterate, un-orient.
+
+    ``dtype`` float32 runs the same steps in float32 storage; it exists only
+    so that the CPU baseline can also be timed in the GPU path's precision
+    class.  Parity references always use the float64 default."""
+    x, transposed = orient(decode(m).astype(dtype, copy=False))
     x = frobenius_normalize(x, eps)
     x = newton_schulz(x, steps, a, b, c)
     return x.T if transposed else x
@@ -165,14 +169,14 @@ def _slices(shape: tuple[int, ...]):
 
 def muon_step(params, grads, momenta, *, lr: float, beta: float, ns_steps: int,
               a: float, b: float, c: float, eps: float = DEFAULT_EPS, nesterov: bool = False,
-              weight_decay: float = 0.0, update_scale_mode: str = "none"):
+              weight_decay: float = 0.0, update_scale_mode: str = "none", dtype=np.float64):
     """One Muon step over a list of parameters.
 
     Each parameter is 2-D [R, C] or 3-D [E, R, C]; every 2-D slice is handled
     on its own.  Returns ``(new_params, new_momenta, updates)``: new parameters
     as float64 arrays (not rounded to the parameter's storage type), new
     momenta as float32 arrays and the orthogonalised directions O as float64
-    (before the shape factor).
+    (before the shape factor).  ``dtype``: see ``orthogonalize``.
     """
     new_params, new_momenta, updates = [], [], []
     lr = f32(lr)
@@ -184,7 +188,7 @@ def muon_step(params, grads, momenta, *, lr: float, beta: float, ns_steps: int,
         f = update_scale(d.shape[-2], d.shape[-1], update_scale_mode)
         o = np.zeros(m_new.shape, dtype=np.float64)
         for sl in _slices(m_new.shape):
-            o[sl] = orthogonalize(d[sl], ns_steps, a, b, c, eps)
+            o[sl] = orthogonalize(d[sl], ns_steps, a, b, c, eps, dtype)
         new_params.append(w64 - lr * wd * w64 - lr * f * o)
         new_momenta.append(m_new)
         updates.append(o)

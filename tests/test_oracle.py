@@ -472,3 +472,16 @@ def test_planted_nesterov_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(muon_ref, "update_direction",
                         lambda m, g, beta, nest: (1.0 + float(np.float32(beta))) * real(m, g, beta, False))
     assert nesterov_pair_error(muon_ref.muon_step, True) > 1e-3
+
+
+def test_float32_storage_option_is_only_a_timing_variant():
+    """The float32 storage option (used only to time the CPU baseline in the
+    GPU path's precision class) runs the same steps: it agrees with the
+    float64 default to float32 accuracy and does not change the default."""
+    rng = np.random.default_rng(5)
+    g = rng.standard_normal((40, 300)).astype(np.float32)
+    o64 = oracle.orthogonalize(g, 5, *QUINTIC)
+    o32 = oracle.orthogonalize(g, 5, *QUINTIC, dtype=np.float32)
+    assert o64.dtype == np.float64 and o32.dtype == np.float32
+    assert np.linalg.norm(o32 - o64) / np.linalg.norm(o64) < 1e-5
+    assert np.array_equal(o64, oracle.orthogonalize(g, 5, *QUINTIC, dtype=np.float64))
