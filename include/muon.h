@@ -202,6 +202,39 @@ int muon_plan_timings(muon_plan_t plan, double* out_ms, int64_t* out_count, int3
  * memory.  NULL is a no-op. */
 int muon_plan_destroy(muon_plan_t plan);
 
+/* Size of the fixed device scratch array of muon_step_noalloc: 64 MiB per
+ * device, held from the first call on that device until the process ends. */
+#define MUON_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one Muon
+ * step over the parameters described by descs/opts (as for
+ * muon_plan_create), run in a fixed file-scope device array of
+ * MUON_NOALLOC_SCRATCH_BYTES instead of a plan's workspace.  The results are
+ * those of muon_plan_create + muon_step on the same arguments (same kernels,
+ * same arithmetic).
+ *  - params/grads/momentum, lr, beta, ns_steps, a, b, c, stream: as for
+ *    muon_step.  opts->use_graph and opts->timing must be 0.
+ *  - device_error: NULL, or a 4-byte aligned DEVICE word owned by the caller
+ *    into which bit 0 is OR-ed when a slice's momentum norm is not finite
+ *    (the word is not cleared by this call).
+ *  - Calls no hipMalloc, hipFree or other device or pinned-host allocation.
+ *    The plan is built on the host's C++ heap and freed before return; the
+ *    scratch is cleared by a kernel, and its tables (a few KB) are copied
+ *    from pageable host memory, which makes those copies synchronous with
+ *    respect to the host.
+ *  - Every call on one device shares that device's scratch and overwrites
+ *    it: calls that overlap on one GPU (other streams, other threads) race.
+ *    Steps enqueued one after another on one stream are ordered as usual.
+ * Errors: those of muon_plan_create and muon_step, plus UNSUPPORTED when the
+ * step needs more than MUON_NOALLOC_SCRATCH_BYTES of scratch (checked on the
+ * host before any device call; use a plan instead), INVALID_ARGUMENT for
+ * use_graph/timing or a misaligned device_error. */
+int muon_step_noalloc(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_opts_t* opts,
+                      void* const* params, const void* const* grads, void* const* momentum, float lr,
+                      float beta, int32_t ns_steps, float a, float b, float c, uint32_t* device_error,
+                      void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* muon_last_error(void);
 

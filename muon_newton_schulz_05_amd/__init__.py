@@ -30,4 +30,6 @@ from .binding import (  # noqa: F401
     muon_plan_status,
     muon_plan_timings,
     muon_step,
+    muon_step_noalloc,
+    MUON_NOALLOC_SCRATCH_BYTES,
 )

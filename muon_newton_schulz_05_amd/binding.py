@@ -34,7 +34,8 @@ KERNEL_CLASSES = ("skinny_gram", "skinny_poly", "skinny_apply", "momentum", "nor
                   "update")
 EXPORTED = ("muon_default_opts", "muon_plan_create", "muon_plan_describe", "muon_plan_query",
             "muon_step", "muon_plan_status", "muon_plan_timings", "muon_plan_destroy",
-            "muon_last_error")
+            "muon_step_noalloc", "muon_last_error")
+MUON_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class ParamDesc(ctypes.Structure):
@@ -104,10 +105,14 @@ def load_library(path: str = LIB_PATH):
     lib.muon_plan_timings.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
                                       ctypes.c_int32]
     lib.muon_plan_destroy.argtypes = [P]
+    lib.muon_step_noalloc.argtypes = [ctypes.POINTER(ParamDesc), ctypes.c_int32, ctypes.POINTER(PlanOpts),
+                                      ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P),
+                                      ctypes.c_float, ctypes.c_float, ctypes.c_int32,
+                                      ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P]
     lib.muon_last_error.argtypes = []
     lib.muon_last_error.restype = ctypes.c_char_p
     for name in ("muon_plan_create", "muon_plan_describe", "muon_plan_query", "muon_step",
-                 "muon_plan_status", "muon_plan_timings", "muon_plan_destroy"):
+                 "muon_plan_status", "muon_plan_timings", "muon_plan_destroy", "muon_step_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -186,6 +191,19 @@ def muon_step(plan, params, grads, momentum, lr, beta, ns_steps, a, b, c, stream
     P = ctypes.c_void_p * n
     _check(load_library().muon_step(plan, P(*params), P(*grads), P(*momentum), lr, beta, ns_steps,
                                     a, b, c, ctypes.c_void_p(stream)), "muon_step")
+
+
+def muon_step_noalloc(descs, opts, params, grads, momentum, lr, beta, ns_steps, a, b, c,
+                      device_error, stream) -> None:
+    """One step in the library's fixed device scratch (no plan, no allocation).
+    params/grads/momentum: sequences of device addresses (ints); device_error:
+    a device address of a uint32 word, or 0."""
+    n = len(params)
+    P = ctypes.c_void_p * n
+    _check(load_library().muon_step_noalloc(descs, len(descs), ctypes.byref(opts) if opts else None,
+                                            P(*params), P(*grads), P(*momentum), lr, beta, ns_steps, a, b, c,
+                                            ctypes.c_void_p(device_error or None), ctypes.c_void_p(stream)),
+           "muon_step_noalloc")
 
 
 def muon_plan_status(plan) -> int:

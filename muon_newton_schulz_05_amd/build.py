@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmuon.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.cpp", "planner.cpp", "skinny.hip", "stream.hip", "stream_big.hip"]
+SOURCES = ["api.cpp", "planner.cpp", "skinny.hip", "stream.hip", "stream_big.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -65,6 +65,7 @@ struct muon_plan {
   std::vector<hipEvent_t> event_pool;
   double acc_ms[muon::kNumClasses] = {};
   int64_t acc_cnt[muon::kNumClasses] = {};
+  uint32_t* err_word = nullptr;  // the device error word (in the workspace, or the caller's)
 };
 
 namespace {
@@ -85,6 +86,91 @@ hipEvent_t take_event(muon_plan_t plan) {
   hipEvent_t e = nullptr;
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
+}
+
+// A table the kernels read from the workspace: its offset and bytes.
+struct Upload {
+  uint64_t off;
+  std::vector<char> bytes;
+};
+
+template <typename T>
+void add_upload(std::vector<Upload>* ups, uint64_t off, const std::vector<T>& v) {
+  Upload u{off, std::vector<char>(sizeof(T) * v.size())};
+  std::memcpy(u.bytes.data(), v.data(), u.bytes.size());
+  ups->push_back(std::move(u));
+}
+
+// The device tables of a plan whose workspace starts at plan->ws: every
+// bucket's slice table, the skinny and large bucket arrays (which hold
+// workspace addresses) and the large-tile tables.  Also sets
+// plan->skinny_b0.  Returns false if the host is out of memory.
+bool device_tables(muon_plan_t plan, std::vector<Upload>* ups) try {
+  const muon::Plan& p = plan->p;
+  for (const auto& bp : p.buckets) {
+    std::vector<muon::DevMat> table;
+    for (int si : bp.slices) {
+      const muon::Slice& s = p.slices[si];
+      muon::DevMat d;
+      d.param = s.param;
+      d.transposed = s.transposed;
+      d.pdtype = s.pdtype;
+      d.gdtype = s.gdtype;
+      d.slice_off = s.slice_off;
+      table.push_back(d);
+    }
+    add_upload(ups, bp.off_mats, table);
+  }
+  if (!p.skinny.empty()) {
+    std::vector<muon::SkinnyBucket> sbs;
+    int item0 = 0, slice0 = 0;
+    for (int b : p.skinny) {
+      const muon::BucketPlan& bp = p.buckets[b];
+      muon::SkinnyBucket sb{};
+      sb.mats = at<muon::DevMat>(plan, bp.off_mats);
+      sb.gram_parts = at<double>(plan, bp.off_gram);
+      sb.qs = at<float>(plan, bp.off_qs);
+      sb.m = (int32_t)bp.m;
+      sb.n = (int32_t)bp.n;
+      sb.n_chunks = bp.n_chunks;
+      sb.count = (int32_t)bp.slices.size();
+      sb.item0 = item0;
+      sb.slice0 = slice0;
+      item0 += sb.count * sb.n_chunks;
+      slice0 += sb.count;
+      sbs.push_back(sb);
+    }
+    plan->skinny_b0 = sbs[0];
+    add_upload(ups, p.off_skinny_params, sbs);
+  }
+  if (!p.big.empty()) {
+    std::vector<muon::BigBucket> bbs;
+    for (int b : p.big) {
+      const muon::BucketPlan& bp = p.buckets[b];
+      muon::BigBucket bb{};
+      for (int i = 0; i < 2; ++i) {
+        bb.x[i] = plan->ws + bp.off_x[i];
+        bb.xt[i] = plan->ws + bp.off_xt[i];
+      }
+      bb.a32 = at<float>(plan, bp.off_a32);
+      bb.e16 = at<uint16_t>(plan, bp.off_a16);
+      bb.dg = at<float>(plan, bp.off_dg);
+      bb.r16 = at<uint16_t>(plan, bp.off_phi);
+      bb.scale = at<float>(plan, bp.off_scale);
+      bb.mats = at<muon::DevMat>(plan, bp.off_mats);
+      bb.m = bp.m;
+      bb.n = bp.n;
+      bb.mp = bp.mp;
+      bb.np = bp.np;
+      bb.vec = (bp.m % 4 == 0) && (bp.n % 4 == 0);
+      bbs.push_back(bb);
+    }
+    add_upload(ups, p.off_big_params, bbs);
+    for (int ph = 0; ph < 3; ++ph) add_upload(ups, p.off_big_tab[ph], p.big_tab[ph]);
+  }
+  return true;
+} catch (const std::bad_alloc&) {
+  return false;
 }
 
 // Run one launch, bracketed by events when timing is on.
@@ -113,7 +199,7 @@ hipError_t enqueue_skinny(muon_plan_t plan, hipStream_t s, bool timing, const mu
     L.sv = *first;
     L.sc_out = at<muon::DevScalars>(plan, p.off_scalars);
   }
-  L.err = at<uint32_t>(plan, p.off_err);
+  L.err = plan->err_word;
   L.items = p.skinny_items;
   L.slices = p.skinny_slices;
   L.m_max = p.skinny_m_max;
@@ -187,7 +273,7 @@ hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, 
   mo.x_bytes = bp.x_bytes;
   if ((e = timed(plan, muon::kClsMomentum, s, timing, [&] { return muon::launch_momentum(mo, s); })) != hipSuccess)
     return e;
-  muon::NormLaunch no{at<float>(plan, bp.off_sq), scale, sc, at<uint32_t>(plan, p.off_err), cnt, bp.km_tiles};
+  muon::NormLaunch no{at<float>(plan, bp.off_sq), scale, sc, plan->err_word, cnt, bp.km_tiles};
   if ((e = timed(plan, muon::kClsNorm, s, timing, [&] { return muon::launch_norm(no, s); })) != hipSuccess)
     return e;
   if (ns == 0) {
@@ -260,6 +346,45 @@ hipError_t enqueue_buckets(muon_plan_t plan, int ns, hipStream_t s, bool timing,
   }
   if (!plan->p.big.empty() && ns > 0) return enqueue_big_rounds(plan, ns, s, timing);
   return hipSuccess;
+}
+
+// Checks of muon_step's arguments that need no device: pointers (non-null,
+// 16-byte aligned), ns_steps range, finite scalars.
+int check_step_args(const muon::Plan& p, void* const* params, const void* const* grads, void* const* momentum,
+                    float lr, float beta, int32_t ns_steps, float a, float b, float c) {
+  if (!params || !grads || !momentum) return fail(MUON_ERR_INVALID_ARGUMENT, "null pointer array");
+  for (int i = 0; i < p.n_params; ++i) {
+    const void* ptr3[3] = {params[i], grads[i], momentum[i]};
+    const char* names[3] = {"params", "grads", "momentum"};
+    for (int k = 0; k < 3; ++k) {
+      if (ptr3[k] == nullptr) return fail(MUON_ERR_INVALID_ARGUMENT, "%s[%d] is null", names[k], i);
+      if ((reinterpret_cast<uintptr_t>(ptr3[k]) & 15) != 0)
+        return fail(MUON_ERR_INVALID_ARGUMENT, "%s[%d] is not 16-byte aligned", names[k], i);
+    }
+  }
+  if (ns_steps < 0 || ns_steps > p.max_ns_steps)
+    return fail(MUON_ERR_INVALID_ARGUMENT, "ns_steps %d outside [0, %d]", ns_steps, p.max_ns_steps);
+  const float sc5[5] = {lr, beta, a, b, c};
+  const char* sn[5] = {"lr", "beta", "a", "b", "c"};
+  for (int k = 0; k < 5; ++k)
+    if (!std::isfinite(sc5[k])) return fail(MUON_ERR_INVALID_ARGUMENT, "%s is not finite", sn[k]);
+  return MUON_OK;
+}
+
+muon::DevScalars step_scalars(const muon::Plan& p, float lr, float beta, int32_t ns_steps, float a, float b,
+                              float c) {
+  muon::DevScalars v;
+  v.lr = lr;
+  v.beta = beta;
+  v.a = a;
+  v.b = b;
+  v.c = c;
+  v.eps = p.eps;
+  v.decay = lr * p.weight_decay;
+  v.ns_steps = ns_steps;
+  v.nesterov = p.nesterov;
+  v.scale_mode = p.update_scale;
+  return v;
 }
 
 // Mark the end of the step just enqueued on s.
@@ -341,75 +466,14 @@ int muon_plan_create(const muon_param_desc_t* descs, int32_t n_params, const muo
     return fail(MUON_ERR_OOM, "workspace of %llu bytes: %s", (unsigned long long)p.ws_total,
                 hipGetErrorString(e));
   }
+  plan->err_word = at<uint32_t>(plan, p.off_err);
   // Zero once: padding of the streamed workspace must stay exactly zero.
   e = hipMemset(plan->ws, 0, p.ws_total);
-  std::vector<muon::DevMat> table;
-  for (const auto& bp : p.buckets) {
+  std::vector<Upload> ups;
+  if (e == hipSuccess && !device_tables(plan, &ups)) e = hipErrorOutOfMemory;
+  for (const Upload& u : ups) {
     if (e != hipSuccess) break;
-    table.clear();
-    for (int si : bp.slices) {
-      const muon::Slice& s = p.slices[si];
-      muon::DevMat d;
-      d.param = s.param;
-      d.transposed = s.transposed;
-      d.pdtype = s.pdtype;
-      d.gdtype = s.gdtype;
-      d.slice_off = s.slice_off;
-      table.push_back(d);
-    }
-    e = hipMemcpy(plan->ws + bp.off_mats, table.data(), sizeof(muon::DevMat) * table.size(),
-                  hipMemcpyHostToDevice);
-  }
-  if (e == hipSuccess && !p.skinny.empty()) {
-    std::vector<muon::SkinnyBucket> sbs;
-    int item0 = 0, slice0 = 0;
-    for (int b : p.skinny) {
-      const muon::BucketPlan& bp = p.buckets[b];
-      muon::SkinnyBucket sb{};
-      sb.mats = at<muon::DevMat>(plan, bp.off_mats);
-      sb.gram_parts = at<double>(plan, bp.off_gram);
-      sb.qs = at<float>(plan, bp.off_qs);
-      sb.m = (int32_t)bp.m;
-      sb.n = (int32_t)bp.n;
-      sb.n_chunks = bp.n_chunks;
-      sb.count = (int32_t)bp.slices.size();
-      sb.item0 = item0;
-      sb.slice0 = slice0;
-      item0 += sb.count * sb.n_chunks;
-      slice0 += sb.count;
-      sbs.push_back(sb);
-    }
-    plan->skinny_b0 = sbs[0];
-    e = hipMemcpy(plan->ws + p.off_skinny_params, sbs.data(), sizeof(muon::SkinnyBucket) * sbs.size(),
-                  hipMemcpyHostToDevice);
-  }
-  if (e == hipSuccess && !p.big.empty()) {
-    std::vector<muon::BigBucket> bbs;
-    for (int b : p.big) {
-      const muon::BucketPlan& bp = p.buckets[b];
-      muon::BigBucket bb{};
-      for (int i = 0; i < 2; ++i) {
-        bb.x[i] = plan->ws + bp.off_x[i];
-        bb.xt[i] = plan->ws + bp.off_xt[i];
-      }
-      bb.a32 = at<float>(plan, bp.off_a32);
-      bb.e16 = at<uint16_t>(plan, bp.off_a16);
-      bb.dg = at<float>(plan, bp.off_dg);
-      bb.r16 = at<uint16_t>(plan, bp.off_phi);
-      bb.scale = at<float>(plan, bp.off_scale);
-      bb.mats = at<muon::DevMat>(plan, bp.off_mats);
-      bb.m = bp.m;
-      bb.n = bp.n;
-      bb.mp = bp.mp;
-      bb.np = bp.np;
-      bb.vec = (bp.m % 4 == 0) && (bp.n % 4 == 0);
-      bbs.push_back(bb);
-    }
-    e = hipMemcpy(plan->ws + p.off_big_params, bbs.data(), sizeof(muon::BigBucket) * bbs.size(),
-                  hipMemcpyHostToDevice);
-    for (int ph = 0; ph < 3 && e == hipSuccess; ++ph)
-      e = hipMemcpy(plan->ws + p.off_big_tab[ph], p.big_tab[ph].data(),
-                    sizeof(muon::BigTile) * p.big_tab[ph].size(), hipMemcpyHostToDevice);
+    e = hipMemcpy(plan->ws + u.off, u.bytes.data(), u.bytes.size(), hipMemcpyHostToDevice);
   }
   if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&plan->pinned),
                                          sizeof(muon::PtrEntry) * p.n_params, hipHostMallocDefault);
@@ -442,22 +506,8 @@ int muon_step(muon_plan_t plan, void* const* params, const void* const* grads, v
               float lr, float beta, int32_t ns_steps, float a, float b, float c, void* stream) {
   if (!plan_ok(plan)) return fail(MUON_ERR_INVALID_ARGUMENT, "invalid plan handle");
   const muon::Plan& p = plan->p;
-  if (!params || !grads || !momentum) return fail(MUON_ERR_INVALID_ARGUMENT, "null pointer array");
-  for (int i = 0; i < p.n_params; ++i) {
-    const void* ptr3[3] = {params[i], grads[i], momentum[i]};
-    const char* names[3] = {"params", "grads", "momentum"};
-    for (int k = 0; k < 3; ++k) {
-      if (ptr3[k] == nullptr) return fail(MUON_ERR_INVALID_ARGUMENT, "%s[%d] is null", names[k], i);
-      if ((reinterpret_cast<uintptr_t>(ptr3[k]) & 15) != 0)
-        return fail(MUON_ERR_INVALID_ARGUMENT, "%s[%d] is not 16-byte aligned", names[k], i);
-    }
-  }
-  if (ns_steps < 0 || ns_steps > p.max_ns_steps)
-    return fail(MUON_ERR_INVALID_ARGUMENT, "ns_steps %d outside [0, %d]", ns_steps, p.max_ns_steps);
-  const float sc5[5] = {lr, beta, a, b, c};
-  const char* sn[5] = {"lr", "beta", "a", "b", "c"};
-  for (int k = 0; k < 5; ++k)
-    if (!std::isfinite(sc5[k])) return fail(MUON_ERR_INVALID_ARGUMENT, "%s is not finite", sn[k]);
+  const int bad = check_step_args(p, params, grads, momentum, lr, beta, ns_steps, a, b, c);
+  if (bad != MUON_OK) return bad;
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -503,17 +553,7 @@ int muon_step(muon_plan_t plan, void* const* params, const void* const* grads, v
     plan->ptrs_valid = true;
   }
 
-  muon::DevScalars v;
-  v.lr = lr;
-  v.beta = beta;
-  v.a = a;
-  v.b = b;
-  v.c = c;
-  v.eps = p.eps;
-  v.decay = lr * p.weight_decay;
-  v.ns_steps = ns_steps;
-  v.nesterov = p.nesterov;
-  v.scale_mode = p.update_scale;
+  const muon::DevScalars v = step_scalars(p, lr, beta, ns_steps, a, b, c);
   const bool timing = p.timing != 0;
   const bool graph = p.use_graph && !timing && s != nullptr;
   if (!graph) {
@@ -550,6 +590,74 @@ int muon_step(muon_plan_t plan, void* const* params, const void* const* grads, v
   e = hipGraphLaunch(plan->gexec, s);
   if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
   return record_step(plan, s);
+}
+
+int muon_step_noalloc(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_opts_t* opts,
+                      void* const* params, const void* const* grads, void* const* momentum, float lr,
+                      float beta, int32_t ns_steps, float a, float b, float c, uint32_t* device_error,
+                      void* stream) {
+  if (opts && (opts->use_graph || opts->timing))
+    return fail(MUON_ERR_INVALID_ARGUMENT, "muon_step_noalloc takes neither use_graph nor timing");
+  // The plan lives on this stack frame; its workspace is the fixed scratch.
+  muon_plan plan;
+  std::string err;
+  int rc;
+  try {
+    rc = muon::make_plan(descs, n_params, opts, 256, &plan.p, &err);
+  } catch (const std::bad_alloc&) {
+    return fail(MUON_ERR_OOM, "host memory for the plan");
+  }
+  if (rc != MUON_OK) return fail(rc, "%s", err.c_str());
+  const muon::Plan& p = plan.p;
+  if (p.ws_total > muon::kScratchBytes)
+    return fail(MUON_ERR_UNSUPPORTED,
+                "muon_step_noalloc: these parameters need %llu bytes of scratch, the fixed array holds %llu "
+                "(use a plan)",
+                (unsigned long long)p.ws_total, (unsigned long long)muon::kScratchBytes);
+  if ((reinterpret_cast<uintptr_t>(device_error) & 3) != 0)
+    return fail(MUON_ERR_INVALID_ARGUMENT, "device_error is not 4-byte aligned");
+  const int bad = check_step_args(p, params, grads, momentum, lr, beta, ns_steps, a, b, c);
+  if (bad != MUON_OK) return bad;
+
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = muon::scratch_address(dev, &plan.ws);
+  if (e != hipSuccess) return hip_fail(e, "address of the fixed scratch");
+  plan.device = dev;
+  plan.err_word = device_error ? device_error : at<uint32_t>(&plan, p.off_err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // The tables this step's kernels read, built on the host with the
+  // scratch's addresses; the pointer table last.
+  std::vector<Upload> ups;
+  if (!device_tables(&plan, &ups)) return fail(MUON_ERR_OOM, "host memory for the tables");
+  try {
+    std::vector<muon::PtrEntry> ptrs(p.n_params);
+    for (int i = 0; i < p.n_params; ++i) {
+      ptrs[i].w = params[i];
+      ptrs[i].g = grads[i];
+      ptrs[i].m = static_cast<float*>(momentum[i]);
+    }
+    add_upload(&ups, p.off_ptrs, ptrs);
+  } catch (const std::bad_alloc&) {
+    return fail(MUON_ERR_OOM, "host memory for the tables");
+  }
+  // The scratch keeps whatever the last call on this device left: clear the
+  // part this step uses (the streamed path relies on zero padding, the
+  // error word starts at zero), then write the tables.  The copies read
+  // pageable host memory, which the runtime consumes before returning.
+  e = muon::launch_fill_zero(plan.ws, p.ws_total, s);
+  if (e != hipSuccess) return hip_fail(e, "clearing the scratch");
+  for (const Upload& u : ups) {
+    e = hipMemcpyAsync(plan.ws + u.off, u.bytes.data(), u.bytes.size(), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "table upload");
+  }
+  const muon::DevScalars v = step_scalars(p, lr, beta, ns_steps, a, b, c);
+  e = enqueue_buckets(&plan, ns_steps, s, false, &v);
+  if (e != hipSuccess) return hip_fail(e, "launch");
+  g_last_error.clear();
+  return MUON_OK;
 }
 
 int muon_plan_status(muon_plan_t plan, uint32_t* device_error) {

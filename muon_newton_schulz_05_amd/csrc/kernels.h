@@ -11,6 +11,14 @@ namespace muon {
 // Writes the step's scalars.
 hipError_t launch_prologue(DevScalars* dst, const DevScalars& v, hipStream_t s);
 
+// ---------------------------------------------------------------- fixed scratch (muon_step_noalloc)
+constexpr uint64_t kScratchBytes = MUON_NOALLOC_SCRATCH_BYTES;
+// Device address of the fixed scratch array on `device` (looked up once per
+// device, then cached).
+hipError_t scratch_address(int device, char** out);
+// Zero `bytes` (a multiple of 16) at p with a kernel on s.
+hipError_t launch_fill_zero(void* p, uint64_t bytes, hipStream_t s);
+
 // ---------------------------------------------------------------- skinny (m <= 32)
 // The first kernel of an eager step carries the step's scalars by value and
 // writes them to the plan's scalar block for the kernels after it (sc_out

@@ -350,3 +350,27 @@ def test_overlong_slices_leave_the_large_tile_products(m):
     assert info["launches_per_ns"] == 3 + 3  # its own three launches + the grouped large launches
     buckets, _ = _tables([(600, (1 << 23) - 256, 1)])
     assert [b[:2] for b in buckets] == [(600, (1 << 23) - 256)]
+
+
+def test_noalloc_checks_on_the_host_before_any_device_call(m):
+    """muon_step_noalloc refuses a step larger than its fixed scratch, and the
+    options that need a plan, before touching any device (so this runs
+    without a GPU)."""
+    lib = m.load_library()
+    P = ctypes.c_void_p * 1
+    ptr = P(16)
+    big = m.make_descs([(4096, 4096)], ["f32"], ["bf16"])
+    assert lib.muon_step_noalloc(big, 1, ctypes.byref(m.make_opts()), ptr, ptr, ptr, 0.02, 0.95, 5,
+                                 *workloads.QUINTIC, None, None) == 2
+    assert "scratch" in m.muon_last_error()
+    small = m.make_descs([(24, 100)], ["f32"], ["bf16"])
+    for kw in (dict(use_graph=True), dict(timing=True)):
+        assert lib.muon_step_noalloc(small, 1, ctypes.byref(m.make_opts(**kw)), ptr, ptr, ptr, 0.02, 0.95, 5,
+                                     *workloads.QUINTIC, None, None) == 1
+    assert lib.muon_step_noalloc(m.make_descs([(2, 2, 2, 2)]), 1, None, ptr, ptr, ptr, 0.02, 0.95, 5,
+                                 *workloads.QUINTIC, None, None) == 1
+    # A step that fits but has a misaligned pointer is refused before any launch.
+    bad = P(8)
+    assert lib.muon_step_noalloc(small, 1, None, bad, bad, bad, 0.02, 0.95, 5, *workloads.QUINTIC, None,
+                                 None) == 1
+    assert m.MUON_NOALLOC_SCRATCH_BYTES == 64 << 20
