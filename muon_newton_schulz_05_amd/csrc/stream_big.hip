@@ -12,7 +12,8 @@
 //            A^2 = E E + diag(d) A + A diag(d) - diag(d)^2,
 //          where only E E runs on the matrix cores; R is rounded to bf16;
 //   apply  X' = s (X + R X) = s (a X + (b A + c A^2) X); the X term is added
-//          in float32 in the epilogue (bf16 X is exact in float32).
+//          to the float32 accumulators from the X^T operand slices already
+//          in LDS (bf16 X is exact in float32), so the epilogue reads no X.
 //
 // Keeping the diagonal out of the bf16 operands and shifting the polynomial by
 // the identity leaves bf16 rounding only on the small off-diagonal part of A
@@ -209,6 +210,33 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
     __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
   };
 
+  // Epi::kAddX (X + R X, second operand X^T): the k-slices whose k range is
+  // this tile's own row range hold X at exactly the entries of the output
+  // tile (B-stage row j, k = i holds X[i][j]), so the waves whose rows they
+  // are add them to their accumulators and the epilogue reads no X.  Slice
+  // kt covers tile rows 64 (kt mod 4) .. + 63, rows 64 (kt mod 2) .. + 63 of
+  // the waves with wm = (kt mod 4) / 2: their 32-row blocks I0 = 2 (kt mod 2)
+  // and I0 + 1.  Register 4 q + e of block I0 + ii is row
+  // 32 ii + 8 q + 4 (l / 32) + e of the slice, column l mod 32: four
+  // consecutive k of B-stage row rb + 32 j, one 8-byte read.  (I0 is a
+  // constant, so the accumulators stay in registers.)
+  auto add_x = [&](const char* st, auto i0_tag) {
+    constexpr int I0 = decltype(i0_tag)::value;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = rb + 32 * j, ck = 4 * ii + q;
+          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(st + r * kRB + ((ck ^ swz(r)) << 4) + 8 * (lane >> 5));
+          acc[I0 + ii][j][4 * q + 0] += bf16_lo(v.x);
+          acc[I0 + ii][j][4 * q + 1] += bf16_hi(v.x);
+          acc[I0 + ii][j][4 * q + 2] += bf16_lo(v.y);
+          acc[I0 + ii][j][4 * q + 3] += bf16_hi(v.y);
+        }
+  };
+
   // kNS - 1 slices in flight.  Iteration kt: wait for this wave's loads of
   // slice kt; one barrier then says that every wave's part of slice kt is in
   // LDS and that every wave has finished reading slice kt - 1, whose stage is
@@ -224,6 +252,12 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // no LDS access moves across the barrier
     if (kt + kNS - 1 < nk) issue(kt + kNS - 1, stage == 0 ? kNS - 1 : stage - 1);
+    if constexpr (Epi::kAddX) {
+      if ((kt >> 2) == tm && wm == ((kt & 3) >> 1)) {
+        if (kt & 1) add_x(lds + stage * kStage, std::integral_constant<int, 2>{});
+        else add_x(lds + stage * kStage, std::integral_constant<int, 0>{});
+      }
+    }
     multiply(lds + stage * kStage);
     stage = stage == kNS - 1 ? 0 : stage + 1;
   }
@@ -391,6 +425,7 @@ struct GramPhase {
   // The transposed tile of E comes from LDS; A itself is stored only for
   // tiles on or above the diagonal, the only ones the polynomial reads.
   static constexpr bool kMirror = true;
+  static constexpr bool kAddX = false;
   struct Aux {};
   static constexpr int kBatch = 32, kBatchLast = 0;
   static __device__ Aux load(const Ctx&, int, int, int) { return Aux{}; }
@@ -436,6 +471,7 @@ struct PolyPhase {
   // R is symmetric: its transposed tile comes from LDS, so A is read only
   // on and above the diagonal.
   static constexpr bool kMirror = true;
+  static constexpr bool kAddX = false;
   static __device__ void store_t(const Ctx& x, int r, int c, u32x4_t v) {
     *reinterpret_cast<MUON_GLOBAL u32x4_t*>(as_global(x.r16 + (int64_t)r * x.mp + c)) = v;
   }
@@ -470,19 +506,20 @@ struct PolyPhase {
 };
 
 // Operands of R X: rows of R and rows of X^T (both contiguous along k = m).
+// The X term of X + R X is added to the accumulators from the X^T slices in
+// LDS (kAddX), so neither epilogue reads X.
 __device__ __forceinline__ Operands apply_operands(const BigArgs& g, const BigBucket& bb, int z) {
   return Operands{reinterpret_cast<const char*>(bb.r16 + (int64_t)z * bb.mp * bb.mp),
                   bb.xt[g.src] + (int64_t)z * bb.np * bb.mp * 2, bb.mp, bb.mp, big_k_over_m(bb.m)};
 }
 
 // X' = s (X + R X): X' [mp][np] from the row view, X'^T [np][mp] written
-// from LDS (the same values), so only the old X is read.
+// from LDS (the same values).
 struct ApplyPhase {
   static __device__ Operands operands(const BigArgs& g, const BigBucket& bb, int z) {
     return apply_operands(g, bb, z);
   }
   struct Ctx {
-    const uint16_t* x_old;
     uint16_t* x_new;
     uint16_t* xt_new;
     int64_t mp, np;
@@ -490,24 +527,19 @@ struct ApplyPhase {
   };
   static __device__ Ctx context(const BigArgs& g, const BigBucket& bb, int z) {
     const int64_t o = (int64_t)z * bb.mp * bb.np * 2;
-    return Ctx{reinterpret_cast<const uint16_t*>(bb.x[g.src] + o),
-               reinterpret_cast<uint16_t*>(bb.x[g.src ^ 1] + o),
-               reinterpret_cast<uint16_t*>(bb.xt[g.src ^ 1] + o), bb.mp, bb.np,
-               g.first ? bb.scale[2 * z] : 1.f};
+    return Ctx{reinterpret_cast<uint16_t*>(bb.x[g.src ^ 1] + o), reinterpret_cast<uint16_t*>(bb.xt[g.src ^ 1] + o),
+               bb.mp, bb.np, g.first ? bb.scale[2 * z] : 1.f};
   }
-  static __device__ float prescale(const Ctx&) { return 1.f; }
+  static __device__ float prescale(const Ctx& x) { return x.pre; }
   static __device__ int views(const Ctx&, bool) { return kViewRow | kViewCol; }
   static constexpr bool kMirror = true;
-  using Aux = u32x2_t;  // old X (r, c .. c+3), bf16
-  static constexpr int kBatch = 8, kBatchLast = 0;
-  static __device__ Aux load(const Ctx& x, int, int r, int c) {
-    return *reinterpret_cast<const MUON_GLOBAL u32x2_t*>(as_global(x.x_old + (int64_t)r * x.np + c));
-  }
-  static __device__ f32x4_t store(const Ctx& x, int, int r, int c, f32x4_t v, Aux o) {
-    const f32x4_t y{x.pre * (v.x + bf16_lo(o.x)), x.pre * (v.y + bf16_hi(o.x)), x.pre * (v.z + bf16_lo(o.y)),
-                    x.pre * (v.w + bf16_hi(o.y))};
-    st_bf16x4(x.x_new + (int64_t)r * x.np + c, y);
-    return y;
+  static constexpr bool kAddX = true;
+  struct Aux {};
+  static constexpr int kBatch = 32, kBatchLast = 0;
+  static __device__ Aux load(const Ctx&, int, int, int) { return Aux{}; }
+  static __device__ f32x4_t store(const Ctx& x, int, int r, int c, f32x4_t v, Aux) {
+    st_bf16x4(x.x_new + (int64_t)r * x.np + c, v);
+    return v;
   }
   static __device__ void store_t(const Ctx& x, int r, int c, u32x4_t v) {
     *reinterpret_cast<MUON_GLOBAL u32x4_t*>(as_global(x.xt_new + (int64_t)r * x.mp + c)) = v;
@@ -523,9 +555,7 @@ struct FinalPhase {
   }
   struct Ctx {
     char* w;
-    const uint16_t* xo;  // X (row view) or X^T (column view) of this round
     int64_t rows, len;   // stored rows and row length of the slice
-    int64_t xstride;     // row stride of xo
     int pdtype, view, vec;
     float k;             // lr f s
     float decay;         // lr wd
@@ -535,10 +565,7 @@ struct FinalPhase {
     const PtrEntry pe = g.ptrs[d.param];
     Ctx x;
     x.w = static_cast<char*>(pe.w) + d.slice_off * (d.pdtype == 1 ? 2 : 4);
-    const int64_t o = (int64_t)z * bb.mp * bb.np * 2;
     x.view = d.transposed ? kViewCol : kViewRow;
-    x.xo = reinterpret_cast<const uint16_t*>((d.transposed ? bb.xt[g.src] : bb.x[g.src]) + o);
-    x.xstride = d.transposed ? bb.mp : bb.np;
     x.rows = d.transposed ? bb.n : bb.m;
     x.len = d.transposed ? bb.m : bb.n;
     x.pdtype = d.pdtype;
@@ -550,16 +577,15 @@ struct FinalPhase {
   static __device__ float prescale(const Ctx&) { return 1.f; }
   static __device__ int views(const Ctx& x, bool) { return x.view; }
   static constexpr bool kMirror = false;
+  static constexpr bool kAddX = true;
   static __device__ void store_t(const Ctx&, int, int, u32x4_t) {}  // no transposed copy
   struct Aux {
     f32x4_t w;   // W (r, c .. c+3) as float32 (entries past the row end unused)
-    u32x2_t xo;  // old X in this view, bf16
   };
   static constexpr int kBatch = 4, kBatchLast = 0;
   static __device__ Aux load(const Ctx& x, int, int r, int c) {
     Aux q{};
     if (r >= x.rows || c >= x.len) return q;
-    q.xo = *reinterpret_cast<const MUON_GLOBAL u32x2_t*>(as_global(x.xo + (int64_t)r * x.xstride + c));
     const int64_t idx = (int64_t)r * x.len + c;
     if (x.vec && c + 3 < x.len) {
       if (x.pdtype == 1) {  // bfloat16 W
@@ -578,10 +604,8 @@ struct FinalPhase {
   }
   static __device__ f32x4_t store(const Ctx& x, int, int r, int c, f32x4_t v, const Aux& q) {
     if (r >= x.rows || c >= x.len) return v;
-    const f32x4_t n{q.w.x - x.decay * q.w.x - x.k * (v.x + bf16_lo(q.xo.x)),
-                    q.w.y - x.decay * q.w.y - x.k * (v.y + bf16_hi(q.xo.x)),
-                    q.w.z - x.decay * q.w.z - x.k * (v.z + bf16_lo(q.xo.y)),
-                    q.w.w - x.decay * q.w.w - x.k * (v.w + bf16_hi(q.xo.y))};
+    const f32x4_t n{q.w.x - x.decay * q.w.x - x.k * v.x, q.w.y - x.decay * q.w.y - x.k * v.y,
+                    q.w.z - x.decay * q.w.z - x.k * v.z, q.w.w - x.decay * q.w.w - x.k * v.w};
     const int64_t idx = (int64_t)r * x.len + c;
     if (x.vec && c + 3 < x.len) {
       if (x.pdtype == 1) {  // bfloat16 W, rounded to nearest even
