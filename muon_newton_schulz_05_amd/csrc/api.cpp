@@ -143,6 +143,36 @@ bool device_tables(muon_plan_t plan, std::vector<Upload>* ups) try {
     plan->skinny_b0 = sbs[0];
     add_upload(ups, p.off_skinny_params, sbs);
   }
+  if (!p.small.empty()) {
+    std::vector<muon::SmallBucket> sbs;
+    int64_t t0[3] = {0, 0, 0};
+    for (int b : p.small) {
+      const muon::BucketPlan& bp = p.buckets[b];
+      muon::SmallBucket sb{};
+      sb.mats = at<muon::DevMat>(plan, bp.off_mats);
+      for (int i = 0; i < 2; ++i) {
+        sb.x[i] = plan->ws + bp.off_x[i];
+        sb.xt[i] = plan->ws + bp.off_xt[i];
+      }
+      sb.a32 = at<float>(plan, bp.off_a32);
+      sb.phi = plan->ws + bp.off_phi;
+      sb.plo = bp.p_hilo ? at<uint16_t>(plan, bp.off_plo) : nullptr;
+      sb.scale = at<float>(plan, bp.off_scale);
+      sb.m = bp.m;
+      sb.n = bp.n;
+      sb.mp = bp.mp;
+      sb.np = bp.np;
+      sb.count = (int32_t)bp.slices.size();
+      const int64_t ti = bp.mp / muon::kSmallTile, tj = bp.np / muon::kSmallTile;
+      const int64_t per[3] = {ti * ti, ti * ti, ti * tj};
+      for (int ph = 0; ph < 3; ++ph) {
+        sb.t0[ph] = (int32_t)t0[ph];
+        t0[ph] += per[ph] * sb.count;
+      }
+      sbs.push_back(sb);
+    }
+    add_upload(ups, p.off_small_params, sbs);
+  }
   if (!p.big.empty()) {
     std::vector<muon::BigBucket> bbs;
     for (int b : p.big) {
@@ -214,6 +244,33 @@ hipError_t enqueue_skinny(muon_plan_t plan, hipStream_t s, bool timing, const mu
   return timed(plan, muon::kClsSkinnyApply, s, timing, [&] { return muon::launch_skinny_apply(L, s); });
 }
 
+// Newton-Schulz rounds of all small streamed buckets: one launch per
+// product phase and round over all of them.
+hipError_t enqueue_small_rounds(muon_plan_t plan, int ns, hipStream_t s, bool timing) {
+  const muon::Plan& p = plan->p;
+  muon::SmallArgs g{};
+  g.buckets = at<muon::SmallBucket>(plan, p.off_small_params);
+  g.nb = (int)p.small.size();
+  g.sc = at<muon::DevScalars>(plan, p.off_scalars);
+  g.ptrs = at<muon::PtrEntry>(plan, p.off_ptrs);
+  const bool f32 = p.mode == MUON_MODE_FP32;
+  hipError_t e;
+  for (int it = 0; it < ns; ++it) {
+    g.src = it & 1;
+    g.first = it == 0;
+    if ((e = timed(plan, muon::kClsGram, s, timing,
+                   [&] { return muon::launch_small(0, false, f32, g, p.small_wgs[0], s); })) != hipSuccess)
+      return e;
+    if ((e = timed(plan, muon::kClsPoly, s, timing,
+                   [&] { return muon::launch_small(1, false, f32, g, p.small_wgs[1], s); })) != hipSuccess)
+      return e;
+    if ((e = timed(plan, muon::kClsApply, s, timing,
+                   [&] { return muon::launch_small(2, it == ns - 1, f32, g, p.small_wgs[2], s); })) != hipSuccess)
+      return e;
+  }
+  return hipSuccess;
+}
+
 // Newton-Schulz rounds of all large bf16 buckets: one launch per product
 // phase and round, each walking its tile table across the buckets.
 hipError_t enqueue_big_rounds(muon_plan_t plan, int ns, hipStream_t s, bool timing) {
@@ -280,7 +337,7 @@ hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, 
     muon::Update0Launch u{mats, ptrs, sc, scale, bp.m, bp.n, cnt};
     return timed(plan, muon::kClsUpdate, s, timing, [&] { return muon::launch_update0(u, s); });
   }
-  if (bp.big) return hipSuccess;  // rounds run grouped over all large buckets
+  if (bp.big || bp.small) return hipSuccess;  // rounds run grouped over all large (small) buckets
   for (int it = 0; it < ns; ++it) {
     const int src = it & 1, dst = src ^ 1;
     const float* sfirst = it == 0 ? scale : nullptr;
@@ -343,6 +400,10 @@ hipError_t enqueue_buckets(muon_plan_t plan, int ns, hipStream_t s, bool timing,
     hipError_t e = enqueue_stream(plan, bp, ns, s, timing, first);
     if (e != hipSuccess) return e;
     first = nullptr;
+  }
+  if (!plan->p.small.empty() && ns > 0) {
+    hipError_t e = enqueue_small_rounds(plan, ns, s, timing);
+    if (e != hipSuccess) return e;
   }
   if (!plan->p.big.empty() && ns > 0) return enqueue_big_rounds(plan, ns, s, timing);
   return hipSuccess;

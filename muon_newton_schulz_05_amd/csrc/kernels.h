@@ -110,6 +110,22 @@ struct ApplyLaunch {
 };
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
 
+// ---------------------------------------------------------------- streamed, small buckets (grouped)
+// One launch per product phase covers every bucket with padded m <=
+// kSmallMaxMp (32 x 32 output tiles, the contraction split over 4 waves).
+struct SmallArgs {
+  const SmallBucket* buckets;
+  int nb;
+  int src;                // this round reads X[src], X^T[src]
+  int first;              // first round: fold the normalisation scale in
+  const DevScalars* sc;
+  const PtrEntry* ptrs;
+};
+// phase 0 gram, 1 poly, 2 apply (final_round: W update); f32_operands: fp32
+// mode (else bf16 X and a bf16 hi/lo P).  wgs: workgroups of the phase.
+hipError_t launch_small(int phase, bool final_round, bool f32_operands, const SmallArgs& a, int64_t wgs,
+                        hipStream_t s);
+
 // ---------------------------------------------------------------- streamed, large bf16 buckets
 // One launch per product phase covers every large bucket; the tile table
 // (entries: bucket, slice, 256 x 256 output tile) fixes the order.

@@ -22,6 +22,8 @@ constexpr int64_t kBigMaxN = int64_t(1) << 23;
 inline constexpr int64_t big_k_over_m(int64_t d) { return (d + kBigKStep - 1) / kBigKStep * kBigKStep; }
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;  // tile-table padding entry
 constexpr int kMomTile = 64;          // momentum kernel tile (oriented 64 x 64)
+constexpr int kSmallMaxMp = 256;      // streamed buckets with padded m <= this: grouped 32 x 32 products
+constexpr int kSmallTile = 32;        // their output tile
 
 enum KernelClass { kClsSkinnyGram = 0, kClsSkinnyPoly, kClsSkinnyApply, kClsMomentum, kClsNorm,
                    kClsGram, kClsPoly, kClsApply, kClsUpdate, kNumClasses };
@@ -73,6 +75,22 @@ struct SkinnyBucket {
 struct BigTile {
   uint32_t bz;  // bucket << 24 | slice; kNoTile marks padding
   uint32_t mn;  // tm | tn << 16 (256 x 256 output tiles)
+};
+
+// Device addresses of one small streamed bucket (padded m <= kSmallMaxMp).
+// Each product phase of a round is one launch over every such bucket;
+// workgroup b belongs to the last bucket with t0[phase] <= b.
+struct SmallBucket {
+  const DevMat* mats;  // slice table
+  char* x[2];          // X ping-pong, [count][mp][np] (bf16 or float)
+  char* xt[2];         // X^T ping-pong, [count][np][mp]
+  float* a32;          // A, [count][mp][mp]
+  char* phi;           // P (float), or its bf16 high part
+  uint16_t* plo;       // bf16 low part of P (bf16 mode), else null
+  float* scale;        // [count][2] = {s, s^2}
+  int64_t m, n, mp, np;
+  int32_t count;
+  int32_t t0[3];       // first workgroup of the bucket in the gram, poly and apply launches
 };
 
 // Device addresses of one large bucket's workspace (filled at plan creation).

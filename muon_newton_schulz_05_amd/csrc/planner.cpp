@@ -217,8 +217,12 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
       bp.off_sq = ws.take(cnt * bp.km_tiles * sizeof(float));
       bp.off_scale = ws.take(cnt * 2 * sizeof(float));
       if (bp.big) bp.off_dg = ws.take(cnt * bp.mp * sizeof(float));
+      // Padded m <= kSmallMaxMp: 32 x 32 tile products, grouped over all such
+      // buckets.  The choice depends on the shape alone, so a slice's
+      // arithmetic does not depend on the plan it sits in.
+      bp.small = !bp.big && bp.mp <= kSmallMaxMp;
       p.launches_fixed += 2;   // momentum, norm
-      if (!bp.big) p.launches_per_ns += 3;  // gram, poly, apply (the last apply also updates W)
+      if (!bp.big && !bp.small) p.launches_per_ns += 3;  // gram, poly, apply (the last apply also updates W)
     }
     bp.ws_bytes = ws.take(0) - bp.ws_begin;
   }
@@ -240,6 +244,24 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
   if (!p.skinny.empty()) {
     p.launches_fixed += 3;
     p.off_skinny_params = ws.take(p.skinny.size() * sizeof(SkinnyBucket));
+  }
+  // Small streamed buckets share one launch per product phase.
+  for (int b = 0; b < (int)p.buckets.size(); ++b) {
+    const BucketPlan& bp = p.buckets[b];
+    if (!bp.small) continue;
+    p.small.push_back(b);
+    const int64_t ti = bp.mp / kSmallTile, tj = bp.np / kSmallTile, cnt = (int64_t)bp.slices.size();
+    p.small_wgs[0] += cnt * ti * ti;
+    p.small_wgs[1] += cnt * ti * ti;
+    p.small_wgs[2] += cnt * ti * tj;
+  }
+  if (!p.small.empty()) {
+    if (p.small_wgs[2] >= (int64_t(1) << 31)) {
+      *err = "too many small product tiles in one plan";
+      return MUON_ERR_UNSUPPORTED;
+    }
+    p.launches_per_ns += 3;
+    p.off_small_params = ws.take(p.small.size() * sizeof(SmallBucket));
   }
   // Large buckets share one launch per product phase.
   for (int b = 0; b < (int)p.buckets.size(); ++b)

@@ -38,6 +38,7 @@ struct BucketPlan {
 
   // streamed path
   bool big = false;         // bf16 mode and m >= kBigMinM: 256 x 256 tile products
+  bool small = false;       // padded m <= kSmallMaxMp: grouped 32 x 32 tile products
   int64_t mp = 0, np = 0;   // padded dims
   int x_bytes = 0;          // X element size (2: bf16, 4: fp32)
   bool poly_f32 = false;    // A^2 from float32 A (else bf16 copy of A)
@@ -78,6 +79,11 @@ struct Plan {
   int skinny_items = 0, skinny_slices = 0, skinny_m_max = 0;
   std::vector<BigTile> big_tab[3];
   uint64_t off_big_tab[3] = {0, 0, 0};
+  // Small streamed buckets: their indices, the device SmallBucket array and
+  // the workgroups of each grouped phase launch (gram, poly, apply).
+  std::vector<int> small;
+  uint64_t off_small_params = 0;
+  int64_t small_wgs[3] = {0, 0, 0};
   uint64_t ws_total = 0;
   int launches_fixed = 0, launches_per_ns = 0;
 };

@@ -418,6 +418,172 @@ __global__ __launch_bounds__(256) void k_update0(Update0Launch a) {
   }
 }
 
+// ------------------------------------------------------------------ small products, grouped
+// Buckets whose padded m is at most kSmallMaxMp (m <= 256): every product
+// phase of a round is one launch over all of them.  One 32 x 32 output tile
+// per 256-thread workgroup; the contraction is split over the four waves:
+// wave w takes k = 32 w .. 32 w + 31 of every 128-wide chunk, and the four
+// partial sums are added in the fixed order ((w0 + w1) + w2) + w3.  The
+// tile and the split depend on the slice's shape alone, so fused and
+// single-slice runs give the same bits.  Chunks are double-buffered through
+// registers into LDS; 16-byte chunk c of tile row r sits in slot c ^ (r mod 8),
+// so the 16-byte fragment reads of 8 consecutive rows hit distinct banks.
+constexpr int kSmCK = 128;  // k elements per chunk (every padded dimension is a multiple of 128)
+
+template <int Ph>
+__device__ __forceinline__ int64_t small_tiles_j(const SmallBucket& b) {
+  return Ph == 2 ? b.np / kSmallTile : b.mp / kSmallTile;
+}
+
+// Ph: 0 gram (A = s2 X X^T), 1 poly (P = b A + c A A), 2 apply (X' = s (a X + P X)),
+// 3 the last round's apply, which updates W.  T: the operand element type.
+template <typename T, int Ph>
+__global__ __launch_bounds__(256) void k_small(SmallArgs g) {
+  constexpr int ES = (int)sizeof(T);
+  constexpr int RB = kSmCK * ES;            // bytes of one tile row per chunk
+  constexpr int CPR = RB / 16;              // 16-byte chunks per row
+  constexpr int H = kSmallTile * CPR / 256; // 16-byte pieces per thread, operand and chunk
+  constexpr int PH = Ph == 3 ? 2 : Ph;      // tile grid of the phase
+  __shared__ __attribute__((aligned(16))) char lds[2][2][kSmallTile * RB];
+
+  // The workgroup's bucket: the last one whose first workgroup is <= b.
+  const int wg = blockIdx.x;
+  int lo = 0, hi = g.nb - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (g.buckets[mid].t0[PH] <= wg) lo = mid;
+    else hi = mid - 1;
+  }
+  const SmallBucket bk = g.buckets[lo];
+  // The round's ping-pong buffers, chosen without indexing a local array by
+  // a run-time value (which would put the bucket in scratch memory).
+  char* const x_src = g.src ? bk.x[1] : bk.x[0];
+  char* const x_dst = g.src ? bk.x[0] : bk.x[1];
+  char* const xt_src = g.src ? bk.xt[1] : bk.xt[0];
+  char* const xt_dst = g.src ? bk.xt[0] : bk.xt[1];
+  const int64_t tj_n = small_tiles_j<PH>(bk), ti_n = bk.mp / kSmallTile;
+  const int64_t local = wg - bk.t0[PH];
+  const int z = (int)(local / (ti_n * tj_n));
+  const int64_t t = local - (int64_t)z * ti_n * tj_n;
+  const int ti = (int)(t / tj_n), tj = (int)(t - (t / tj_n) * tj_n);
+
+  // Operands: rows of A and of B, both contiguous along k.
+  const char *a, *a2 = nullptr, *b;
+  int64_t ld, K;
+  if constexpr (Ph == 0) {
+    a = b = x_src + (int64_t)z * bk.mp * bk.np * ES;
+    ld = bk.np;
+    K = bk.np;
+  } else if constexpr (Ph == 1) {
+    a = b = reinterpret_cast<const char*>(bk.a32 + (int64_t)z * bk.mp * bk.mp);
+    ld = bk.mp;
+    K = bk.mp;
+  } else {
+    a = bk.phi + (int64_t)z * bk.mp * bk.mp * ES;
+    if (bk.plo) a2 = reinterpret_cast<const char*>(bk.plo + (int64_t)z * bk.mp * bk.mp);
+    b = xt_src + (int64_t)z * bk.np * bk.mp * ES;
+    ld = bk.mp;
+    K = bk.mp;
+  }
+  const char* A = a + (int64_t)ti * kSmallTile * ld * ES;
+  const char* A2 = a2 ? a2 + (int64_t)ti * kSmallTile * ld * ES : nullptr;
+  const char* B = b + (int64_t)tj * kSmallTile * ld * ES;
+  const int nk = (int)(K / kSmCK);
+  const int total = A2 ? 2 * nk : nk;  // with a bf16 hi/lo pair: the hi part's chunks, then the lo part's
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  u32x4_t ra[H], rb[H];
+  auto gload = [&](int it) {
+    const int kt = it % nk;
+    const char* Ab = it >= nk ? A2 : A;
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const int p = tid + 256 * h, row = p / CPR, c = p % CPR;
+      const int64_t off = (int64_t)row * ld * ES + (int64_t)kt * RB + c * 16;
+      ra[h] = *reinterpret_cast<const MUON_GLOBAL u32x4_t*>(as_global(Ab + off));
+      rb[h] = *reinterpret_cast<const MUON_GLOBAL u32x4_t*>(as_global(B + off));
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const int p = tid + 256 * h, row = p / CPR, c = p % CPR;
+      const int slot = row * RB + ((c ^ (row & 7)) << 4);
+      *reinterpret_cast<u32x4_t*>(&lds[buf][0][slot]) = ra[h];
+      *reinterpret_cast<u32x4_t*>(&lds[buf][1][slot]) = rb[h];
+    }
+  };
+  // 16-byte fragment of row r at logical chunk c.
+  auto frag = [&](const char* st, int r, int c) {
+    return *reinterpret_cast<const u32x4_t*>(st + r * RB + ((c ^ (r & 7)) << 4));
+  };
+
+  f32x16_t acc = f32x16_t{};
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int r = lane & 31, half = lane >> 5;
+  for (int it = 0; it < total; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < total) gload(it + 1);
+    const char* As = lds[cur][0];
+    const char* Bs = lds[cur][1];
+    if constexpr (ES == 2) {
+      // 32 k per wave: two 32x32x16 products; lane l holds k 8 (l/32) .. + 7 of each.
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int c = 4 * wave + 2 * s2 + half;
+        const u32x4_t av = frag(As, r, c), bv = frag(Bs, r, c);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                      __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+      }
+    } else {
+      // 32 k per wave in 4 groups of 8: lane l reads 4 consecutive k (16 bytes)
+      // at 8 s4 + 4 (l/32); product e adds k 8 s4 + e (lanes 0-31) and
+      // 8 s4 + 4 + e (lanes 32-63).  A and B use the same k order.
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int c = 8 * wave + 2 * s4 + half;
+        const f32x4_t av = __builtin_bit_cast(f32x4_t, frag(As, r, c));
+        const f32x4_t bv = __builtin_bit_cast(f32x4_t, frag(Bs, r, c));
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bv.w, acc, 0, 0, 0);
+      }
+    }
+    if (it + 1 < total) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // The four waves' partial tiles, added in a fixed order.  Accumulator
+  // register q of lane l is row 8 (q/4) + 4 (l/32) + q mod 4, column l mod 32.
+  float* red = reinterpret_cast<float*>(&lds[0][0][0]);  // [wave][32][33], over both buffers
+  static_assert(4 * 32 * 33 * 4 <= (int)sizeof(lds), "the reduction buffer fits in the chunk buffers");
+#pragma unroll
+  for (int q = 0; q < 16; ++q) red[(wave * 32 + 8 * (q >> 2) + 4 * half + (q & 3)) * 33 + r] = acc[q];
+  __syncthreads();
+  const int col = tid & 31, i0 = 4 * (tid >> 5);
+  float v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = (i0 + u) * 33 + col;
+    v[u] = ((red[e] + red[32 * 33 + e]) + red[2 * 32 * 33 + e]) + red[3 * 32 * 33 + e];
+  }
+  const int gi = ti * kSmallTile + i0, gj = tj * kSmallTile + col;
+  if constexpr (Ph == 0) {
+    GramEpi{bk.a32, nullptr, g.first ? bk.scale : nullptr, bk.mp}(z, gi, gj, v);
+  } else if constexpr (Ph == 1) {
+    PolyEpi{bk.a32, bk.phi, bk.plo, bk.plo == nullptr, g.sc, bk.mp}(z, gi, gj, v);
+  } else if constexpr (Ph == 2) {
+    ApplyEpi<T>{reinterpret_cast<const T*>(x_src), reinterpret_cast<T*>(x_dst), reinterpret_cast<T*>(xt_dst),
+                g.first ? bk.scale : nullptr, g.sc, bk.mp, bk.np}(z, gi, gj, v);
+  } else {
+    FinalEpi<T>{reinterpret_cast<const T*>(x_src), g.first ? bk.scale : nullptr, g.sc, bk.mats, g.ptrs,
+                bk.mp, bk.np, bk.m, bk.n}(z, gi, gj, v);
+  }
+}
+
 template <typename T, class Epi>
 hipError_t run_gemm(GemmCore c, const Epi& e, int64_t rows, int64_t cols, int count, hipStream_t s) {
   // rows and cols are multiples of 128 (the workspace padding).
@@ -503,6 +669,24 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   ApplyEpi<float> e{static_cast<const float*>(a.x_old), static_cast<float*>(a.x_new),
                     static_cast<float*>(a.xt_new), a.scale, a.sc, a.mp, a.np};
   return run_gemm<float>(c, e, a.mp, a.np, a.count, s);
+}
+
+hipError_t launch_small(int phase, bool final_round, bool f32_operands, const SmallArgs& a, int64_t wgs,
+                        hipStream_t s) {
+  const dim3 grid((unsigned)wgs), block(256);
+  if (phase == 1) {
+    hipLaunchKernelGGL((k_small<float, 1>), grid, block, 0, s, a);  // A is float32 in both modes
+  } else if (phase == 0) {
+    if (f32_operands) hipLaunchKernelGGL((k_small<float, 0>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_small<uint16_t, 0>), grid, block, 0, s, a);
+  } else if (final_round) {
+    if (f32_operands) hipLaunchKernelGGL((k_small<float, 3>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_small<uint16_t, 3>), grid, block, 0, s, a);
+  } else {
+    if (f32_operands) hipLaunchKernelGGL((k_small<float, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_small<uint16_t, 2>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_update0(const Update0Launch& a, hipStream_t s) {

@@ -149,6 +149,22 @@ def test_skinny_buckets_share_three_launches(m):
     assert info["launches_fixed"] == 3 and info["launches_per_ns"] == 0
 
 
+def test_small_streamed_buckets_share_three_launches_per_round(m):
+    """Every streamed bucket with padded m <= 256 (m <= 256) runs each
+    product phase of a round in one launch with the others; a bucket with
+    larger m takes its own three launches, and the large bf16 buckets share
+    three more."""
+    shapes = [(100, 300), (200, 150), (64, 64), (3, 40, 500), (256, 1000)]
+    d = m.make_descs(shapes, ["f32"] * 5, ["bf16"] * 5)
+    for mode in ("bf16", "fp32"):
+        info = m.info_dict(m.muon_plan_describe(d, m.make_opts(mode=mode)))
+        assert [b["path"] for b in info["buckets"]] == ["stream"] * 5
+        assert info["launches_per_ns"] == 3, mode
+    mixed = m.make_descs(shapes + [(300, 520), (600, 700)], ["f32"] * 7, ["bf16"] * 7)
+    assert m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="bf16")))["launches_per_ns"] == 3 + 3 + 3
+    assert m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="fp32")))["launches_per_ns"] == 3 + 3 + 3
+
+
 def test_skinny_path_can_be_disabled(m):
     info = describe(m, workloads.WORKLOADS["fused_74x24x10240"], skinny_max_m=-1)
     assert info["buckets"][0]["path"] == "stream"
