@@ -111,17 +111,17 @@ def big_apply_bytes(wl: workloads.Workload) -> float:
     """Compulsory HBM bytes per launch of the large-tile apply class (k - 1
     apply launches and one final launch per step), over the slices with
     m > 512 in their padded workspace layout (multiples of 256): an apply
-    reads R (2 mp^2) and X^T, reads the old X and writes X' and X'^T (2 mp np
-    each); the final launch reads R, X^T and the old X and reads and writes W
-    (float32, 8 m n)."""
+    reads R (2 mp^2) and X^T and writes X' and X'^T (2 mp np each; the X term
+    comes from the X^T operand already on chip); the final launch reads R and
+    X^T and reads and writes W (float32, 8 m n)."""
     k = wl.ns_steps
     apply = final = 0.0
     for m, n in wl.oriented_matrices():
         if m <= 512:
             continue
         mp, np_ = -(-m // 256) * 256, -(-n // 256) * 256
-        apply += 2 * mp * mp + 8 * mp * np_
-        final += 2 * mp * mp + 4 * mp * np_ + 8 * m * n
+        apply += 2 * mp * mp + 6 * mp * np_
+        final += 2 * mp * mp + 2 * mp * np_ + 8 * m * n
     return ((k - 1) * apply + final) / k if k > 0 else 0.0
 
 
