@@ -400,8 +400,8 @@ def main():
     ap.add_argument("--also", default=",".join(EXTRA_WORKLOADS),
                     help="comma-separated workloads measured after the headline one and reported as "
                          "extra keys ('none': skip)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of float64 oracle time (0: skip)")
-    ap.add_argument("--cpu-budget-fp32", type=float, default=6.0, help="seconds of float32 oracle time")
+    ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of float64 oracle time (0: skip)")
+    ap.add_argument("--cpu-budget-fp32", type=float, default=3.0, help="seconds of float32 oracle time")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the copy/GEMM ceiling measurement")
     ap.add_argument("--copy-only", action="store_true",
