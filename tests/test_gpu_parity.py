@@ -278,6 +278,34 @@ def test_graph_replay_matches_eager():
         assert np.array_equal(x, y)
 
 
+def test_steps_on_two_streams_are_ordered():
+    """A step enqueued on another stream than the plan's previous step waits
+    for it (both use the plan's workspace): three steps alternating between
+    two streams, with no host synchronisation in between, give bitwise the W
+    and M of three steps on one stream (skinny, small and large buckets)."""
+    import torch
+
+    from muon_newton_schulz_05_amd import MuonPlan
+    shapes = [(24, 3000), (96, 300), (600, 700)]
+    params, grads, moms = make_inputs(shapes, "bf16", 141, w_std=0.02, m_std=1e-3)
+    outs = []
+    for alternate in (False, True):
+        p = [to_device(x, "cuda:0") for x in params]
+        g = [to_device(x, "cuda:0") for x in grads]
+        m = [to_device(x, "cuda:0") for x in moms]
+        torch.cuda.synchronize()
+        plan = MuonPlan(p, grad_dtypes=[x.dtype for x in g], mode="bf16")
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        for i in range(3):
+            st = (s2 if i % 2 else s1) if alternate else s1
+            plan.step(g, m, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q, stream=st)
+        plan.status()  # waits for the plan's last step
+        outs.append([to_host(x) for x in p + m])
+        plan.close()
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y)
+
+
 def test_step_rejects_bad_arguments_without_side_effects():
     import torch
 
