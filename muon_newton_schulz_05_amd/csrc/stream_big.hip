@@ -41,9 +41,10 @@
 // x-th stretch of the table.  Each stretch holds whole blocks of 4 x 8 tiles
 // (the 32 workgroups an XCD runs at once share 4 row and 8 column panels in
 // its L2), longest contraction first, with the work balanced over the XCDs.
-// Symmetric products (X X^T, E E) list only tiles on or above the diagonal;
-// the bf16 result of an off-diagonal tile is also written to its mirror
-// position.  The epilogue turns the accumulators around in LDS and writes
+// Symmetric products (X X^T, E E) list only tiles on or above the diagonal
+// and compute their mirrors below it; the bf16 result of an off-diagonal tile
+// is also written to its mirror position.  Waves whose rows all lie past m
+// skip their products.  The epilogue turns the accumulators around in LDS and writes
 // whole rows of 16-byte pieces.  Where a transposed copy holds the same values
 // (the mirror tiles, and X'^T next to X'), it is read out of LDS after the
 // row-view results, so the side inputs of the epilogue are read only once.
@@ -121,7 +122,12 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   if (t.bz == kNoTile) return;  // uniform over the workgroup, before any barrier
   const BigBucket& bb = g.buckets[t.bz >> 24];  // read in place: fields are indexed by round parity
   const int z = (int)(t.bz & 0xFFFFFFu);
-  const int tm = (int)(t.mn & 0xFFFFu), tn = (int)(t.mn >> 16);
+  // The table lists a symmetric product's tiles on and above the diagonal;
+  // Epi::kLower phases compute the mirror tile below it instead (the
+  // transposed copy goes out through the mirror writes), so that a padded
+  // last tile row, not column, holds the rows past m.
+  const int t_i = (int)(t.mn & 0xFFFFu), t_j = (int)(t.mn >> 16);
+  const int tm = Epi::kLower ? t_j : t_i, tn = Epi::kLower ? t_i : t_j;
   const Operands op = Epi::operands(g, bb, z);
   // The epilogue's context (table reads for the final phase) is fetched
   // here, so its loads complete during the products.
@@ -131,6 +137,13 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   // The wave index is uniform over the wave; saying so keeps branches on it scalar.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;  // 128 rows x 64 columns per wave
+  // Every product is zero in its rows past m: X and E are zero there, and R
+  // holds only its identity shift there, which meets rows of X that are
+  // zero.  A wave whose 128 rows all lie past m therefore skips its
+  // products, and its accumulators keep the zero they would give.  Those
+  // waves (4..7) sit one on each SIMD, so every matrix core of a half-padded
+  // tile runs half loaded.
+  const bool idle = wm == 1 && bb.m - (int64_t)tm * kBigTile <= 128;
   const char* A = op.a + (int64_t)tm * kBigTile * op.lda * 2;
   const char* B = op.b + (int64_t)tn * kBigTile * op.ldb * 2;
   const int nk = (int)(op.K / kBK);
@@ -258,7 +271,7 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
         else add_x(lds + stage * kStage, std::integral_constant<int, 0>{});
       }
     }
-    multiply(lds + stage * kStage);
+    if (!idle) multiply(lds + stage * kStage);
     stage = stage == kNS - 1 ? 0 : stage + 1;
   }
   __syncthreads();  // every wave is done with the stages before they hold the epilogue
@@ -423,8 +436,9 @@ struct GramPhase {
   static __device__ float prescale(const Ctx& x) { return x.pre; }
   static __device__ int views(const Ctx&, bool diag) { return diag ? kViewRow : kViewRow | kViewCol; }
   // The transposed tile of E comes from LDS; A itself is stored only for
-  // tiles on or above the diagonal, the only ones the polynomial reads.
+  // tiles on or below the diagonal, the only ones the polynomial reads.
   static constexpr bool kMirror = true;
+  static constexpr bool kLower = true;
   static constexpr bool kAddX = false;
   struct Aux {};
   static constexpr int kBatch = 32, kBatchLast = 0;
@@ -469,8 +483,9 @@ struct PolyPhase {
   static __device__ float prescale(const Ctx&) { return 1.f; }
   static __device__ int views(const Ctx&, bool diag) { return diag ? kViewRow : kViewRow | kViewCol; }
   // R is symmetric: its transposed tile comes from LDS, so A is read only
-  // on and above the diagonal.
+  // on and below the diagonal.
   static constexpr bool kMirror = true;
+  static constexpr bool kLower = true;
   static constexpr bool kAddX = false;
   static __device__ void store_t(const Ctx& x, int r, int c, u32x4_t v) {
     *reinterpret_cast<MUON_GLOBAL u32x4_t*>(as_global(x.r16 + (int64_t)r * x.mp + c)) = v;
@@ -533,6 +548,7 @@ struct ApplyPhase {
   static __device__ float prescale(const Ctx& x) { return x.pre; }
   static __device__ int views(const Ctx&, bool) { return kViewRow | kViewCol; }
   static constexpr bool kMirror = true;
+  static constexpr bool kLower = false;
   static constexpr bool kAddX = true;
   struct Aux {};
   static constexpr int kBatch = 32, kBatchLast = 0;
@@ -577,6 +593,7 @@ struct FinalPhase {
   static __device__ float prescale(const Ctx&) { return 1.f; }
   static __device__ int views(const Ctx& x, bool) { return x.view; }
   static constexpr bool kMirror = false;
+  static constexpr bool kLower = false;
   static constexpr bool kAddX = true;
   static __device__ void store_t(const Ctx&, int, int, u32x4_t) {}  // no transposed copy
   struct Aux {
