@@ -22,8 +22,8 @@
 //                   Nesterov momentum) on the matrix cores (split-K over the
 //                   long dimension);
 //   k_skinny_poly   per slice: the sum of the partials, s = 1/(||X0||_F +
-//                   eps) from its trace, A0 = s^2 (the sum), the k-round
-//                   recurrence in float64, Qs = s Q;
+//                   eps) from its trace, the k-round recurrence from
+//                   A0 = s^2 (the sum) in float64, Qs = s Q;
 //   k_skinny_apply  O = Qs X0 (matrix cores), W <- W - decay W - lr f O.
 // Chunks are fixed by n alone, so a slice's arithmetic does not depend on the
 // batch it is fused into.  Both memory passes stream 16-byte accesses in
@@ -474,10 +474,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
 }
 
 // ------------------------------------------------------------------ poly
-// Per slice: the sum of the Gram partials, s = 1/(||X||_F + eps) from its
-// trace, A0 = s^2 (the sum), then the rounds in the m x m Gram space
+// Per slice: the sum G of the Gram partials, s = 1/(||X||_F + eps) from its
+// trace, then the rounds in the m x m Gram space from A0 = s^2 G
 // (A_{t+1} = P_t^2 A_t, Q = P_{k-1} ... P_0), all in float64, and finally
-// s Q as float32.  Products
+// s Q as float32.  The first round works on G itself with s^2 taken into
+// its coefficients, so A0 is never formed.  Products
 // run on the float64 matrix cores: each of the four waves owns one 16 x 16
 // tile of a 32 x 32 result (16x16x4 float64 instruction: lane l supplies
 // X[l % 16][l / 16] and Y[l / 16][l % 16] of each 4-wide k step and receives
@@ -487,8 +488,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
 // instructions) and tiles past m are skipped: they would add exact zeros.
 // A and Q are double-buffered, so a round needs three barriers.
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
+typedef double f64x2_t __attribute__((ext_vector_type(2)));
 constexpr int kPolyLd = 33;                                                  // row stride (doubles)
-constexpr int kPolyLds = (6 * 32 * kPolyLd + 1) * (int)sizeof(double);  // A[2], Q[2], P, S and s
+constexpr int kPolyLds = 6 * 32 * kPolyLd * (int)sizeof(double);  // A[2], Q[2], P and S
 typedef double PolyRow[kPolyLd];
 
 template <int KQ>
@@ -497,7 +499,6 @@ __device__ __forceinline__ void poly_slice(const SkinnyLaunch& a, const SkinnyBu
   PolyRow* const base = reinterpret_cast<PolyRow*>(lds);
   PolyRow* const P = base + 128;
   PolyRow* const S = base + 160;
-  double* sh_s = lds + 6 * 32 * kPolyLd;
   auto Abuf = [&](int i) { return base + 32 * i; };
   auto Qbuf = [&](int i) { return base + 64 + 32 * i; };
   const int m = bk.m, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -506,80 +507,83 @@ __device__ __forceinline__ void poly_slice(const SkinnyLaunch& a, const SkinnyBu
   const int nt = m * (m + 1) / 2;
   const int nch = bk.n_chunks;
 
-  // Gram sums over the packed upper triangles: entry v = tid + 256 k of the
-  // triangle (kPer = 3 covers m <= 32; KQ <= 5 means m <= 20, nt <= 210, one
-  // entry); the loads of a thread's entries for kBatch chunks are in flight
-  // together (40 chunks, n = 10240, in one batch where the registers allow),
-  // and each entry is summed in chunk order.  Loads past the end read a valid
-  // address and are discarded, so the batch is one straight run.
-  constexpr int kPer = KQ <= 5 ? 1 : (KQ <= 7 ? 2 : 3), kBatch = kPer <= 2 ? 40 : 20;
+  // Gram sums over the packed upper triangles, each entry summed in chunk
+  // order.  Thread t takes the entry pairs (2 p, 2 p + 1), p = t + 256 k
+  // (kPairs = 2 covers m <= 32): one 16-byte load per chunk where nt is even
+  // (every pair then starts on a 16-byte boundary), two 8-byte loads
+  // otherwise.  The loads of kBatch chunks are in flight together (all 40 of
+  // n = 10240 in one batch where the registers allow), and the LDS is
+  // cleared while the first batch is on its way.
+  constexpr int kPairs = KQ <= 7 ? 1 : 2, kBatch = kPairs == 1 ? 40 : 20;
   const double* parts = bk.gram_parts + (int64_t)z * nch * nt;
-  double sum[kPer];
+  const bool even = (nt & 1) == 0;
+  double sum[kPairs][2];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) sum[k] = 0.0;
+  for (int k = 0; k < kPairs; ++k) sum[k][0] = sum[k][1] = 0.0;
   for (int c0 = 0; c0 < nch; c0 += kBatch) {
-    double part[kPer][kBatch];
+    f64x2_t part[kPairs][kBatch];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int v = tid + kThreads * k, vc = v < nt ? v : 0;
+    for (int k = 0; k < kPairs; ++k) {
+      const int e0 = 2 * (tid + kThreads * k);
+      if (e0 >= nt) continue;
+      const bool two = e0 + 1 < nt;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int c = c0 + u < nch ? c0 + u : nch - 1;
-        part[k][u] = parts[(int64_t)c * nt + vc];
+        const double* q = parts + (int64_t)c * nt + e0;
+        if (even) {
+          part[k][u] = *reinterpret_cast<const MUON_GLOBAL f64x2_t*>(as_global(q));
+        } else {
+          part[k][u].x = *reinterpret_cast<const MUON_GLOBAL double*>(as_global(q));
+          part[k][u].y = two ? *reinterpret_cast<const MUON_GLOBAL double*>(as_global(q + 1)) : 0.0;
+        }
       }
     }
+    if (c0 == 0)
+      for (int e = tid; e < 6 * 32 * kPolyLd; e += kThreads) lds[e] = 0.0;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const bool in = tid + kThreads * k < nt;
+    for (int k = 0; k < kPairs; ++k) {
+      if (2 * (tid + kThreads * k) >= nt) continue;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) sum[k] += (in && c0 + u < nch) ? part[k][u] : 0.0;
+      for (int u = 0; u < kBatch; ++u) {
+        const bool in = c0 + u < nch;
+        sum[k][0] += in ? part[k][u].x : 0.0;
+        sum[k][1] += in ? part[k][u].y : 0.0;
+      }
     }
   }
-  for (int e = tid; e < 6 * 32 * kPolyLd; e += kThreads) lds[e] = 0.0;
   __syncthreads();
-  // The summed Gram matrix, both triangles.
-  int row[kPer], col[kPer];
+  // The summed Gram matrix G, both triangles, and Q = I.
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    int i = 0, r = tid + kThreads * k;
-    if (r < nt) {
-      while (r >= m - i) {
-        r -= m - i;
+  for (int k = 0; k < kPairs; ++k) {
+    const int e0 = 2 * (tid + kThreads * k);
+    if (e0 >= nt) continue;
+    int i = 0, r = e0;
+    while (r >= m - i) {
+      r -= m - i;
+      ++i;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (e0 + h >= nt) break;
+      if (h == 1 && ++r >= m - i) {  // the pair's second entry opens the next row
+        r = 0;
         ++i;
       }
-    }
-    row[k] = i;
-    col[k] = i + r;
-    if (tid + kThreads * k < nt) {
-      Abuf(0)[i][i + r] = sum[k];
-      Abuf(0)[i + r][i] = sum[k];
+      Abuf(0)[i][i + r] = sum[k][h];
+      Abuf(0)[i + r][i] = sum[k][h];
     }
   }
   for (int e = tid; e < m; e += kThreads) Qbuf(0)[e][e] = 1.0;
   __syncthreads();
-  // Sum of squares of X0 = trace of its Gram matrix (wave 0: one diagonal
-  // entry per lane, then a butterfly); s = 1 / (||X0||_F + eps).
-  if (wave == 0) {
-    double v = lane < m ? Abuf(0)[lane][lane] : 0.0;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if (lane == 0) {
-      *sh_s = 1.0 / (sqrt(v) + (double)Sc.eps);
-      if (!isfinite(v)) atomicOr(a.err, kErrNonFinite);
-    }
-  }
-  __syncthreads();
-  const double s = *sh_s;
-  // A0 = s^2 (X0 X0^T), each thread scaling the entries it wrote.
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    if (tid + kThreads * k < nt) {
-      const double x = sum[k] * s * s;
-      Abuf(0)[row[k]][col[k]] = x;
-      Abuf(0)[col[k]][row[k]] = x;
-    }
-  }
-  __syncthreads();
+  // Sum of squares of X0 = trace of G, summed by every thread in row order;
+  // s = 1 / (||X0||_F + eps).  A0 = s^2 G is never formed: the first round
+  // takes s^2 into its coefficients and into A1.
+  double tr = 0.0;
+  for (int i = 0; i < m; ++i) tr += Abuf(0)[i][i];
+  const double s = 1.0 / (sqrt(tr) + (double)Sc.eps);
+  if (tid == 0 && !isfinite(tr)) atomicOr(a.err, kErrNonFinite);
+  const double s2 = s * s;
 
   const int ti = 16 * (wave >> 1), tj = 16 * (wave & 1);
   const int li = lane & 15, lk = lane >> 4;
@@ -609,13 +613,19 @@ __device__ __forceinline__ void poly_slice(const SkinnyLaunch& a, const SkinnyBu
   for (int it = 0; it < ns; ++it) {
     const bool more = it + 1 < ns;
     PolyRow* const Ac = Abuf(cur);
-    // P = a I + b A + c A^2
+    // Round 0 holds G = A0 / s^2: P = a I + (b s^2) G + (c s^4) G^2 and
+    // A1 = s^2 P^2 G.
+    const double kb = it == 0 ? cb * s2 : cb, kc = it == 0 ? cc * (s2 * s2) : cc, ka = it == 0 ? s2 : 1.0;
+    // P = a I + b A + c A^2 (the entries of A read ahead of the product)
     if (live) {
+      double av[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) av[r] = Ac[ti + lk + 4 * r][tj + li];
       const f64x4_t t = prod(Ac, Ac);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = ti + lk + 4 * r, j = tj + li;
-        P[i][j] = cb * Ac[i][j] + cc * t[r] + ((i == j && i < m) ? ca : 0.0);
+        P[i][j] = kb * av[r] + kc * t[r] + ((i == j && i < m) ? ca : 0.0);
       }
     }
     __syncthreads();
@@ -638,7 +648,7 @@ __device__ __forceinline__ void poly_slice(const SkinnyLaunch& a, const SkinnyBu
         const f64x4_t t = prod(S, Ac);
         PolyRow* const An = Abuf(cur ^ 1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) An[ti + lk + 4 * r][tj + li] = t[r];
+        for (int r = 0; r < 4; ++r) An[ti + lk + 4 * r][tj + li] = ka * t[r];
       }
       __syncthreads();
     }
