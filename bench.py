@@ -227,8 +227,8 @@ def own_work_flops(wl: workloads.Workload, mode: str):
       skinny (Gram-space rounds): the first Gram matrix once (symmetric,
         m(m+1) n), per round A^2 and P^2 (symmetric, m^2 (m+1) each) and
         P Q, S A (2 m^3 each), then one apply Q X0 (2 m^2 n);
-      large tiles: per round Gram m(m+1) n and A^2 m^2 (m+1) (upper
-        triangles only), apply 2 m^2 n;
+      large tiles: per round Gram m(m+1) n and A^2 m^2 (m+1) (one
+        triangle each), apply 2 m^2 n;
       other streamed: per round Gram 2 m^2 n, A^2 2 m^3 (full squares), apply 2 m^2 n.
     The dense count of the method, k (4 m^2 n + 2 m^3), is Workload.flops()."""
     k = wl.ns_steps
@@ -369,7 +369,7 @@ def measure(wl: workloads.Workload, mode: str, steps: int, warmup: int, dev, gra
         roof = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
                 "algorithmic_flops_per_launch": per_launch, "avg_launch_ms": round(dom_ms_per_launch, 5),
-                "flops_counted": "own work: symmetric products counted once (upper triangles)"}
+                "flops_counted": "own work: symmetric products counted once (one triangle)"}
         if dominant == "apply" and mode == "bf16":
             roof["traffic"] = measured_traffic("apply", wl.name)
             roof["algorithmic_bytes_per_launch"] = big_apply_bytes(wl)
