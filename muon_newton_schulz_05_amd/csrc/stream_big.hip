@@ -42,9 +42,10 @@
 // (the 32 workgroups an XCD runs at once share 4 row and 8 column panels in
 // its L2), longest contraction first, with the work balanced over the XCDs.
 // Symmetric products (X X^T, E E) list only tiles on or above the diagonal
-// and compute their mirrors below it; the bf16 result of an off-diagonal tile
-// is also written to its mirror position.  Waves whose rows all lie past m
-// skip their products.  The epilogue turns the accumulators around in LDS and writes
+// (on slices with a padded last tile row they compute the mirrors below it,
+// and waves whose rows all lie past m skip their products); the bf16 result
+// of an off-diagonal tile is also written to its mirror position.  The
+// epilogue turns the accumulators around in LDS and writes
 // whole rows of 16-byte pieces.  Where a transposed copy holds the same values
 // (the mirror tiles, and X'^T next to X'), it is read out of LDS after the
 // row-view results, so the side inputs of the epilogue are read only once.
@@ -122,12 +123,14 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   if (t.bz == kNoTile) return;  // uniform over the workgroup, before any barrier
   const BigBucket& bb = g.buckets[t.bz >> 24];  // read in place: fields are indexed by round parity
   const int z = (int)(t.bz & 0xFFFFFFu);
-  // The table lists a symmetric product's tiles on and above the diagonal;
-  // Epi::kLower phases compute the mirror tile below it instead (the
-  // transposed copy goes out through the mirror writes), so that a padded
-  // last tile row, not column, holds the rows past m.
+  // The table lists a symmetric product's tiles on and above the diagonal.
+  // On a slice whose m is not a multiple of the tile, Epi::kLower phases
+  // compute the mirror tile below it instead (the transposed copy goes out
+  // through the mirror writes), so that the padded last tile row, not
+  // column, holds the rows past m.
   const int t_i = (int)(t.mn & 0xFFFFu), t_j = (int)(t.mn >> 16);
-  const int tm = Epi::kLower ? t_j : t_i, tn = Epi::kLower ? t_i : t_j;
+  const bool lower = Epi::kLower && bb.m % kBigTile != 0;
+  const int tm = lower ? t_j : t_i, tn = lower ? t_i : t_j;
   const Operands op = Epi::operands(g, bb, z);
   // The epilogue's context (table reads for the final phase) is fetched
   // here, so its loads complete during the products.
@@ -137,13 +140,14 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   // The wave index is uniform over the wave; saying so keeps branches on it scalar.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;  // 128 rows x 64 columns per wave
-  // Every product is zero in its rows past m: X and E are zero there, and R
-  // holds only its identity shift there, which meets rows of X that are
-  // zero.  A wave whose 128 rows all lie past m therefore skips its
-  // products, and its accumulators keep the zero they would give.  Those
-  // waves (4..7) sit one on each SIMD, so every matrix core of a half-padded
-  // tile runs half loaded.
-  const bool idle = wm == 1 && bb.m - (int64_t)tm * kBigTile <= 128;
+  // The symmetric products X X^T and E E are zero in their rows past m,
+  // where X and E are zero.  In those phases a wave whose 128 rows all lie
+  // past m skips its products, and its accumulators keep the zero they
+  // would give.  Those waves (4..7) sit one on each SIMD, so every matrix
+  // core of a half-padded tile runs half loaded.  (The apply's padded tile
+  // row gained nothing from the same skip, and the branch slowed its
+  // loop, so it has none.)
+  const bool idle = Epi::kLower && wm == 1 && bb.m - (int64_t)tm * kBigTile <= 128;
   const char* A = op.a + (int64_t)tm * kBigTile * op.lda * 2;
   const char* B = op.b + (int64_t)tn * kBigTile * op.ldb * 2;
   const int nk = (int)(op.K / kBK);
@@ -436,7 +440,8 @@ struct GramPhase {
   static __device__ float prescale(const Ctx& x) { return x.pre; }
   static __device__ int views(const Ctx&, bool diag) { return diag ? kViewRow : kViewRow | kViewCol; }
   // The transposed tile of E comes from LDS; A itself is stored only for
-  // tiles on or below the diagonal, the only ones the polynomial reads.
+  // the tiles this phase computes (one side of the diagonal), the only ones
+  // the polynomial reads.
   static constexpr bool kMirror = true;
   static constexpr bool kLower = true;
   static constexpr bool kAddX = false;
@@ -483,7 +488,7 @@ struct PolyPhase {
   static __device__ float prescale(const Ctx&) { return 1.f; }
   static __device__ int views(const Ctx&, bool diag) { return diag ? kViewRow : kViewRow | kViewCol; }
   // R is symmetric: its transposed tile comes from LDS, so A is read only
-  // on and below the diagonal.
+  // for the tiles the Gram phase computed (the same side of the diagonal).
   static constexpr bool kMirror = true;
   static constexpr bool kLower = true;
   static constexpr bool kAddX = false;
