@@ -309,15 +309,33 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
     constexpr int NB = kB < kPieces ? kB : kPieces;
     const int row0 = (V == kViewRow ? tm : tn) * kBigTile + h * 128;
     const int col0 = (V == kViewRow ? tn : tm) * kBigTile;
+    // Epi::kFastPath: where this half tile lies wholly inside the side
+    // input's storage (uniform over the workgroup), the loads and stores run
+    // in a copy of the loop without per-lane guards, chosen once per half:
+    // guards around each load make the compiler wait for it at once, so a
+    // batch's loads would not be in flight together.
+    using Guarded = std::false_type;
+    using Unguarded = std::true_type;
+    bool fast = false;
+    if constexpr (Epi::kFastPath) fast = Epi::fast(cx, V, row0, col0);
     typename Epi::Aux aux[NB];
-    auto load_batch = [&](int b0) {
+    auto load_batch = [&](int b0, auto fast_tag) {
+      constexpr bool kF = decltype(fast_tag)::value;
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         const int idx = (b0 + u) * kThreadsBig + tid;
-        aux[u] = Epi::load(cx, V, row0 + (idx >> 6), col0 + 4 * (idx & 63));
+        aux[u] = Epi::template load<kF>(cx, V, row0 + (idx >> 6), col0 + 4 * (idx & 63));
       }
     };
-    if constexpr (!late) load_batch(0);
+    auto first_batch = [&] {
+      if constexpr (Epi::kFastPath) {
+        if (fast) load_batch(0, Unguarded{});
+        else load_batch(0, Guarded{});
+      } else {
+        load_batch(0, Guarded{});
+      }
+    };
+    if constexpr (!late) first_batch();
     if constexpr (V == kViewRow) {
       // Staged [i][j]; 16-byte slot s of row r sits at s ^ (8 ((r / 4) mod 2)).
       if (wm == h) {
@@ -358,21 +376,30 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
       }
     }
     __syncthreads();
-    if constexpr (late) load_batch(0);
+    if constexpr (late) first_batch();
+    auto batches = [&](auto fast_tag) {
+      constexpr bool kF = decltype(fast_tag)::value;
 #pragma unroll
-    for (int b0 = 0; b0 < kPieces; b0 += NB) {
-      if (b0 > 0) load_batch(b0);
+      for (int b0 = 0; b0 < kPieces; b0 += NB) {
+        if (b0 > 0) load_batch(b0, fast_tag);
 #pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int idx = (b0 + u) * kThreadsBig + tid;
-        const int r = idx >> 6, sl = idx & 63;
-        const int ps = V == kViewRow ? sl ^ (((r >> 2) & 1) << 3) : sl ^ (r & 15);
-        f32x4_t* slot = reinterpret_cast<f32x4_t*>(stg + r * 256 + ps * 4);
-        const f32x4_t res = Epi::store(cx, V, row0 + r, col0 + 4 * sl, *slot, aux[u]);
-        if constexpr (V == kViewRow && Epi::kMirror) {
-          if (mirror) *slot = res;
+        for (int u = 0; u < NB; ++u) {
+          const int idx = (b0 + u) * kThreadsBig + tid;
+          const int r = idx >> 6, sl = idx & 63;
+          const int ps = V == kViewRow ? sl ^ (((r >> 2) & 1) << 3) : sl ^ (r & 15);
+          f32x4_t* slot = reinterpret_cast<f32x4_t*>(stg + r * 256 + ps * 4);
+          const f32x4_t res = Epi::template store<kF>(cx, V, row0 + r, col0 + 4 * sl, *slot, aux[u]);
+          if constexpr (V == kViewRow && Epi::kMirror) {
+            if (mirror) *slot = res;
+          }
         }
       }
+    };
+    if constexpr (Epi::kFastPath) {
+      if (fast) batches(Unguarded{});
+      else batches(Guarded{});
+    } else {
+      batches(Guarded{});
     }
     __syncthreads();
     if constexpr (V == kViewRow && Epi::kMirror) {
@@ -447,10 +474,13 @@ struct GramPhase {
   static constexpr bool kAddX = false;
   struct Aux {};
   static constexpr int kBatch = 32, kBatchLast = 0;
+  static constexpr bool kFastPath = false;
+  template <bool>
   static __device__ Aux load(const Ctx&, int, int, int) { return Aux{}; }
   static __device__ void store_t(const Ctx& x, int r, int c, u32x4_t v) {
     *reinterpret_cast<MUON_GLOBAL u32x4_t*>(as_global(x.e16 + (int64_t)r * x.mp + c)) = v;
   }
+  template <bool>
   static __device__ f32x4_t store(const Ctx& x, int, int r, int c, f32x4_t v, Aux) {
     const int64_t idx = (int64_t)r * x.mp + c;
     st_f32x4(x.a32 + idx, v);
@@ -500,10 +530,13 @@ struct PolyPhase {
     float dr;       // d (r)
   };
   static constexpr int kBatch = 4, kBatchLast = 16;
+  static constexpr bool kFastPath = false;
+  template <bool>
   static __device__ Aux load(const Ctx& x, int, int r, int c) {
     return Aux{ld_f32x4(x.a32 + (int64_t)r * x.mp + c), ld_f32x4(x.dg + c),
                *reinterpret_cast<const MUON_GLOBAL float*>(as_global(x.dg + r))};
   }
+  template <bool>
   static __device__ f32x4_t store(const Ctx& x, int, int r, int c, f32x4_t ee, const Aux& q) {
     const int64_t idx = (int64_t)r * x.mp + c;
     const f32x4_t a = q.a, dc = q.dc;
@@ -557,7 +590,10 @@ struct ApplyPhase {
   static constexpr bool kAddX = true;
   struct Aux {};
   static constexpr int kBatch = 32, kBatchLast = 0;
+  static constexpr bool kFastPath = false;
+  template <bool>
   static __device__ Aux load(const Ctx&, int, int, int) { return Aux{}; }
+  template <bool>
   static __device__ f32x4_t store(const Ctx& x, int, int r, int c, f32x4_t v, Aux) {
     st_bf16x4(x.x_new + (int64_t)r * x.np + c, v);
     return v;
@@ -604,9 +640,21 @@ struct FinalPhase {
   struct Aux {
     f32x4_t w;   // W (r, c .. c+3) as float32 (entries past the row end unused)
   };
-  static constexpr int kBatch = 4, kBatchLast = 0;
+  static constexpr int kBatch = 4, kBatchLast = 16;
+  // The unguarded path: a float32 W whose rows are whole 16-byte groups, and
+  // a half tile that lies wholly inside the slice (every tile of a slice
+  // whose sides are multiples of 256).
+  static constexpr bool kFastPath = true;
+  static __device__ bool fast(const Ctx& x, int, int row0, int col0) {
+    return x.vec && x.pdtype == 0 && row0 + 128 <= x.rows && col0 + kBigTile <= x.len;
+  }
+  template <bool kUnguarded>
   static __device__ Aux load(const Ctx& x, int, int r, int c) {
     Aux q{};
+    if constexpr (kUnguarded) {
+      q.w = *reinterpret_cast<const MUON_GLOBAL f32x4_t*>(as_global(x.w) + 4 * ((int64_t)r * x.len + c));
+      return q;
+    }
     if (r >= x.rows || c >= x.len) return q;
     const int64_t idx = (int64_t)r * x.len + c;
     if (x.vec && c + 3 < x.len) {
@@ -624,11 +672,16 @@ struct FinalPhase {
     }
     return q;
   }
+  template <bool kUnguarded>
   static __device__ f32x4_t store(const Ctx& x, int, int r, int c, f32x4_t v, const Aux& q) {
-    if (r >= x.rows || c >= x.len) return v;
     const f32x4_t n{q.w.x - x.decay * q.w.x - x.k * v.x, q.w.y - x.decay * q.w.y - x.k * v.y,
                     q.w.z - x.decay * q.w.z - x.k * v.z, q.w.w - x.decay * q.w.w - x.k * v.w};
     const int64_t idx = (int64_t)r * x.len + c;
+    if constexpr (kUnguarded) {
+      *reinterpret_cast<MUON_GLOBAL f32x4_t*>(as_global(x.w) + 4 * idx) = n;
+      return n;
+    }
+    if (r >= x.rows || c >= x.len) return v;
     if (x.vec && c + 3 < x.len) {
       if (x.pdtype == 1) {  // bfloat16 W, rounded to nearest even
         *reinterpret_cast<MUON_GLOBAL u32x2_t*>(as_global(x.w) + 2 * idx) =
