@@ -79,6 +79,13 @@ static_assert(kBK % 16 == 0 && kCPR <= 8 && kNS >= 2 && kLds <= 160 * 1024, "til
 // bank groups.
 __device__ __forceinline__ int swz(int r) { return (r / kRW) & (kCPR - 1); }
 
+// Epilogue staging of the row view (128 rows of 256 float32): the 16-byte
+// slot s of row r sits at s ^ stage_swz(r).  Bit 3 follows r / 4, so the
+// two half-waves of an accumulator write (rows r and r + 4) fill disjoint
+// halves of the banks; the low bits follow r / 8, so the 16 rows 8 k + u
+// that the transposed readout gathers at once sit in 16 distinct slots.
+__device__ __forceinline__ int stage_swz(int r) { return ((r >> 3) & 15) ^ (((r >> 2) & 1) << 3); }
+
 // Wait until at most `slices` k-slices of this wave's operand loads are in flight.
 __device__ __forceinline__ void wait_loads(int slices) {
   static_assert(kNS - 2 <= 3, "extend the cases");
@@ -337,7 +344,7 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
     };
     if constexpr (!late) first_batch();
     if constexpr (V == kViewRow) {
-      // Staged [i][j]; 16-byte slot s of row r sits at s ^ (8 ((r / 4) mod 2)).
+      // Staged [i][j]; 16-byte slot s of row r sits at s ^ stage_swz(r).
       if (wm == h) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
               for (int u = 0; u < 4; ++u) {
                 const int r = i * 32 + 8 * q + 4 * (lane >> 5) + u;
                 const int col = wn * 64 + j * 32 + (lane & 31);
-                const int ps = (col >> 2) ^ (((r >> 2) & 1) << 3);
+                const int ps = (col >> 2) ^ stage_swz(r);
                 stg[r * 256 + ps * 4 + (col & 3)] = pre * acc[i][j][4 * q + u];
               }
       }
@@ -386,7 +393,7 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
         for (int u = 0; u < NB; ++u) {
           const int idx = (b0 + u) * kThreadsBig + tid;
           const int r = idx >> 6, sl = idx & 63;
-          const int ps = V == kViewRow ? sl ^ (((r >> 2) & 1) << 3) : sl ^ (r & 15);
+          const int ps = V == kViewRow ? sl ^ stage_swz(r) : sl ^ (r & 15);
           f32x4_t* slot = reinterpret_cast<f32x4_t*>(stg + r * 256 + ps * 4);
           const f32x4_t res = Epi::template store<kF>(cx, V, row0 + r, col0 + 4 * sl, *slot, aux[u]);
           if constexpr (V == kViewRow && Epi::kMirror) {
@@ -404,18 +411,19 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
     __syncthreads();
     if constexpr (V == kViewRow && Epi::kMirror) {
       if (!mirror) return;
-      // Transposed rows: wave w takes tile columns 32 w .. 32 w + 31 (one per
-      // lane of each half-wave) and, in step t, rows 16 t + 8 (l / 32) .. + 7
-      // of this half, written as one 16-byte piece of row (column) c.
-      const int c = 32 * wave + (lane & 31);
+      // Transposed rows: in step t wave w takes tile columns 32 w + 4 t ..
+      // + 3, one per 16 lanes; lane l reads rows 8 (l mod 16) .. + 7 of this
+      // half down its column and writes them as one 16-byte piece of row
+      // (column) c, so each group of 16 lanes writes 256 contiguous bytes.
+      const int r0 = 8 * (lane & 15);
 #pragma unroll 2
       for (int t = 0; t < 8; ++t) {
-        const int r0 = 16 * t + 8 * (lane >> 5);
+        const int c = 32 * wave + 4 * t + (lane >> 4);
         float e[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int r = r0 + u;
-          e[u] = stg[r * 256 + 4 * ((c >> 2) ^ (((r >> 2) & 1) << 3)) + (c & 3)];
+          e[u] = stg[r * 256 + 4 * ((c >> 2) ^ stage_swz(r)) + (c & 3)];
         }
         Epi::store_t(cx, tn * kBigTile + c, tm * kBigTile + h * 128 + r0,
                      u32x4_t{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
