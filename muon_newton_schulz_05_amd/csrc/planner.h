@@ -100,7 +100,8 @@ void fill_info(const Plan& p, muon_plan_info_t* info);
 // Tile table of one product phase over the plan's large buckets (phase 0:
 // X X^T, 1: E E, 2: R X).  Output tiles are grouped in blocks of 4 tile rows
 // x 8 tile columns of one slice (for the symmetric phases only tiles on or
-// above the diagonal; the kernel computes their mirrors); blocks are dealt, longest contraction first, to the 8 XCD
+// above the diagonal, with the 8 x 8 triangles on the diagonal as blocks of
+// their own); blocks are dealt, longest contraction first, to the 8 XCD
 // stretches of the table, each block to the stretch with the least work so
 // far; stretches are padded with kNoTile to a common length.
 std::vector<BigTile> big_table(const Plan& p, int phase);
