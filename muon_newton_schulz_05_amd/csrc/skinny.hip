@@ -227,14 +227,16 @@ __device__ __forceinline__ void gram_chunk(const SkinnyLaunch& a, const SkinnyBu
     using GT = decltype(gtype);
     const int cb = wave * 64;
     float lm[kChunks][4], lg[kChunks][4];
+    // Every piece is loaded, those outside the slice from the nearest piece
+    // inside it (their values are not used): with no guard around a load,
+    // the loads of all pieces are in flight together.  (cw is a multiple of
+    // 4 on this path.)
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) {
-      const int v = lane + 64 * k, row = v >> 4, cc = cb + 4 * (v & 15);
-      if (row < m && cc < cm.cw) {
-        const int64_t off = (int64_t)row * n + cm.c0 + cc;
-        ld_vec4<F32>(Mb, off, lm[k]);
-        ld_vec4<GT>(Gb, off, lg[k]);
-      }
+      const int v = lane + 64 * k, row = min(v >> 4, m - 1), cc = min(cb + 4 * (v & 15), cm.cw - 4);
+      const int64_t off = (int64_t)row * n + cm.c0 + cc;
+      ld_vec4<F32>(Mb, off, lm[k]);
+      ld_vec4<GT>(Gb, off, lg[k]);
     }
     if (lane < 16) {
       *reinterpret_cast<u32x2_t*>(&H[m][cb + 4 * lane]) = u32x2_t{0u, 0u};
