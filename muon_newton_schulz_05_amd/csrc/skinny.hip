@@ -749,15 +749,18 @@ __device__ __forceinline__ void apply_direct(const SkinnyLaunch& a, const Skinny
   char* const Wb = static_cast<char*>(pe.w) + d.slice_off * (d.pdtype ? 2 : 4);
 
   // Every load first: the Qs operands, the X0 pieces, then the W pieces of
-  // the lane's O rows.
+  // the lane's O rows.  X0 is loaded without guards, pieces outside the
+  // slice from the nearest piece inside it (n is a multiple of 4 on this
+  // path): a guard around a load makes the compiler wait for it at once.
+  // The rows past the slice are zeroed before the products; a lane past the
+  // slice's end only computes columns it does not store.
   float qa[NT][RM];
   load_qs_operands<RM>(bk.qs + (int64_t)z * 1024, p, g, R, nt, qa);
   f32x4_t x[RM];
 #pragma unroll
   for (int q = 0; q < RM; ++q) {
-    const int row = R * g + q;
-    x[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (q < R && in && row < m) x[q] = *reinterpret_cast<const MUON_GLOBAL f32x4_t*>(as_global(Mb + (int64_t)row * n + c));
+    const int row = min(R * g + q, m - 1);
+    x[q] = *reinterpret_cast<const MUON_GLOBAL f32x4_t*>(as_global(Mb + (int64_t)row * n + (in ? c : n - 4)));
   }
   float gx[NEST ? RM : 1][4];
   if constexpr (NEST) {
@@ -773,39 +776,60 @@ __device__ __forceinline__ void apply_direct(const SkinnyLaunch& a, const Skinny
       }
     }
   }
-  float w[NT][4][4];
+  // W likewise, in the type it is stored in, by a copy of the rest of the
+  // function per W dtype, so that no guard or conversion sits next to a
+  // load.  (A form that loaded a float32 W as integer words and stored it
+  // as floats gave wrong results; loads and stores of one type do not.)
+  auto w_pass = [&](auto b16_tag) {
+    constexpr bool kB16 = decltype(b16_tag)::value;
+    using Raw = typename std::conditional<kB16, u32x2_t, f32x4_t>::type;
+    const int cl = in ? c : n - 4;  // n is a multiple of 4 on this path
+    Raw wr[NT][4];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * t + 4 * g + r;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) w[t][r][u] = 0.f;
-      if (t < nt && in && row < m) {
-        if (d.pdtype) ld_vec4<B16>(Wb, (int64_t)row * n + c, w[t][r]);
-        else ld_vec4<F32>(Wb, (int64_t)row * n + c, w[t][r]);
+      for (int r = 0; r < 4; ++r) {
+        const int row = min(16 * t + 4 * g + r, m - 1);
+        wr[t][r] = *reinterpret_cast<const MUON_GLOBAL Raw*>(as_global(Wb) + (kB16 ? 2 : 4) * ((int64_t)row * n + cl));
       }
-    }
-  if constexpr (NEST) {
 #pragma unroll
     for (int q = 0; q < RM; ++q)
+      if (q >= R || R * g + q >= m) x[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NEST) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[q][u] = fmaf(beta, x[q][u], gx[q][u]);
-  }
-  f32x4_t acc[NT][4];
-  apply_products<RM>(x, qa, R, nt, acc);
+      for (int q = 0; q < RM; ++q)
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * t + 4 * g + r;
-      if (t >= nt || !in || row >= m) continue;
-      float o[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) o[u] = w_update(w[t][r][u], decay, lrf, acc[t][u][r]);
-      if (d.pdtype) st_vec4<B16>(Wb, (int64_t)row * n + c, o);
-      else st_vec4<F32>(Wb, (int64_t)row * n + c, o);
+        for (int u = 0; u < 4; ++u) x[q][u] = fmaf(beta, x[q][u], gx[q][u]);
     }
+    f32x4_t acc[NT][4];
+    apply_products<RM>(x, qa, R, nt, acc);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * t + 4 * g + r;
+        if (t >= nt || !in || row >= m) continue;
+        float w[4];
+        if constexpr (kB16) {
+          w[0] = bf16_lo(wr[t][r].x);
+          w[1] = bf16_hi(wr[t][r].x);
+          w[2] = bf16_lo(wr[t][r].y);
+          w[3] = bf16_hi(wr[t][r].y);
+        } else {
+          w[0] = wr[t][r].x;
+          w[1] = wr[t][r].y;
+          w[2] = wr[t][r].z;
+          w[3] = wr[t][r].w;
+        }
+        float o[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[u] = w_update(w[u], decay, lrf, acc[t][u][r]);
+        if constexpr (kB16) st_vec4<B16>(Wb, (int64_t)row * n + c, o);
+        else st_vec4<F32>(Wb, (int64_t)row * n + c, o);
+      }
+  };
+  if (d.pdtype) w_pass(std::true_type{});
+  else w_pass(std::false_type{});
 }
 
 // Staged form (any slice): the chunk's X0 is turned around in LDS, the
