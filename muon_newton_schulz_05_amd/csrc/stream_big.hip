@@ -82,8 +82,8 @@ __device__ __forceinline__ int swz(int r) { return (r / kRW) & (kCPR - 1); }
 // Epilogue staging of the row view (128 rows of 256 float32): the 16-byte
 // slot s of row r sits at s ^ stage_swz(r).  Bit 3 follows r / 4, so the
 // two half-waves of an accumulator write (rows r and r + 4) fill disjoint
-// halves of the banks; the low bits follow r / 8, so the 16 rows 8 k + u
-// that the transposed readout gathers at once sit in 16 distinct slots.
+// halves of the banks; the low bits follow r / 8, so the rows 8 k + u that
+// the transposed readout gathers at once sit in distinct slots.
 __device__ __forceinline__ int stage_swz(int r) { return ((r >> 3) & 15) ^ (((r >> 2) & 1) << 3); }
 
 // Wait until at most `slices` k-slices of this wave's operand loads are in flight.
@@ -412,13 +412,16 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
     if constexpr (V == kViewRow && Epi::kMirror) {
       if (!mirror) return;
       // Transposed rows: in step t wave w takes tile columns 32 w + 4 t ..
-      // + 3, one per 16 lanes; lane l reads rows 8 (l mod 16) .. + 7 of this
-      // half down its column and writes them as one 16-byte piece of row
-      // (column) c, so each group of 16 lanes writes 256 contiguous bytes.
-      const int r0 = 8 * (lane & 15);
+      // + 3; lane l takes column j = (l / 8) mod 4 of them and reads rows
+      // 8 k .. + 7 of this half down it, k = l mod 8 + 8 (l / 32), writing
+      // them as one 16-byte piece of row (column) c.  Each half-wave then
+      // gathers 8 row groups x 4 columns, whole 16-byte slots in 8 (16 for
+      // the wave) distinct positions, and each column's 16 lanes write 256
+      // contiguous bytes.
+      const int r0 = 8 * ((lane & 7) + 8 * (lane >> 5));
 #pragma unroll 2
       for (int t = 0; t < 8; ++t) {
-        const int c = 32 * wave + 4 * t + (lane >> 4);
+        const int c = 32 * wave + 4 * t + ((lane >> 3) & 3);
         float e[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
