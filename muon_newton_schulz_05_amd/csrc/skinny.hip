@@ -762,17 +762,23 @@ __device__ __forceinline__ void apply_direct(const SkinnyLaunch& a, const Skinny
     const int row = min(R * g + q, m - 1);
     x[q] = *reinterpret_cast<const MUON_GLOBAL f32x4_t*>(as_global(Mb + (int64_t)row * n + (in ? c : n - 4)));
   }
-  float gx[NEST ? RM : 1][4];
+  // Nesterov momentum: G at the same pieces, unguarded too, as its stored
+  // bits (this kernel never writes G), converted where it is used.
+  u32x4_t graw[NEST ? RM : 1];
   if constexpr (NEST) {
     const char* const Gb = static_cast<const char*>(pe.g) + d.slice_off * (d.gdtype ? 2 : 4);
+    if (d.gdtype) {
 #pragma unroll
-    for (int q = 0; q < RM; ++q) {
-      const int row = R * g + q;
+      for (int q = 0; q < RM; ++q) {
+        const int row = min(R * g + q, m - 1);
+        const u32x2_t b = *reinterpret_cast<const MUON_GLOBAL u32x2_t*>(as_global(Gb) + 2 * ((int64_t)row * n + (in ? c : n - 4)));
+        graw[q] = u32x4_t{b.x, b.y, 0u, 0u};
+      }
+    } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) gx[q][u] = 0.f;
-      if (q < R && in && row < m) {
-        if (d.gdtype) ld_vec4<B16>(Gb, (int64_t)row * n + c, gx[q]);
-        else ld_vec4<F32>(Gb, (int64_t)row * n + c, gx[q]);
+      for (int q = 0; q < RM; ++q) {
+        const int row = min(R * g + q, m - 1);
+        graw[q] = *reinterpret_cast<const MUON_GLOBAL u32x4_t*>(as_global(Gb) + 4 * ((int64_t)row * n + (in ? c : n - 4)));
       }
     }
   }
@@ -797,9 +803,17 @@ __device__ __forceinline__ void apply_direct(const SkinnyLaunch& a, const Skinny
       if (q >= R || R * g + q >= m) x[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if constexpr (NEST) {
 #pragma unroll
-      for (int q = 0; q < RM; ++q)
+      for (int q = 0; q < RM; ++q) {
+        f32x4_t gq;
+        if (d.gdtype) {
+          gq = f32x4_t{bf16_lo(graw[q].x), bf16_hi(graw[q].x), bf16_lo(graw[q].y), bf16_hi(graw[q].y)};
+        } else {
+          gq = __builtin_bit_cast(f32x4_t, graw[q]);
+        }
+        if (q >= R || R * g + q >= m) gq = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[q][u] = fmaf(beta, x[q][u], gx[q][u]);
+        for (int u = 0; u < 4; ++u) x[q][u] = fmaf(beta, x[q][u], gq[u]);
+      }
     }
     f32x4_t acc[NT][4];
     apply_products<RM>(x, qa, R, nt, acc);
