@@ -110,14 +110,14 @@ def measured_traffic(kernel: str, workload: str):
 def big_apply_bytes(wl: workloads.Workload) -> float:
     """Compulsory HBM bytes per launch of the large-tile apply class (k - 1
     apply launches and one final launch per step), over the slices with
-    m > 512 in their padded workspace layout (multiples of 256): an apply
+    m >= 129 in their padded workspace layout (multiples of 256): an apply
     reads R (2 mp^2) and X^T and writes X' and X'^T (2 mp np each; the X term
     comes from the X^T operand already on chip); the final launch reads R and
     X^T and reads and writes W (float32, 8 m n)."""
     k = wl.ns_steps
     apply = final = 0.0
     for m, n in wl.oriented_matrices():
-        if m <= 512:
+        if path_of(m, "bf16") != "large":
             continue
         mp, np_ = -(-m // 256) * 256, -(-n // 256) * 256
         apply += 2 * mp * mp + 6 * mp * np_
@@ -218,7 +218,7 @@ def path_of(m: int, mode: str) -> str:
     """Kernel path the planner gives an oriented slice with m rows."""
     if m <= 32:
         return "skinny"
-    return "large" if mode == "bf16" and m >= 513 else "stream"
+    return "large" if mode == "bf16" and m >= 129 else "stream"
 
 
 def own_work_flops(wl: workloads.Workload, mode: str):

@@ -108,6 +108,9 @@ typedef struct {
   int32_t nesterov;        /* 1: orthogonalise G + beta M (M already updated) instead of M   */
   int32_t update_scale;    /* muon_update_scale_t: factor f on O, from the stored [R, C]    */
   float weight_decay;      /* wd >= 0: W <- W - lr wd W - lr f O (decoupled)                 */
+  int32_t large_min_m;     /* bf16 mode: streamed slices with m >= this (>= 33) take the
+                              256 x 256-tile products; 0 = default 129, -1 = never (every
+                              streamed slice takes the 32- or 128-tile products)              */
 } muon_plan_opts_t;
 
 /* Shape factor f of the update of a slice stored as [R, C]. */

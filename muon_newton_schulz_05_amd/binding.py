@@ -49,7 +49,7 @@ class PlanOpts(ctypes.Structure):
                 ("max_ns_steps", ctypes.c_int32), ("workspace_limit", ctypes.c_uint64),
                 ("skinny_max_m", ctypes.c_int32), ("timing", ctypes.c_int32),
                 ("n_cu", ctypes.c_int32), ("nesterov", ctypes.c_int32), ("update_scale", ctypes.c_int32),
-                ("weight_decay", ctypes.c_float)]
+                ("weight_decay", ctypes.c_float), ("large_min_m", ctypes.c_int32)]
 
 
 MUON_SCALE_NONE, MUON_SCALE_ASPECT, MUON_SCALE_RMS = 0, 1, 2
@@ -149,7 +149,7 @@ def make_descs(shapes, param_dtypes=None, grad_dtypes=None):
 
 def make_opts(mode="bf16", use_graph=False, eps=1e-7, max_ns_steps=16, workspace_limit=0,
               skinny_max_m=0, timing=False, n_cu=0, nesterov=False, update_scale="none",
-              weight_decay=0.0) -> PlanOpts:
+              weight_decay=0.0, large_min_m=0) -> PlanOpts:
     o = muon_default_opts()
     o.mode = {"fp32": MUON_MODE_FP32, "bf16": MUON_MODE_BF16_MFMA}.get(mode, mode)
     o.use_graph = int(bool(use_graph))
@@ -162,6 +162,7 @@ def make_opts(mode="bf16", use_graph=False, eps=1e-7, max_ns_steps=16, workspace
     o.nesterov = int(nesterov)
     o.update_scale = UPDATE_SCALES.get(update_scale, update_scale)
     o.weight_decay = weight_decay
+    o.large_min_m = large_min_m
     return o
 
 
@@ -270,7 +271,7 @@ class MuonPlan:
 
     def __init__(self, params, grad_dtypes=None, mode: str = "bf16", use_graph=False, eps=1e-7,
                  timing=False, skinny_max_m=0, workspace_limit=0, max_ns_steps=16, nesterov=False,
-                 update_scale="none", weight_decay=0.0):
+                 update_scale="none", weight_decay=0.0, large_min_m=0):
         import torch
         self.params = list(params)
         if not self.params:
@@ -296,7 +297,7 @@ class MuonPlan:
         self.opts = make_opts(mode=mode, use_graph=use_graph, eps=eps, timing=timing,
                               skinny_max_m=skinny_max_m, workspace_limit=workspace_limit,
                               max_ns_steps=max_ns_steps, nesterov=nesterov, update_scale=update_scale,
-                              weight_decay=weight_decay)
+                              weight_decay=weight_decay, large_min_m=large_min_m)
         self.device = dev
         with torch.cuda.device(dev):
             self.handle = muon_plan_create(self.descs, self.opts)

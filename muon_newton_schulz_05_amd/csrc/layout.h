@@ -11,7 +11,7 @@ constexpr int kMaxSkinnyM = 32;       // skinny path: one 32-row MFMA tile holds
 constexpr int kSkinnyChunk = 256;     // skinny path: columns per workgroup (fixed by n alone)
 constexpr int kStreamPad = 128;       // streamed workspace dims are padded to this
 constexpr int kBigTile = 256;         // large bf16 buckets: product tile, and their padding
-constexpr int kBigMinM = 513;         // bf16 buckets with m >= this take the large-tile products
+constexpr int kBigMinM = 129;         // default: bf16 buckets with m >= this take the large-tile products
 constexpr int kBigKStep = 64;         // large-tile products: k elements per slice
 // Longest padded n of the large-tile products: 255 rows of n bf16 plus a
 // 16-byte chunk offset stay below 2^32 bytes.

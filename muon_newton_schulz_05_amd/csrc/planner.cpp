@@ -35,6 +35,7 @@ void default_opts(muon_plan_opts_t* o) {
   o->max_ns_steps = 16;
   o->workspace_limit = 0;
   o->skinny_max_m = 0;
+  o->large_min_m = 0;
   o->timing = 0;
   o->n_cu = 0;
 }
@@ -70,6 +71,11 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
     *err = buf;
     return MUON_ERR_INVALID_ARGUMENT;
   }
+  if (opts.large_min_m < -1 || (opts.large_min_m > 0 && opts.large_min_m <= kMaxSkinnyM)) {
+    std::snprintf(buf, sizeof buf, "large_min_m must be -1, 0 or at least %d", kMaxSkinnyM + 1);
+    *err = buf;
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
   if (opts.nesterov != 0 && opts.nesterov != 1) {
     *err = "nesterov must be 0 or 1";
     return MUON_ERR_INVALID_ARGUMENT;
@@ -94,6 +100,8 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
   p.workspace_limit = opts.workspace_limit;
   p.skinny_max_m = opts.skinny_max_m == 0 ? kMaxSkinnyM
                    : opts.skinny_max_m < 0 ? 0 : opts.skinny_max_m;
+  p.large_min_m = opts.large_min_m == 0 ? kBigMinM
+                  : opts.large_min_m < 0 ? INT32_MAX : opts.large_min_m;
   p.timing = opts.timing ? 1 : 0;
   p.use_graph = opts.use_graph ? 1 : 0;
   p.nesterov = opts.nesterov;
@@ -198,7 +206,7 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
       // The large-tile products address a 256-row operand panel with 32-bit
       // lane offsets and a tile column in 16 bits, so slices longer than
       // kBigMaxN take the general products instead.
-      bp.big = p.mode == MUON_MODE_BF16_MFMA && bp.m >= kBigMinM && round_up(bp.n, kBigTile) <= kBigMaxN;
+      bp.big = p.mode == MUON_MODE_BF16_MFMA && bp.m >= p.large_min_m && round_up(bp.n, kBigTile) <= kBigMaxN;
       const int64_t pad = bp.big ? kBigTile : kStreamPad;
       bp.mp = round_up(bp.m, pad);
       bp.np = round_up(bp.n, pad);

@@ -37,7 +37,7 @@ struct BucketPlan {
   uint64_t off_gram = 0, off_qs = 0;
 
   // streamed path
-  bool big = false;         // bf16 mode and m >= kBigMinM: 256 x 256 tile products
+  bool big = false;         // bf16 mode and m >= the plan's large_min_m: 256 x 256 tile products
   bool small = false;       // padded m <= kSmallMaxMp: grouped 32 x 32 tile products
   int64_t mp = 0, np = 0;   // padded dims
   int x_bytes = 0;          // X element size (2: bf16, 4: fp32)
@@ -58,6 +58,7 @@ struct Plan {
   int max_ns_steps = 16;
   uint64_t workspace_limit = 0;
   int skinny_max_m = kMaxSkinnyM;
+  int64_t large_min_m = kBigMinM;  // bf16 mode: m from which slices take the large tiles
   int timing = 0, use_graph = 0;
   int nesterov = 0, update_scale = MUON_SCALE_NONE;  // update variants
   float weight_decay = 0.f;

@@ -1,5 +1,5 @@
 // stream_big.hip -- matrix products of the streamed path for large slices in
-// bf16 mode (m > 512, dimensions padded to multiples of 256).
+// bf16 mode (m >= 129, dimensions padded to multiples of 256).
 //
 // Per Newton-Schulz round ("关于分布式Muon的想法整合及讨论" §2 and §6: the Gram
 // matrix is recomputed each round; "MindSpore HyperParallel X 盘古,Muon优化器实现

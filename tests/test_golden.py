@@ -75,7 +75,7 @@ def test_last_tiles_structure():
         assert abs(float(np.linalg.norm(t.astype(np.float64))) - c["tile_frobenius"]) < 1e-5 * c["tile_frobenius"]
         buckets.add(key)
     large = {(n, min(p.shape[-2:]), max(p.shape[-2:])) for n, wl in workloads.WORKLOADS.items()
-             for p in wl.params if min(p.shape[-2:]) > 512}
+             for p in wl.params if min(p.shape[-2:]) >= 129}
     assert buckets == large
 
 

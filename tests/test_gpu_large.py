@@ -1,4 +1,4 @@
-"""Parity of the large-slice products (bf16 mode, m > 512: 256 x 256 tiles,
+"""Parity of the large-slice products (bf16 mode, m >= 129: 256 x 256 tiles,
 float32 diagonal kept out of the bf16 operands, identity-shifted polynomial).
 
 Sizes are chosen so that the oracle runs in seconds while the products still
@@ -50,13 +50,23 @@ def test_large_shapes(shape):
     _check([shape])
 
 
+@pytest.mark.parametrize("shape", [(129, 1000), (1000, 129), (200, 333), (256, 256), (2, 300, 520),
+                                   (384, 1536), (512, 512)])
+def test_mid_shapes(shape):
+    """Slices with 129 <= m <= 512 take the large tiles too: one or two tile
+    rows, so every tile of the symmetric phases sits on the diagonal, and
+    m = 129 leaves all but one row of its tile row as padding."""
+    _check([shape])
+
+
 def test_large_fusion_is_bitexact():
     """Fused large buckets give bitwise the W and M of one plan per slice:
     three [600,700] slices fused, the two slices of a [2,520,1030] stack,
     and two [2100,2200] slices (9 row tiles: the 4 x 8 block branch of the
-    tile table) next to a transposed [700,600].  A slice's products do not
-    depend on which table entries or workgroups computed its tiles."""
-    shapes = [(600, 700)] * 3 + [(2, 520, 1030), (2100, 2200), (2100, 2200), (700, 600)]
+    tile table) next to a transposed [700,600] and a [200,333] (one tile
+    row).  A slice's products do not depend on which table entries or
+    workgroups computed its tiles."""
+    shapes = [(600, 700)] * 3 + [(2, 520, 1030), (2100, 2200), (2100, 2200), (700, 600), (200, 333)]
     params, grads, moms = make_inputs(shapes, "bf16", 83, w_std=0.02, m_std=1e-3)
     kw = dict(mode="bf16", lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
     w_f, m_f = gpu_step(params, grads, moms, **kw)

@@ -77,6 +77,16 @@ def test_streamed_shapes(shape, mode):
     check([shape], mode)
 
 
+@pytest.mark.parametrize("shape", [(200, 333), (256, 256), (2, 150, 400), (300, 520), (513, 517),
+                                   (600, 700)])
+def test_bf16_streamed_products_without_large_tiles(shape):
+    """With the large tiles switched off, bf16 slices with m >= 129 take the
+    32-tile grouped products (m <= 256) or the 128-tile products with P as a
+    hi/lo pair (m > 256), as slices longer than the large tiles can address
+    always do."""
+    check([shape], "bf16", plan_kw=dict(large_min_m=-1))
+
+
 @pytest.mark.parametrize("mode", ["bf16", "fp32"])
 def test_mixed_plan(mode):
     """Several buckets in one plan, both paths, transposed members, f32 and bf16 grads."""
@@ -131,12 +141,13 @@ def test_fusion_is_bitexact(mode):
 
 @pytest.mark.parametrize("mode", ["bf16", "fp32"])
 def test_small_product_tile_size_is_bitexact(mode):
-    """Buckets with padded m above 256 take 128 x 128 tiles when a launch has
-    at least 256 of them, else 64 x 64 tiles; each output entry sums its k
-    steps in the same order for either size, so 64 slices of [300,520] fused
-    (128-wide tiles) and single slices (64-wide tiles) agree bit for bit."""
+    """Streamed buckets with padded m above 256 take 128 x 128 tiles when a
+    launch has at least 256 of them, else 64 x 64 tiles; each output entry
+    sums its k steps in the same order for either size, so 64 slices of
+    [300,520] fused (128-wide tiles) and single slices (64-wide tiles) agree
+    bit for bit.  (In bf16 mode the large tiles are switched off.)"""
     params, grads, moms = make_inputs([(64, 300, 520)], "bf16", 61, w_std=0.02, m_std=1e-3)
-    kw = dict(mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    kw = dict(mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q, plan_kw=dict(large_min_m=-1))
     w_f, m_f = gpu_step(params, grads, moms, **kw)
     for e in (0, 37, 63):
         w_1, m_1 = gpu_step([params[0][e]], [grads[0][e]], [moms[0][e]], **kw)
@@ -373,6 +384,34 @@ def test_streamed_ill_conditioned_fp32(kind):
     err = max(update_errors(w_gpu[0], params[0], 1.0, o_ref[0], TOL["fp32"]))
     print(f"{shape} {kind} fp32: {err:.3e}")
     assert err <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("kind", ["logspaced", "rank1_noise"])
+@pytest.mark.parametrize("shape,plan_kw", [((96, 700), None), ((200, 333), None), ((600, 700), None),
+                                           ((300, 520), dict(large_min_m=-1))],
+                         ids=["small", "large-mid", "large", "streamed-hilo"])
+def test_bf16_ill_conditioned_resolved_directions(shape, plan_kw, kind):
+    """bf16 mode stores X in bf16, whose 8-bit significand cannot hold a
+    singular direction far below the largest one; the polynomial then
+    amplifies what is left of it (by up to a^k), so over the whole matrix
+    these inputs miss the bf16 bar (logspaced 4-10%, rank one plus noise
+    about 117%, alike on every streamed path).  The directions that bf16
+    resolves must still be right: O restricted to the singular vectors of G
+    with sigma / sigma_1 > 2^-8 meets the bar."""
+    g = _conditioned(shape, kind, 72)
+    params, moms = [np.zeros(shape, np.float32)], [np.zeros(shape, np.float32)]
+    w_gpu, _ = gpu_step(params, [g], moms, mode="bf16", lr=1.0, beta=0.9, ns_steps=5, coeffs=Q,
+                        plan_kw=plan_kw)
+    _, _, o_ref = oracle_step(params, [g], moms, lr=1.0, beta=0.9, ns_steps=5, coeffs=Q)
+    o_gpu = -w_gpu[0].astype(np.float64)   # W0 = 0 and lr = 1
+    u, s, vt = np.linalg.svd(g.astype(np.float64), full_matrices=False)
+    k = int((s / s[0] > 2.0 ** -8).sum())
+    a = u[:, :k].T @ o_gpu @ vt[:k].T
+    b = u[:, :k].T @ o_ref[0] @ vt[:k].T
+    err = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+    whole = float(np.linalg.norm(o_gpu - o_ref[0]) / np.linalg.norm(o_ref[0]))
+    print(f"{shape} {kind} bf16: resolved ({k} directions) {err:.3e}, whole {whole:.3e}")
+    assert err <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("mode", ["bf16", "fp32"])

@@ -52,8 +52,8 @@ int main(void) {
   printf("%zu %zu %zu %zu\n", offsetof(muon_param_desc_t, shape), offsetof(muon_plan_opts_t, workspace_limit),
          offsetof(muon_plan_opts_t, n_cu), offsetof(muon_plan_info_t, buckets));
   printf("%zu %zu\n", offsetof(muon_bucket_info_t, workspace_bytes), offsetof(muon_plan_info_t, launches_per_ns));
-  printf("%zu %zu %zu\n", offsetof(muon_plan_opts_t, nesterov), offsetof(muon_plan_opts_t, update_scale),
-         offsetof(muon_plan_opts_t, weight_decay));
+  printf("%zu %zu %zu %zu\n", offsetof(muon_plan_opts_t, nesterov), offsetof(muon_plan_opts_t, update_scale),
+         offsetof(muon_plan_opts_t, weight_decay), offsetof(muon_plan_opts_t, large_min_m));
   return 0;
 }
 '''
@@ -68,7 +68,7 @@ int main(void) {
            ctypes.sizeof(b.PlanInfo), b.ParamDesc.shape.offset, b.PlanOpts.workspace_limit.offset,
            b.PlanOpts.n_cu.offset, b.PlanInfo.buckets.offset, b.BucketInfo.workspace_bytes.offset,
            b.PlanInfo.launches_per_ns.offset, b.PlanOpts.nesterov.offset, b.PlanOpts.update_scale.offset,
-           b.PlanOpts.weight_decay.offset]
+           b.PlanOpts.weight_decay.offset, b.PlanOpts.large_min_m.offset]
     assert got == vals
 
 
@@ -111,7 +111,7 @@ def test_graph_plans_count_the_scalar_prologue(m):
 
 
 def test_large_bucket_workspace_is_padded_to_the_big_tile(m):
-    """bf16 buckets with m > 512 are padded to 256 (1408 -> 1536); their
+    """bf16 buckets with m >= 129 are padded to 256 (1408 -> 1536); their
     workspace holds X and X^T twice, A (float32), E and R (bf16), the
     diagonal and the two tile tables."""
     d = m.make_descs([(1408, 2048)], ["f32"], ["bf16"])
@@ -150,19 +150,30 @@ def test_skinny_buckets_share_three_launches(m):
 
 
 def test_small_streamed_buckets_share_three_launches_per_round(m):
-    """Every streamed bucket with padded m <= 256 (m <= 256) runs each
-    product phase of a round in one launch with the others; a bucket with
-    larger m takes its own three launches, and the large bf16 buckets share
-    three more."""
+    """Every streamed bucket with padded m <= 256 (m <= 256) that does not
+    take the large tiles runs each product phase of a round in one launch
+    with the others.  In float32 mode that is every such bucket, and a bucket
+    with larger m takes its own three launches.  In bf16 mode the buckets with
+    m >= 129 share the three large-tile launches instead."""
     shapes = [(100, 300), (200, 150), (64, 64), (3, 40, 500), (256, 1000)]
     d = m.make_descs(shapes, ["f32"] * 5, ["bf16"] * 5)
-    for mode in ("bf16", "fp32"):
+    for mode, launches in (("bf16", 3 + 3), ("fp32", 3)):
         info = m.info_dict(m.muon_plan_describe(d, m.make_opts(mode=mode)))
         assert [b["path"] for b in info["buckets"]] == ["stream"] * 5
-        assert info["launches_per_ns"] == 3, mode
+        assert info["launches_per_ns"] == launches, mode
+    small = m.make_descs([(100, 300), (64, 64), (3, 40, 500), (128, 4000)], ["f32"] * 4, ["bf16"] * 4)
+    assert m.info_dict(m.muon_plan_describe(small, m.make_opts(mode="bf16")))["launches_per_ns"] == 3
     mixed = m.make_descs(shapes + [(300, 520), (600, 700)], ["f32"] * 7, ["bf16"] * 7)
-    assert m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="bf16")))["launches_per_ns"] == 3 + 3 + 3
+    assert m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="bf16")))["launches_per_ns"] == 3 + 3
     assert m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="fp32")))["launches_per_ns"] == 3 + 3 + 3
+    # large_min_m moves the threshold (-1: no large tiles)
+    off = m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="bf16", large_min_m=-1)))
+    assert off["launches_per_ns"] == 3 + 3 + 3
+    high = m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="bf16", large_min_m=301)))
+    assert high["launches_per_ns"] == 3 + 3 + 3   # small group, [300,520] alone, [600,700] large
+    low = m.info_dict(m.muon_plan_describe(small, m.make_opts(mode="bf16", large_min_m=65)))
+    assert low["launches_per_ns"] == 3 + 3        # m = 64 and 40 stay small; m = 100 and 128 go large
+    assert m.info_dict(m.muon_plan_describe(small, m.make_opts(mode="bf16", large_min_m=33)))["launches_per_ns"] == 3
 
 
 def test_skinny_path_can_be_disabled(m):
@@ -199,6 +210,8 @@ def test_argument_errors(m):
     expect_error(m, INV, [(4, 4)], eps=float("nan"))
     expect_error(m, INV, [(4, 4)], max_ns_steps=-2)
     expect_error(m, INV, [(4, 4)], skinny_max_m=33)
+    expect_error(m, INV, [(4, 4)], large_min_m=32)
+    expect_error(m, INV, [(4, 4)], large_min_m=-2)
     expect_error(m, INV, [(4, 4)], nesterov=2)
     expect_error(m, INV, [(4, 4)], update_scale=3)
     expect_error(m, INV, [(4, 4)], weight_decay=-0.1)
