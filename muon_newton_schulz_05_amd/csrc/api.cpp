@@ -143,10 +143,12 @@ bool device_tables(muon_plan_t plan, std::vector<Upload>* ups) try {
     plan->skinny_b0 = sbs[0];
     add_upload(ups, p.off_skinny_params, sbs);
   }
-  if (!p.small.empty()) {
+  // The grouped streamed buckets: workgroup ranges counted in each phase's
+  // output tiles (tile[ph] x tile[ph]).
+  auto group_params = [&](const std::vector<int>& group, const int tile[3]) {
     std::vector<muon::SmallBucket> sbs;
     int64_t t0[3] = {0, 0, 0};
-    for (int b : p.small) {
+    for (int b : group) {
       const muon::BucketPlan& bp = p.buckets[b];
       muon::SmallBucket sb{};
       sb.mats = at<muon::DevMat>(plan, bp.off_mats);
@@ -163,16 +165,20 @@ bool device_tables(muon_plan_t plan, std::vector<Upload>* ups) try {
       sb.mp = bp.mp;
       sb.np = bp.np;
       sb.count = (int32_t)bp.slices.size();
-      const int64_t ti = bp.mp / muon::kSmallTile, tj = bp.np / muon::kSmallTile;
-      const int64_t per[3] = {ti * ti, ti * ti, ti * tj};
       for (int ph = 0; ph < 3; ++ph) {
+        const int64_t ti = bp.mp / tile[ph], tj = (ph == 2 ? bp.np : bp.mp) / tile[ph];
         sb.t0[ph] = (int32_t)t0[ph];
-        t0[ph] += per[ph] * sb.count;
+        t0[ph] += ti * tj * sb.count;
       }
       sbs.push_back(sb);
     }
-    add_upload(ups, p.off_small_params, sbs);
+    return sbs;
+  };
+  if (!p.small.empty()) {
+    const int tile[3] = {muon::kSmallTile, muon::kSmallTile, muon::kSmallTile};
+    add_upload(ups, p.off_small_params, group_params(p.small, tile));
   }
+  if (!p.mid.empty()) add_upload(ups, p.off_mid_params, group_params(p.mid, p.mid_bt));
   if (!p.big.empty()) {
     std::vector<muon::BigBucket> bbs;
     for (int b : p.big) {
@@ -244,28 +250,28 @@ hipError_t enqueue_skinny(muon_plan_t plan, hipStream_t s, bool timing, const mu
   return timed(plan, muon::kClsSkinnyApply, s, timing, [&] { return muon::launch_skinny_apply(L, s); });
 }
 
-// Newton-Schulz rounds of all small streamed buckets: one launch per
-// product phase and round over all of them.
-hipError_t enqueue_small_rounds(muon_plan_t plan, int ns, hipStream_t s, bool timing) {
+// Newton-Schulz rounds of a group of streamed buckets (the small ones, or
+// the others that do not take the large tiles): one launch per product
+// phase and round over all of them.
+hipError_t enqueue_group_rounds(muon_plan_t plan, bool small, int ns, hipStream_t s, bool timing) {
   const muon::Plan& p = plan->p;
   muon::SmallArgs g{};
-  g.buckets = at<muon::SmallBucket>(plan, p.off_small_params);
-  g.nb = (int)p.small.size();
+  g.buckets = at<muon::SmallBucket>(plan, small ? p.off_small_params : p.off_mid_params);
+  g.nb = (int)(small ? p.small.size() : p.mid.size());
   g.sc = at<muon::DevScalars>(plan, p.off_scalars);
   g.ptrs = at<muon::PtrEntry>(plan, p.off_ptrs);
   const bool f32 = p.mode == MUON_MODE_FP32;
+  auto launch = [&](int ph, bool final_round) {
+    return small ? muon::launch_small(ph, final_round, f32, g, p.small_wgs[ph], s)
+                 : muon::launch_mid(ph, final_round, f32, g, p.mid_wgs[ph], p.mid_bt[ph], s);
+  };
   hipError_t e;
   for (int it = 0; it < ns; ++it) {
     g.src = it & 1;
     g.first = it == 0;
-    if ((e = timed(plan, muon::kClsGram, s, timing,
-                   [&] { return muon::launch_small(0, false, f32, g, p.small_wgs[0], s); })) != hipSuccess)
-      return e;
-    if ((e = timed(plan, muon::kClsPoly, s, timing,
-                   [&] { return muon::launch_small(1, false, f32, g, p.small_wgs[1], s); })) != hipSuccess)
-      return e;
-    if ((e = timed(plan, muon::kClsApply, s, timing,
-                   [&] { return muon::launch_small(2, it == ns - 1, f32, g, p.small_wgs[2], s); })) != hipSuccess)
+    if ((e = timed(plan, muon::kClsGram, s, timing, [&] { return launch(0, false); })) != hipSuccess) return e;
+    if ((e = timed(plan, muon::kClsPoly, s, timing, [&] { return launch(1, false); })) != hipSuccess) return e;
+    if ((e = timed(plan, muon::kClsApply, s, timing, [&] { return launch(2, it == ns - 1); })) != hipSuccess)
       return e;
   }
   return hipSuccess;
@@ -337,50 +343,7 @@ hipError_t enqueue_stream(muon_plan_t plan, const muon::BucketPlan& bp, int ns, 
     muon::Update0Launch u{mats, ptrs, sc, scale, bp.m, bp.n, cnt};
     return timed(plan, muon::kClsUpdate, s, timing, [&] { return muon::launch_update0(u, s); });
   }
-  if (bp.big || bp.small) return hipSuccess;  // rounds run grouped over all large (small) buckets
-  for (int it = 0; it < ns; ++it) {
-    const int src = it & 1, dst = src ^ 1;
-    const float* sfirst = it == 0 ? scale : nullptr;
-    muon::GramLaunch gl{plan->ws + bp.off_x[src], at<float>(plan, bp.off_a32),
-                        bp.off_a16 ? at<uint16_t>(plan, bp.off_a16) : nullptr, sfirst, bp.mp, bp.np,
-                        cnt, bp.x_bytes};
-    if ((e = timed(plan, muon::kClsGram, s, timing, [&] { return muon::launch_gram(gl, s); })) != hipSuccess)
-      return e;
-    muon::PolyLaunch pl;
-    pl.op = bp.poly_f32 ? (const void*)at<float>(plan, bp.off_a32) : (const void*)at<uint16_t>(plan, bp.off_a16);
-    pl.op_bytes = bp.poly_f32 ? 4 : 2;
-    pl.a32 = at<float>(plan, bp.off_a32);
-    pl.phi = plan->ws + bp.off_phi;
-    pl.plo = bp.p_hilo ? at<uint16_t>(plan, bp.off_plo) : nullptr;
-    pl.p_bytes = p.mode == MUON_MODE_FP32 ? 4 : 2;
-    pl.sc = sc;
-    pl.mp = bp.mp;
-    pl.count = cnt;
-    if ((e = timed(plan, muon::kClsPoly, s, timing, [&] { return muon::launch_poly(pl, s); })) != hipSuccess)
-      return e;
-    muon::ApplyLaunch al;
-    al.phi = plan->ws + bp.off_phi;
-    al.plo = bp.p_hilo ? (const void*)(plan->ws + bp.off_plo) : nullptr;
-    al.p_bytes = pl.p_bytes;
-    al.xt_old = plan->ws + bp.off_xt[src];
-    al.x_old = plan->ws + bp.off_x[src];
-    al.x_new = plan->ws + bp.off_x[dst];
-    al.xt_new = plan->ws + bp.off_xt[dst];
-    al.scale = sfirst;
-    al.sc = sc;
-    al.mp = bp.mp;
-    al.np = bp.np;
-    al.m = bp.m;
-    al.n = bp.n;
-    al.count = cnt;
-    al.x_bytes = bp.x_bytes;
-    al.final_round = it == ns - 1;
-    al.mats = mats;
-    al.ptrs = ptrs;
-    if ((e = timed(plan, muon::kClsApply, s, timing, [&] { return muon::launch_apply(al, s); })) != hipSuccess)
-      return e;
-  }
-  return hipSuccess;
+  return hipSuccess;  // the rounds run grouped over the buckets (small, other, large)
 }
 
 // Every bucket's launches, in plan order.  The number of Newton-Schulz
@@ -402,7 +365,11 @@ hipError_t enqueue_buckets(muon_plan_t plan, int ns, hipStream_t s, bool timing,
     first = nullptr;
   }
   if (!plan->p.small.empty() && ns > 0) {
-    hipError_t e = enqueue_small_rounds(plan, ns, s, timing);
+    hipError_t e = enqueue_group_rounds(plan, true, ns, s, timing);
+    if (e != hipSuccess) return e;
+  }
+  if (!plan->p.mid.empty() && ns > 0) {
+    hipError_t e = enqueue_group_rounds(plan, false, ns, s, timing);
     if (e != hipSuccess) return e;
   }
   if (!plan->p.big.empty() && ns > 0) return enqueue_big_rounds(plan, ns, s, timing);

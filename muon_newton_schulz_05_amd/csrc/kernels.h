@@ -66,53 +66,11 @@ struct NormLaunch {
 };
 hipError_t launch_norm(const NormLaunch& a, hipStream_t s);
 
-// A = scale2 * X X^T  (scale2 = s^2 on the first round, else 1)
-struct GramLaunch {
-  const void* x;
-  float* a32;
-  uint16_t* a16;          // bf16 copy of A (or null)
-  const float* scale;     // null after the first round
-  int64_t mp, np;
-  int count, x_bytes;
-};
-hipError_t launch_gram(const GramLaunch& a, hipStream_t s);
-
-// P = b A + c A A  (A symmetric, so A A = A A^T)
-struct PolyLaunch {
-  const void* op;         // A as the product's operand: a32 (float) or a16 (bf16)
-  int op_bytes;
-  const float* a32;
-  void* phi;              // P (float) or its bf16 high part
-  uint16_t* plo;          // bf16 low part (or null)
-  int p_bytes;
-  const DevScalars* sc;
-  int64_t mp;
-  int count;
-};
-hipError_t launch_poly(const PolyLaunch& a, hipStream_t s);
-
-// X' = scale * (a X + P X); the final round subtracts lr * X' from W instead.
-struct ApplyLaunch {
-  const void* phi;
-  const void* plo;        // or null
-  int p_bytes;
-  const void* xt_old;
-  const void* x_old;
-  void* x_new;
-  void* xt_new;
-  const float* scale;     // null after the first round
-  const DevScalars* sc;
-  int64_t mp, np, m, n;
-  int count, x_bytes;
-  int final_round;
-  const DevMat* mats;
-  const PtrEntry* ptrs;
-};
-hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
-
-// ---------------------------------------------------------------- streamed, small buckets (grouped)
-// One launch per product phase covers every bucket with padded m <=
-// kSmallMaxMp (32 x 32 output tiles, the contraction split over 4 waves).
+// ---------------------------------------------------------------- streamed products (grouped)
+// One launch per product phase covers every bucket of a group: the small
+// buckets (padded m <= kSmallMaxMp: 32 x 32 output tiles, the contraction
+// split over 4 waves), or the other streamed buckets that do not take the
+// large tiles (BT x BT output tiles).  Both read this bucket array.
 struct SmallArgs {
   const SmallBucket* buckets;
   int nb;
@@ -125,6 +83,10 @@ struct SmallArgs {
 // mode (else bf16 X and a bf16 hi/lo P).  wgs: workgroups of the phase.
 hipError_t launch_small(int phase, bool final_round, bool f32_operands, const SmallArgs& a, int64_t wgs,
                         hipStream_t s);
+// The same for the other group; bt: the output tile (64 or 128) of this
+// phase, in whose units the buckets' t0 and wgs count.
+hipError_t launch_mid(int phase, bool final_round, bool f32_operands, const SmallArgs& a, int64_t wgs, int bt,
+                      hipStream_t s);
 
 // ---------------------------------------------------------------- streamed, large bf16 buckets
 // One launch per product phase covers every large bucket; the tile table

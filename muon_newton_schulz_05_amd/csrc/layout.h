@@ -24,6 +24,7 @@ constexpr uint32_t kNoTile = 0xFFFFFFFFu;  // tile-table padding entry
 constexpr int kMomTile = 64;          // momentum kernel tile (oriented 64 x 64)
 constexpr int kSmallMaxMp = 256;      // streamed buckets with padded m <= this: grouped 32 x 32 products
 constexpr int kSmallTile = 32;        // their output tile
+constexpr int kMidMinTiles = 256;     // other streamed buckets: fewer 128-tiles per phase than this take 64-tiles
 
 enum KernelClass { kClsSkinnyGram = 0, kClsSkinnyPoly, kClsSkinnyApply, kClsMomentum, kClsNorm,
                    kClsGram, kClsPoly, kClsApply, kClsUpdate, kNumClasses };
@@ -77,8 +78,9 @@ struct BigTile {
   uint32_t mn;  // tm | tn << 16 (256 x 256 output tiles)
 };
 
-// Device addresses of one small streamed bucket (padded m <= kSmallMaxMp).
-// Each product phase of a round is one launch over every such bucket;
+// Device addresses of one streamed bucket that does not take the large tiles
+// (the small ones, padded m <= kSmallMaxMp, form one group, the others
+// another).  Each product phase of a round is one launch over a group;
 // workgroup b belongs to the last bucket with t0[phase] <= b.
 struct SmallBucket {
   const DevMat* mats;  // slice table

@@ -230,7 +230,6 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
       // arithmetic does not depend on the plan it sits in.
       bp.small = !bp.big && bp.mp <= kSmallMaxMp;
       p.launches_fixed += 2;   // momentum, norm
-      if (!bp.big && !bp.small) p.launches_per_ns += 3;  // gram, poly, apply (the last apply also updates W)
     }
     bp.ws_bytes = ws.take(0) - bp.ws_begin;
   }
@@ -270,6 +269,35 @@ int make_plan(const muon_param_desc_t* descs, int32_t n_params, const muon_plan_
     }
     p.launches_per_ns += 3;
     p.off_small_params = ws.take(p.small.size() * sizeof(SmallBucket));
+  }
+  // The other streamed buckets share one launch per product phase too.  The
+  // output tile of a phase is 128, or 64 when the whole group has fewer
+  // 128-tiles than the chip has CUs; each output entry takes its k steps in
+  // the same order for either size, so the choice changes no bit.
+  int64_t t128[3] = {0, 0, 0};
+  for (int b = 0; b < (int)p.buckets.size(); ++b) {
+    const BucketPlan& bp = p.buckets[b];
+    if (bp.path != MUON_PATH_STREAM || bp.big || bp.small) continue;
+    p.mid.push_back(b);
+    const int64_t ti = bp.mp / 128, tj = bp.np / 128, cnt = (int64_t)bp.slices.size();
+    t128[0] += cnt * ti * ti;
+    t128[1] += cnt * ti * ti;
+    t128[2] += cnt * ti * tj;
+  }
+  if (!p.mid.empty()) {
+    // Longest contractions first, so the launch does not end on them: the
+    // Gram phase contracts over n (the other phases over m).
+    std::stable_sort(p.mid.begin(), p.mid.end(), [&](int a, int b) { return p.buckets[a].np > p.buckets[b].np; });
+    for (int ph = 0; ph < 3; ++ph) {
+      p.mid_bt[ph] = t128[ph] < kMidMinTiles ? 64 : 128;
+      p.mid_wgs[ph] = p.mid_bt[ph] == 64 ? 4 * t128[ph] : t128[ph];
+      if (p.mid_wgs[ph] >= (int64_t(1) << 31)) {
+        *err = "too many product tiles in one plan";
+        return MUON_ERR_UNSUPPORTED;
+      }
+    }
+    p.launches_per_ns += 3;
+    p.off_mid_params = ws.take(p.mid.size() * sizeof(SmallBucket));
   }
   // Large buckets share one launch per product phase.
   for (int b = 0; b < (int)p.buckets.size(); ++b)

@@ -85,6 +85,14 @@ struct Plan {
   std::vector<int> small;
   uint64_t off_small_params = 0;
   int64_t small_wgs[3] = {0, 0, 0};
+  // The other streamed buckets (not skinny, small or large): their indices,
+  // the device SmallBucket array, and per product phase the output tile
+  // (128, or 64 when the group has fewer 128-tiles than kMidMinTiles) and
+  // the workgroups in those tiles.
+  std::vector<int> mid;
+  uint64_t off_mid_params = 0;
+  int mid_bt[3] = {128, 128, 128};
+  int64_t mid_wgs[3] = {0, 0, 0};
   uint64_t ws_total = 0;
   int launches_fixed = 0, launches_per_ns = 0;
 };

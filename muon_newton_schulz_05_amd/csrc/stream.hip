@@ -157,26 +157,7 @@ __global__ __launch_bounds__(256) void k_norm(NormLaunch a) {
   }
 }
 
-// ------------------------------------------------------------------ GEMM core
-// BT x BT output tile per 256-thread workgroup (BT = 128, or 64 where a
-// launch would have fewer 128-tiles than the chip has CUs); 4 waves in a
-// 2 x 2 grid, each computing BT/2 x BT/2 with 32x32 matrix-core instructions.
-// k-slices of 64 bytes per row are staged through LDS, double buffered.
-// Every output entry takes its k steps in the same order whatever BT is, so
-// the tile size does not change a single bit of the result.
-constexpr int kRowBytes = 64;       // bytes of k per operand row per stage
-constexpr int kLdsRow = kRowBytes + 16;
-
-struct GemmCore {
-  const char* a;   // A operand base (matrix 0)
-  const char* a2;  // second A operand (hi/lo split) or null
-  const char* b;
-  int64_t lda, ldb;          // row strides in elements
-  int64_t sa, sb;            // matrix strides in elements
-  int64_t K;                 // contraction length (multiple of the k-slice)
-  int tiles_n;               // output tiles along j (set by run_gemm)
-};
-
+// ------------------------------------------------------------------ matrix-core helpers
 __device__ __forceinline__ f32x16_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -184,133 +165,16 @@ __device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <typename T, class Epi, int BT>
-__global__ __launch_bounds__(256) void k_gemm(GemmCore c, Epi epi) {
-  constexpr int BK = kRowBytes / (int)sizeof(T);
-  constexpr int X = BT / 64;  // 32x32 blocks per wave along i and along j
-  constexpr int H = BT / 64;  // 16-byte loads per thread, operand and slice
-  constexpr int WT = BT / 2;  // rows (columns) per wave
-  __shared__ __attribute__((aligned(16))) char lds[2][2][BT * kLdsRow];
-  const int z = blockIdx.z;
-  const int tm = blockIdx.x / c.tiles_n, tn = blockIdx.x % c.tiles_n;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const char* A = c.a + ((int64_t)z * c.sa + (int64_t)tm * BT * c.lda) * (int64_t)sizeof(T);
-  const char* A2 = c.a2 ? c.a2 + ((int64_t)z * c.sa + (int64_t)tm * BT * c.lda) * (int64_t)sizeof(T)
-                        : nullptr;
-  const char* B = c.b + ((int64_t)z * c.sb + (int64_t)tn * BT * c.ldb) * (int64_t)sizeof(T);
-
-  int row[H], c16[H];
-#pragma unroll
-  for (int h = 0; h < H; ++h) {
-    const int idx = tid + 256 * h;
-    row[h] = idx >> 2;
-    c16[h] = idx & 3;
-  }
-  u32x4_t ra[H], rb[H];
-  const int nk = (int)(c.K / BK);
-  const int total = A2 ? 2 * nk : nk;
-
-  auto gload = [&](int it) {
-    const int kt = it % nk;
-    const char* Ab = it >= nk ? A2 : A;
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
-      ra[h] = *reinterpret_cast<const u32x4_t*>(Ab + ((int64_t)row[h] * c.lda + (int64_t)kt * BK) * (int64_t)sizeof(T) + c16[h] * 16);
-      rb[h] = *reinterpret_cast<const u32x4_t*>(B + ((int64_t)row[h] * c.ldb + (int64_t)kt * BK) * (int64_t)sizeof(T) + c16[h] * 16);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
-      *reinterpret_cast<u32x4_t*>(&lds[buf][0][row[h] * kLdsRow + c16[h] * 16]) = ra[h];
-      *reinterpret_cast<u32x4_t*>(&lds[buf][1][row[h] * kLdsRow + c16[h] * 16]) = rb[h];
-    }
-  };
-
-  f32x16_t acc[X][X];
-#pragma unroll
-  for (int x = 0; x < X; ++x)
-#pragma unroll
-    for (int y = 0; y < X; ++y) acc[x][y] = f32x16_t{};
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int it = 0; it < total; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < total) gload(it + 1);
-    const char* As = lds[cur][0];
-    const char* Bs = lds[cur][1];
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8_t af[X], bf[X];
-#pragma unroll
-        for (int x = 0; x < X; ++x)
-          af[x] = *reinterpret_cast<const bf16x8_t*>(As + (wm * WT + x * 32 + (lane & 31)) * kLdsRow + s * 32 + (lane >> 5) * 16);
-#pragma unroll
-        for (int y = 0; y < X; ++y)
-          bf[y] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WT + y * 32 + (lane & 31)) * kLdsRow + s * 32 + (lane >> 5) * 16);
-#pragma unroll
-        for (int x = 0; x < X; ++x)
-#pragma unroll
-          for (int y = 0; y < X; ++y) acc[x][y] = mfma_bf16(af[x], bf[y], acc[x][y]);
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        float af[X], bf[X];
-#pragma unroll
-        for (int x = 0; x < X; ++x)
-          af[x] = *reinterpret_cast<const float*>(As + (wm * WT + x * 32 + (lane & 31)) * kLdsRow + (s * 2 + (lane >> 5)) * 4);
-#pragma unroll
-        for (int y = 0; y < X; ++y)
-          bf[y] = *reinterpret_cast<const float*>(Bs + (wn * WT + y * 32 + (lane & 31)) * kLdsRow + (s * 2 + (lane >> 5)) * 4);
-#pragma unroll
-        for (int x = 0; x < X; ++x)
-#pragma unroll
-          for (int y = 0; y < X; ++y) acc[x][y] = mfma_f32(af[x], bf[y], acc[x][y]);
-      }
-    }
-    if (it + 1 < total) sstore(cur ^ 1);
-    __syncthreads();
-  }
-
-  // Output layout of a 32x32 block: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32.
-#pragma unroll
-  for (int x = 0; x < X; ++x)
-#pragma unroll
-    for (int y = 0; y < X; ++y)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int i0 = tm * BT + wm * WT + x * 32 + 8 * g + 4 * (lane >> 5);
-        const int j = tn * BT + wn * WT + y * 32 + (lane & 31);
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = acc[x][y][4 * g + u];
-        epi(z, i0, j, v);
-      }
-}
-
 // ------------------------------------------------------------------ epilogues
 struct GramEpi {
   float* a32;
-  uint16_t* a16;
   const float* scale;
   int64_t mp;
   __device__ void operator()(int z, int i0, int j, const float v[4]) const {
     const float s = scale ? scale[2 * z + 1] : 1.f;
     const int64_t zb = (int64_t)z * mp * mp;
-    float val[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) val[u] = s * v[u];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u;
-      a32[zb + (int64_t)i * mp + j] = val[u];
-      if (a16) a16[zb + (int64_t)i * mp + j] = to_bf16(val[u]);
-    }
+    for (int u = 0; u < 4; ++u) a32[zb + (int64_t)(i0 + u) * mp + j] = s * v[u];
   }
 };
 
@@ -418,77 +282,116 @@ __global__ __launch_bounds__(256) void k_update0(Update0Launch a) {
   }
 }
 
-// ------------------------------------------------------------------ small products, grouped
-// Buckets whose padded m is at most kSmallMaxMp (m <= 256): every product
-// phase of a round is one launch over all of them.  One 32 x 32 output tile
-// per 256-thread workgroup; the contraction is split over the four waves:
-// wave w takes k = 32 w .. 32 w + 31 of every 128-wide chunk, and the four
-// partial sums are added in the fixed order ((w0 + w1) + w2) + w3.  The
-// tile and the split depend on the slice's shape alone, so fused and
-// single-slice runs give the same bits.  Chunks are double-buffered through
-// registers into LDS; 16-byte chunk c of tile row r sits in slot c ^ (r mod 8),
-// so the 16-byte fragment reads of 8 consecutive rows hit distinct banks.
-constexpr int kSmCK = 128;  // k elements per chunk (every padded dimension is a multiple of 128)
-
-template <int Ph>
-__device__ __forceinline__ int64_t small_tiles_j(const SmallBucket& b) {
-  return Ph == 2 ? b.np / kSmallTile : b.mp / kSmallTile;
-}
+// ------------------------------------------------------------------ grouped products: shared parts
+// The streamed products run grouped: each product phase of a round is one
+// launch over every bucket of a group (the small buckets, padded m <= 256; or
+// the others), and workgroup b belongs to the last bucket with
+// t0[phase] <= b.  The tile grid of a bucket, and the split of each output
+// entry's sum, depend on its shape alone, so fused and single-slice runs give
+// the same bits.
 
 // Ph: 0 gram (A = s2 X X^T), 1 poly (P = b A + c A A), 2 apply (X' = s (a X + P X)),
-// 3 the last round's apply, which updates W.  T: the operand element type.
-template <typename T, int Ph>
-__global__ __launch_bounds__(256) void k_small(SmallArgs g) {
-  constexpr int ES = (int)sizeof(T);
-  constexpr int RB = kSmCK * ES;            // bytes of one tile row per chunk
-  constexpr int CPR = RB / 16;              // 16-byte chunks per row
-  constexpr int H = kSmallTile * CPR / 256; // 16-byte pieces per thread, operand and chunk
-  constexpr int PH = Ph == 3 ? 2 : Ph;      // tile grid of the phase
-  __shared__ __attribute__((aligned(16))) char lds[2][2][kSmallTile * RB];
+// 3 the last round's apply, which updates W.  PH: the tile grid of the phase.
+template <int Ph>
+constexpr int grid_phase() { return Ph == 3 ? 2 : Ph; }
 
-  // The workgroup's bucket: the last one whose first workgroup is <= b.
-  const int wg = blockIdx.x;
+template <int PH>
+__device__ __forceinline__ const SmallBucket& find_bucket(const SmallArgs& g, int wg) {
   int lo = 0, hi = g.nb - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (g.buckets[mid].t0[PH] <= wg) lo = mid;
     else hi = mid - 1;
   }
-  const SmallBucket bk = g.buckets[lo];
-  // The round's ping-pong buffers, chosen without indexing a local array by
-  // a run-time value (which would put the bucket in scratch memory).
-  char* const x_src = g.src ? bk.x[1] : bk.x[0];
-  char* const x_dst = g.src ? bk.x[0] : bk.x[1];
-  char* const xt_src = g.src ? bk.xt[1] : bk.xt[0];
-  char* const xt_dst = g.src ? bk.xt[0] : bk.xt[1];
-  const int64_t tj_n = small_tiles_j<PH>(bk), ti_n = bk.mp / kSmallTile;
+  return g.buckets[lo];
+}
+
+// The round's ping-pong buffers, chosen without indexing a local array by a
+// run-time value (which would put the bucket in scratch memory).
+struct RoundBuffers {
+  char *x_src, *x_dst, *xt_src, *xt_dst;
+};
+__device__ __forceinline__ RoundBuffers round_buffers(const SmallBucket& bk, int src) {
+  return {src ? bk.x[1] : bk.x[0], src ? bk.x[0] : bk.x[1], src ? bk.xt[1] : bk.xt[0], src ? bk.xt[0] : bk.xt[1]};
+}
+
+// Operands of slice z: rows of A and of B, both contiguous along k, with
+// row stride ld and contraction length K (the padded m or n).  The apply's
+// P may come as a bf16 hi/lo pair (a, a2).
+struct Operands {
+  const char *a, *a2, *b;
+  int64_t ld, K;
+};
+template <typename T, int Ph>
+__device__ __forceinline__ Operands slice_operands(const SmallBucket& bk, const RoundBuffers& rb, int z) {
+  constexpr int ES = (int)sizeof(T);
+  Operands o{};
+  if constexpr (Ph == 0) {
+    o.a = o.b = rb.x_src + (int64_t)z * bk.mp * bk.np * ES;
+    o.ld = o.K = bk.np;
+  } else if constexpr (Ph == 1) {
+    o.a = o.b = reinterpret_cast<const char*>(bk.a32 + (int64_t)z * bk.mp * bk.mp);
+    o.ld = o.K = bk.mp;
+  } else {
+    o.a = bk.phi + (int64_t)z * bk.mp * bk.mp * ES;
+    if (bk.plo) o.a2 = reinterpret_cast<const char*>(bk.plo + (int64_t)z * bk.mp * bk.mp);
+    o.b = rb.xt_src + (int64_t)z * bk.np * bk.mp * ES;
+    o.ld = o.K = bk.mp;
+  }
+  return o;
+}
+
+// The phase's epilogue for 4 consecutive rows i0 .. i0 + 3 of column j.
+template <typename T, int Ph>
+__device__ __forceinline__ void phase_epilogue(const SmallArgs& g, const SmallBucket& bk, const RoundBuffers& rb,
+                                               int z, int i0, int j, const float v[4]) {
+  if constexpr (Ph == 0) {
+    GramEpi{bk.a32, g.first ? bk.scale : nullptr, bk.mp}(z, i0, j, v);
+  } else if constexpr (Ph == 1) {
+    PolyEpi{bk.a32, bk.phi, bk.plo, bk.plo == nullptr, g.sc, bk.mp}(z, i0, j, v);
+  } else if constexpr (Ph == 2) {
+    ApplyEpi<T>{reinterpret_cast<const T*>(rb.x_src), reinterpret_cast<T*>(rb.x_dst),
+                reinterpret_cast<T*>(rb.xt_dst), g.first ? bk.scale : nullptr, g.sc, bk.mp, bk.np}(z, i0, j, v);
+  } else {
+    FinalEpi<T>{reinterpret_cast<const T*>(rb.x_src), g.first ? bk.scale : nullptr, g.sc, bk.mats, g.ptrs,
+                bk.mp, bk.np, bk.m, bk.n}(z, i0, j, v);
+  }
+}
+
+// ------------------------------------------------------------------ small products
+// Buckets whose padded m is at most kSmallMaxMp (m <= 256).  One 32 x 32
+// output tile per 256-thread workgroup; the contraction is split over the
+// four waves: wave w takes k = 32 w .. 32 w + 31 of every 128-wide chunk,
+// and the four partial sums are added in the fixed order ((w0 + w1) + w2) + w3.
+// Chunks are double-buffered through registers into LDS; 16-byte chunk c of
+// tile row r sits in slot c ^ (r mod 8), so the 16-byte fragment reads of 8
+// consecutive rows hit distinct banks.
+constexpr int kSmCK = 128;  // k elements per chunk (every padded dimension is a multiple of 128)
+
+template <typename T, int Ph>
+__global__ __launch_bounds__(256) void k_small(SmallArgs g) {
+  constexpr int ES = (int)sizeof(T);
+  constexpr int RB = kSmCK * ES;            // bytes of one tile row per chunk
+  constexpr int CPR = RB / 16;              // 16-byte chunks per row
+  constexpr int H = kSmallTile * CPR / 256; // 16-byte pieces per thread, operand and chunk
+  constexpr int PH = grid_phase<Ph>();
+  __shared__ __attribute__((aligned(16))) char lds[2][2][kSmallTile * RB];
+
+  const int wg = blockIdx.x;
+  const SmallBucket bk = find_bucket<PH>(g, wg);
+  const RoundBuffers rbuf = round_buffers(bk, g.src);
+  const int64_t tj_n = (PH == 2 ? bk.np : bk.mp) / kSmallTile, ti_n = bk.mp / kSmallTile;
   const int64_t local = wg - bk.t0[PH];
   const int z = (int)(local / (ti_n * tj_n));
   const int64_t t = local - (int64_t)z * ti_n * tj_n;
   const int ti = (int)(t / tj_n), tj = (int)(t - (t / tj_n) * tj_n);
 
-  // Operands: rows of A and of B, both contiguous along k.
-  const char *a, *a2 = nullptr, *b;
-  int64_t ld, K;
-  if constexpr (Ph == 0) {
-    a = b = x_src + (int64_t)z * bk.mp * bk.np * ES;
-    ld = bk.np;
-    K = bk.np;
-  } else if constexpr (Ph == 1) {
-    a = b = reinterpret_cast<const char*>(bk.a32 + (int64_t)z * bk.mp * bk.mp);
-    ld = bk.mp;
-    K = bk.mp;
-  } else {
-    a = bk.phi + (int64_t)z * bk.mp * bk.mp * ES;
-    if (bk.plo) a2 = reinterpret_cast<const char*>(bk.plo + (int64_t)z * bk.mp * bk.mp);
-    b = xt_src + (int64_t)z * bk.np * bk.mp * ES;
-    ld = bk.mp;
-    K = bk.mp;
-  }
-  const char* A = a + (int64_t)ti * kSmallTile * ld * ES;
-  const char* A2 = a2 ? a2 + (int64_t)ti * kSmallTile * ld * ES : nullptr;
-  const char* B = b + (int64_t)tj * kSmallTile * ld * ES;
-  const int nk = (int)(K / kSmCK);
+  const Operands op = slice_operands<T, Ph>(bk, rbuf, z);
+  const int64_t ld = op.ld;
+  const char* A = op.a + (int64_t)ti * kSmallTile * ld * ES;
+  const char* A2 = op.a2 ? op.a2 + (int64_t)ti * kSmallTile * ld * ES : nullptr;
+  const char* B = op.b + (int64_t)tj * kSmallTile * ld * ES;
+  const int nk = (int)(op.K / kSmCK);
   const int total = A2 ? 2 * nk : nk;  // with a bf16 hi/lo pair: the hi part's chunks, then the lo part's
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -534,8 +437,7 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs g) {
       for (int s2 = 0; s2 < 2; ++s2) {
         const int c = 4 * wave + 2 * s2 + half;
         const u32x4_t av = frag(As, r, c), bv = frag(Bs, r, c);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                      __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+        acc = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv), acc);
       }
     } else {
       // 32 k per wave in 4 groups of 8: lane l reads 4 consecutive k (16 bytes)
@@ -546,10 +448,10 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs g) {
         const int c = 8 * wave + 2 * s4 + half;
         const f32x4_t av = __builtin_bit_cast(f32x4_t, frag(As, r, c));
         const f32x4_t bv = __builtin_bit_cast(f32x4_t, frag(Bs, r, c));
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bv.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bv.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bv.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bv.w, acc, 0, 0, 0);
+        acc = mfma_f32(av.x, bv.x, acc);
+        acc = mfma_f32(av.y, bv.y, acc);
+        acc = mfma_f32(av.z, bv.z, acc);
+        acc = mfma_f32(av.w, bv.w, acc);
       }
     }
     if (it + 1 < total) sstore(cur ^ 1);
@@ -570,31 +472,157 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs g) {
     const int e = (i0 + u) * 33 + col;
     v[u] = ((red[e] + red[32 * 33 + e]) + red[2 * 32 * 33 + e]) + red[3 * 32 * 33 + e];
   }
-  const int gi = ti * kSmallTile + i0, gj = tj * kSmallTile + col;
-  if constexpr (Ph == 0) {
-    GramEpi{bk.a32, nullptr, g.first ? bk.scale : nullptr, bk.mp}(z, gi, gj, v);
-  } else if constexpr (Ph == 1) {
-    PolyEpi{bk.a32, bk.phi, bk.plo, bk.plo == nullptr, g.sc, bk.mp}(z, gi, gj, v);
-  } else if constexpr (Ph == 2) {
-    ApplyEpi<T>{reinterpret_cast<const T*>(x_src), reinterpret_cast<T*>(x_dst), reinterpret_cast<T*>(xt_dst),
-                g.first ? bk.scale : nullptr, g.sc, bk.mp, bk.np}(z, gi, gj, v);
-  } else {
-    FinalEpi<T>{reinterpret_cast<const T*>(x_src), g.first ? bk.scale : nullptr, g.sc, bk.mats, g.ptrs,
-                bk.mp, bk.np, bk.m, bk.n}(z, gi, gj, v);
-  }
+  phase_epilogue<T, Ph>(g, bk, rbuf, z, ti * kSmallTile + i0, tj * kSmallTile + col, v);
 }
 
-template <typename T, class Epi>
-hipError_t run_gemm(GemmCore c, const Epi& e, int64_t rows, int64_t cols, int count, hipStream_t s) {
-  // rows and cols are multiples of 128 (the workspace padding).
-  if ((rows / 128) * (cols / 128) * count < 256) {
-    c.tiles_n = (int)(cols / 64);
-    hipLaunchKernelGGL((k_gemm<T, Epi, 64>), dim3((int)(rows / 64) * c.tiles_n, 1, count), dim3(256), 0, s, c, e);
-  } else {
-    c.tiles_n = (int)(cols / 128);
-    hipLaunchKernelGGL((k_gemm<T, Epi, 128>), dim3((int)(rows / 128) * c.tiles_n, 1, count), dim3(256), 0, s, c, e);
+// ------------------------------------------------------------------ tiled products
+// The other streamed buckets (padded m > 256 and not on the large tiles: the
+// float32 mode, and bf16 slices the large tiles do not take).  BT x BT output
+// tile per 256-thread workgroup (BT = 128, or 64 where the launch would have
+// fewer 128-tiles than the chip has CUs); 4 waves in a 2 x 2 grid, each
+// computing BT/2 x BT/2 with 32x32 matrix-core instructions.  k-slices of 64
+// bytes per row are staged through LDS, double buffered.  Every output entry
+// takes its k steps in the same order whatever BT is, so the tile size does
+// not change a single bit of the result.
+constexpr int kRowBytes = 64;       // bytes of k per operand row per stage
+constexpr int kLdsRow = kRowBytes + 16;
+
+template <typename T, int Ph, int BT>
+__global__ __launch_bounds__(256) void k_mid(SmallArgs g) {
+  constexpr int ES = (int)sizeof(T);
+  constexpr int BK = kRowBytes / ES;
+  constexpr int X = BT / 64;  // 32x32 blocks per wave along i and along j
+  constexpr int H = BT / 64;  // 16-byte loads per thread, operand and slice
+  constexpr int WT = BT / 2;  // rows (columns) per wave
+  constexpr int PH = grid_phase<Ph>();
+  __shared__ __attribute__((aligned(16))) char lds[2][2][BT * kLdsRow];
+
+  const int wg = blockIdx.x;
+  const SmallBucket bk = find_bucket<PH>(g, wg);
+  const RoundBuffers rbuf = round_buffers(bk, g.src);
+  const int64_t tj_n = (PH == 2 ? bk.np : bk.mp) / BT, ti_n = bk.mp / BT;
+  const int64_t local = wg - bk.t0[PH];
+  const int z = (int)(local / (ti_n * tj_n));
+  const int64_t t = local - (int64_t)z * ti_n * tj_n;
+  const int tm = (int)(t / tj_n), tn = (int)(t - (t / tj_n) * tj_n);
+
+  const Operands op = slice_operands<T, Ph>(bk, rbuf, z);
+  const int64_t ld = op.ld;
+  const char* A = op.a + (int64_t)tm * BT * ld * ES;
+  const char* A2 = op.a2 ? op.a2 + (int64_t)tm * BT * ld * ES : nullptr;
+  const char* B = op.b + (int64_t)tn * BT * ld * ES;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int row[H], c16[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    const int idx = tid + 256 * h;
+    row[h] = idx >> 2;
+    c16[h] = idx & 3;
   }
-  return hipGetLastError();
+  u32x4_t ra[H], rb[H];
+  const int nk = (int)(op.K / BK);
+  const int total = A2 ? 2 * nk : nk;  // with a bf16 hi/lo pair: the hi part's slices, then the lo part's
+
+  auto gload = [&](int it) {
+    const int kt = it % nk;
+    const char* Ab = it >= nk ? A2 : A;
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const int64_t off = ((int64_t)row[h] * ld + (int64_t)kt * BK) * ES + c16[h] * 16;
+      ra[h] = *reinterpret_cast<const MUON_GLOBAL u32x4_t*>(as_global(Ab + off));
+      rb[h] = *reinterpret_cast<const MUON_GLOBAL u32x4_t*>(as_global(B + off));
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      *reinterpret_cast<u32x4_t*>(&lds[buf][0][row[h] * kLdsRow + c16[h] * 16]) = ra[h];
+      *reinterpret_cast<u32x4_t*>(&lds[buf][1][row[h] * kLdsRow + c16[h] * 16]) = rb[h];
+    }
+  };
+
+  f32x16_t acc[X][X];
+#pragma unroll
+  for (int x = 0; x < X; ++x)
+#pragma unroll
+    for (int y = 0; y < X; ++y) acc[x][y] = f32x16_t{};
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int it = 0; it < total; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < total) gload(it + 1);
+    const char* As = lds[cur][0];
+    const char* Bs = lds[cur][1];
+    if constexpr (ES == 2) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8_t af[X], bf[X];
+#pragma unroll
+        for (int x = 0; x < X; ++x)
+          af[x] = *reinterpret_cast<const bf16x8_t*>(As + (wm * WT + x * 32 + (lane & 31)) * kLdsRow + s * 32 + (lane >> 5) * 16);
+#pragma unroll
+        for (int y = 0; y < X; ++y)
+          bf[y] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WT + y * 32 + (lane & 31)) * kLdsRow + s * 32 + (lane >> 5) * 16);
+#pragma unroll
+        for (int x = 0; x < X; ++x)
+#pragma unroll
+          for (int y = 0; y < X; ++y) acc[x][y] = mfma_bf16(af[x], bf[y], acc[x][y]);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        float af[X], bf[X];
+#pragma unroll
+        for (int x = 0; x < X; ++x)
+          af[x] = *reinterpret_cast<const float*>(As + (wm * WT + x * 32 + (lane & 31)) * kLdsRow + (s * 2 + (lane >> 5)) * 4);
+#pragma unroll
+        for (int y = 0; y < X; ++y)
+          bf[y] = *reinterpret_cast<const float*>(Bs + (wn * WT + y * 32 + (lane & 31)) * kLdsRow + (s * 2 + (lane >> 5)) * 4);
+#pragma unroll
+        for (int x = 0; x < X; ++x)
+#pragma unroll
+          for (int y = 0; y < X; ++y) acc[x][y] = mfma_f32(af[x], bf[y], acc[x][y]);
+      }
+    }
+    if (it + 1 < total) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Output layout of a 32x32 block: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32.
+#pragma unroll
+  for (int x = 0; x < X; ++x)
+#pragma unroll
+    for (int y = 0; y < X; ++y)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i0 = tm * BT + wm * WT + x * 32 + 8 * q + 4 * (lane >> 5);
+        const int j = tn * BT + wn * WT + y * 32 + (lane & 31);
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = acc[x][y][4 * q + u];
+        phase_epilogue<T, Ph>(g, bk, rbuf, z, i0, j, v);
+      }
+}
+
+template <int BT>
+void launch_mid_bt(int phase, bool final_round, bool f32_operands, const SmallArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 block(256);
+  if (phase == 1) {
+    hipLaunchKernelGGL((k_mid<float, 1, BT>), grid, block, 0, s, a);  // A is float32 in both modes
+  } else if (phase == 0) {
+    if (f32_operands) hipLaunchKernelGGL((k_mid<float, 0, BT>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_mid<uint16_t, 0, BT>), grid, block, 0, s, a);
+  } else if (final_round) {
+    if (f32_operands) hipLaunchKernelGGL((k_mid<float, 3, BT>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_mid<uint16_t, 3, BT>), grid, block, 0, s, a);
+  } else {
+    if (f32_operands) hipLaunchKernelGGL((k_mid<float, 2, BT>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_mid<uint16_t, 2, BT>), grid, block, 0, s, a);
+  }
 }
 
 }  // namespace
@@ -615,62 +643,6 @@ hipError_t launch_norm(const NormLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gram(const GramLaunch& a, hipStream_t s) {
-  GemmCore c{};
-  c.a = static_cast<const char*>(a.x);
-  c.a2 = nullptr;
-  c.b = c.a;
-  c.lda = c.ldb = a.np;
-  c.sa = c.sb = a.mp * a.np;
-  c.K = a.np;
-  GramEpi e{a.a32, a.a16, a.scale, a.mp};
-  return a.x_bytes == 2 ? run_gemm<uint16_t>(c, e, a.mp, a.mp, a.count, s)
-                        : run_gemm<float>(c, e, a.mp, a.mp, a.count, s);
-}
-
-hipError_t launch_poly(const PolyLaunch& a, hipStream_t s) {
-  GemmCore c{};
-  c.a = static_cast<const char*>(a.op);
-  c.a2 = nullptr;
-  c.b = c.a;
-  c.lda = c.ldb = a.mp;
-  c.sa = c.sb = a.mp * a.mp;
-  c.K = a.mp;
-  PolyEpi e{a.a32, a.phi, a.plo, a.p_bytes == 4, a.sc, a.mp};
-  return a.op_bytes == 2 ? run_gemm<uint16_t>(c, e, a.mp, a.mp, a.count, s)
-                         : run_gemm<float>(c, e, a.mp, a.mp, a.count, s);
-}
-
-hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
-  GemmCore c{};
-  c.a = static_cast<const char*>(a.phi);
-  c.a2 = static_cast<const char*>(a.plo);
-  c.b = static_cast<const char*>(a.xt_old);
-  c.lda = a.mp;
-  c.ldb = a.mp;
-  c.sa = a.mp * a.mp;
-  c.sb = a.np * a.mp;
-  c.K = a.mp;
-  if (a.x_bytes == 2) {
-    if (a.final_round) {
-      FinalEpi<uint16_t> e{static_cast<const uint16_t*>(a.x_old), a.scale, a.sc, a.mats, a.ptrs,
-                           a.mp, a.np, a.m, a.n};
-      return run_gemm<uint16_t>(c, e, a.mp, a.np, a.count, s);
-    }
-    ApplyEpi<uint16_t> e{static_cast<const uint16_t*>(a.x_old), static_cast<uint16_t*>(a.x_new),
-                         static_cast<uint16_t*>(a.xt_new), a.scale, a.sc, a.mp, a.np};
-    return run_gemm<uint16_t>(c, e, a.mp, a.np, a.count, s);
-  }
-  if (a.final_round) {
-    FinalEpi<float> e{static_cast<const float*>(a.x_old), a.scale, a.sc, a.mats, a.ptrs,
-                      a.mp, a.np, a.m, a.n};
-    return run_gemm<float>(c, e, a.mp, a.np, a.count, s);
-  }
-  ApplyEpi<float> e{static_cast<const float*>(a.x_old), static_cast<float*>(a.x_new),
-                    static_cast<float*>(a.xt_new), a.scale, a.sc, a.mp, a.np};
-  return run_gemm<float>(c, e, a.mp, a.np, a.count, s);
-}
-
 hipError_t launch_small(int phase, bool final_round, bool f32_operands, const SmallArgs& a, int64_t wgs,
                         hipStream_t s) {
   const dim3 grid((unsigned)wgs), block(256);
@@ -686,6 +658,14 @@ hipError_t launch_small(int phase, bool final_round, bool f32_operands, const Sm
     if (f32_operands) hipLaunchKernelGGL((k_small<float, 2>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_small<uint16_t, 2>), grid, block, 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_mid(int phase, bool final_round, bool f32_operands, const SmallArgs& a, int64_t wgs, int bt,
+                      hipStream_t s) {
+  const dim3 grid((unsigned)wgs);
+  if (bt == 64) launch_mid_bt<64>(phase, final_round, f32_operands, a, grid, s);
+  else launch_mid_bt<128>(phase, final_round, f32_operands, a, grid, s);
   return hipGetLastError();
 }
 

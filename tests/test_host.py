@@ -149,12 +149,11 @@ def test_skinny_buckets_share_three_launches(m):
     assert info["launches_fixed"] == 3 and info["launches_per_ns"] == 0
 
 
-def test_small_streamed_buckets_share_three_launches_per_round(m):
-    """Every streamed bucket with padded m <= 256 (m <= 256) that does not
-    take the large tiles runs each product phase of a round in one launch
-    with the others.  In float32 mode that is every such bucket, and a bucket
-    with larger m takes its own three launches.  In bf16 mode the buckets with
-    m >= 129 share the three large-tile launches instead."""
+def test_streamed_groups_share_three_launches_per_round(m):
+    """The streamed buckets run their rounds in groups, three launches per
+    round each: the small buckets (padded m <= 256), the other buckets that
+    do not take the large tiles, and the large-tile buckets (bf16 mode,
+    m >= 129 by default)."""
     shapes = [(100, 300), (200, 150), (64, 64), (3, 40, 500), (256, 1000)]
     d = m.make_descs(shapes, ["f32"] * 5, ["bf16"] * 5)
     for mode, launches in (("bf16", 3 + 3), ("fp32", 3)):
@@ -163,14 +162,15 @@ def test_small_streamed_buckets_share_three_launches_per_round(m):
         assert info["launches_per_ns"] == launches, mode
     small = m.make_descs([(100, 300), (64, 64), (3, 40, 500), (128, 4000)], ["f32"] * 4, ["bf16"] * 4)
     assert m.info_dict(m.muon_plan_describe(small, m.make_opts(mode="bf16")))["launches_per_ns"] == 3
-    mixed = m.make_descs(shapes + [(300, 520), (600, 700)], ["f32"] * 7, ["bf16"] * 7)
-    assert m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="bf16")))["launches_per_ns"] == 3 + 3
-    assert m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="fp32")))["launches_per_ns"] == 3 + 3 + 3
+    mixed = m.make_descs(shapes + [(300, 520), (600, 700), (1000, 1100)], ["f32"] * 8, ["bf16"] * 8)
+    info = m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="bf16")))
+    assert info["launches_per_ns"] == 3 + 3 and info["launches_fixed"] == 2 * 8
+    assert m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="fp32")))["launches_per_ns"] == 3 + 3
     # large_min_m moves the threshold (-1: no large tiles)
     off = m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="bf16", large_min_m=-1)))
-    assert off["launches_per_ns"] == 3 + 3 + 3
+    assert off["launches_per_ns"] == 3 + 3
     high = m.info_dict(m.muon_plan_describe(mixed, m.make_opts(mode="bf16", large_min_m=301)))
-    assert high["launches_per_ns"] == 3 + 3 + 3   # small group, [300,520] alone, [600,700] large
+    assert high["launches_per_ns"] == 3 + 3 + 3   # small group, [300,520] in the other group, the rest large
     low = m.info_dict(m.muon_plan_describe(small, m.make_opts(mode="bf16", large_min_m=65)))
     assert low["launches_per_ns"] == 3 + 3        # m = 64 and 40 stay small; m = 100 and 128 go large
     assert m.info_dict(m.muon_plan_describe(small, m.make_opts(mode="bf16", large_min_m=33)))["launches_per_ns"] == 3
