@@ -140,6 +140,31 @@ def test_fusion_is_bitexact(mode):
 
 
 @pytest.mark.parametrize("mode", ["bf16", "fp32"])
+def test_tiled_group_fusion_is_bitexact(mode):
+    """Streamed buckets with padded m > 256 off the large tiles share one
+    launch per product phase: here three oriented shapes (stored both ways,
+    and in 3-D stacks) next to a small bucket.  The fused apply launch has
+    266 tiles of 128 and takes 128-tiles; a single slice takes 64-tiles.
+    Each slice must still get the bits of a plan of its own, and meet the
+    bar.  (bf16 mode with the large tiles off.)"""
+    shapes = [(300, 520), (520, 300), (2, 260, 700), (3, 400, 1200), (400, 1200), (1200, 400), (96, 200)]
+    params, grads, moms = make_inputs(shapes, "bf16", 23, w_std=0.02, m_std=1e-3)
+    kw = dict(mode=mode, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q, plan_kw=dict(large_min_m=-1))
+    w_f, m_f = gpu_step(params, grads, moms, **kw)
+    _, _, o_ref = oracle_step(params, grads, moms, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    for i, shp in enumerate(shapes):
+        errs = update_errors(w_f[i], params[i], 0.02, o_ref[i], TOL[mode])
+        assert max(errs) <= TOL[mode], (shp, max(errs))
+        if len(shp) == 3:
+            for e in range(shp[0]):
+                w_1, m_1 = gpu_step([params[i][e]], [grads[i][e]], [moms[i][e]], **kw)
+                assert np.array_equal(w_f[i][e], w_1[0]) and np.array_equal(m_f[i][e], m_1[0]), (i, e)
+        else:
+            w_1, m_1 = gpu_step([params[i]], [grads[i]], [moms[i]], **kw)
+            assert np.array_equal(w_f[i], w_1[0]) and np.array_equal(m_f[i], m_1[0]), i
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
 def test_small_product_tile_size_is_bitexact(mode):
     """Streamed buckets with padded m above 256 take 128 x 128 tiles when a
     launch has at least 256 of them, else 64 x 64 tiles; each output entry
