@@ -51,6 +51,33 @@ def compulsory_bytes(wl: workloads.Workload) -> float:
     return tot
 
 
+def stream_model(wl: workloads.Workload, mode: str):
+    """The streaming cost model of a step: B_stream, the bytes a design moves
+    when X leaves the chip between the Gram and the apply of every round,
+    m n (s_G + 8 + 2 s_W + (3k + 2) s_X) + k m^2 (8 + 2 s_X) per oriented
+    slice; and T_roof, the sum over same-shape buckets of
+    max(F / matrix-core peak, B_stream / 8 TB/s), F = k (4 m^2 n + 2 m^3).
+    The skinny path's Gram-space rounds skip the per-round X passes, so
+    B_stream / t can exceed the HBM peak there."""
+    k = wl.ns_steps
+    s_x = 2 if mode == "bf16" else 4
+    buckets = {}
+    for p in wl.params:
+        r, c = p.shape[-2:]
+        e = p.shape[0] if len(p.shape) == 3 else 1
+        m, n = min(r, c), max(r, c)
+        b = m * n * (elem_bytes(p.grad_dtype) + 8 + 2 * elem_bytes(p.param_dtype) + (3 * k + 2) * s_x) \
+            + k * m * m * (8 + 2 * s_x)
+        f = k * (4.0 * m * m * n + 2.0 * m ** 3)
+        key = (m, n, p.grad_dtype, p.param_dtype)
+        fb = buckets.setdefault(key, [0.0, 0.0])
+        fb[0] += e * f
+        fb[1] += e * b
+    b_stream = sum(v[1] for v in buckets.values())
+    t_roof = sum(max(f / (MFMA_PEAK_TFLOPS[mode] * 1e12), b / (HBM_PEAK_GBS * 1e9)) for f, b in buckets.values())
+    return b_stream, t_roof
+
+
 def make_gpu_inputs(wl: workloads.Workload, dev):
     """Seeded synthetic inputs generated on the device (same recipe as the
     host generator: Gaussian gradients of the workload's std, stored in the
@@ -379,11 +406,14 @@ def measure(wl: workloads.Workload, mode: str, steps: int, warmup: int, dev, gra
 
     dense = wl.flops()
     comp = compulsory_bytes(wl)
+    b_stream, t_roof = stream_model(wl, mode)
     return {
         "ms": ms, "wall_ms": wall * 1e3 / steps, "pct": step_pct, "graph_ms": graph_ms,
         "value": wl.n_matrices / (ms * 1e-3), "dense_tflops": dense / (ms * 1e-3) / 1e12,
         "own_tflops": own_total / (ms * 1e-3) / 1e12, "own_flops": own_total, "dense_flops": dense,
         "compulsory_gbs": comp / (ms * 1e-3) / 1e9, "roofline": roof,
+        "stream_model_gbs": b_stream / (ms * 1e-3) / 1e9, "stream_model_bytes": b_stream,
+        "t_roof_ms": t_roof * 1e3,
         "kernels_ms_per_step": {k: round(v[0], 5) for k, v in kernel_ms.items()},
         "launches_per_step": info["launches_fixed"] + info["launches_per_ns"] * wl.ns_steps,
         "device_error": status,
@@ -422,7 +452,7 @@ def main():
 
     def defaults(wl):
         big = wl.flops() > 1e13
-        return (10, 2) if big else (200, 10)
+        return (10, 3) if big else (200, 10)
 
     wl = workloads.WORKLOADS[args.workload]
     mode = args.mode or wl.mode
@@ -443,6 +473,9 @@ def main():
             "own_work_frac": round(xr["own_tflops"] / MFMA_PEAK_TFLOPS[xw.mode], 4),
             "compulsory_gbs": round(xr["compulsory_gbs"], 1),
             "compulsory_frac": round(xr["compulsory_gbs"] / HBM_PEAK_GBS, 4),
+            "stream_model_gbs": round(xr["stream_model_gbs"], 1),
+            "stream_model_frac": round(xr["stream_model_gbs"] / HBM_PEAK_GBS, 4),
+            "t_roof_ms": round(xr["t_roof_ms"], 5), "t_roof_frac": round(xr["t_roof_ms"] / xr["ms"], 4),
             "roofline": {k: roof[k] for k in ("bound", "kernel", "achieved", "unit", "frac", "traffic")},
             "kernels_ms_per_step": xr["kernels_ms_per_step"], "device_error": xr["device_error"],
         }
@@ -474,6 +507,12 @@ def main():
         "own_work_flops_per_step": r["own_flops"],
         "compulsory_gbs": round(r["compulsory_gbs"], 1),
         "compulsory_frac": round(r["compulsory_gbs"] / HBM_PEAK_GBS, 4),
+        # the streaming cost model: X written and read back every round
+        "stream_model_bytes_per_step": r["stream_model_bytes"],
+        "stream_model_gbs": round(r["stream_model_gbs"], 1),
+        "stream_model_frac": round(r["stream_model_gbs"] / HBM_PEAK_GBS, 4),
+        "t_roof_ms": round(r["t_roof_ms"], 5),
+        "t_roof_frac": round(r["t_roof_ms"] / r["ms"], 4),
         "roofline": r["roofline"],
         "kernels_ms_per_step": r["kernels_ms_per_step"],
         "launches_per_step": r["launches_per_step"],
