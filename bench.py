@@ -465,10 +465,11 @@ def main():
     for name in [x for x in args.also.split(",") if x and x != "none" and x != wl.name]:
         xw = workloads.WORKLOADS[name]
         xs, xwu = defaults(xw)
-        xr = measure(xw, xw.mode, xs, xwu, dev, graph=False)
+        xr = measure(xw, xw.mode, xs, xwu, dev, graph=not args.no_graph)
         roof = xr["roofline"]
         extras[name] = {
             "ms_per_step": round(xr["ms"], 5), "matrices_per_s": round(xr["value"], 3), "steps": xs,
+            "graph_ms_per_step": None if xr["graph_ms"] is None else round(xr["graph_ms"], 5),
             "dense_tflops": round(xr["dense_tflops"], 2), "own_work_tflops": round(xr["own_tflops"], 2),
             "own_work_frac": round(xr["own_tflops"] / MFMA_PEAK_TFLOPS[xw.mode], 4),
             "compulsory_gbs": round(xr["compulsory_gbs"], 1),
@@ -520,7 +521,18 @@ def main():
         "extra_workloads": extras,
     }
     if not args.no_ceilings:
-        out["ceilings"] = measure_ceilings(dev)
+        out["ceilings"] = ceil = measure_ceilings(dev)
+        # The same achieved rates against what this machine measured: the
+        # library bf16 GEMM for matrix-core classes, the device copy for
+        # HBM-bound ones.
+        def vs_ceiling(roof, mode_):
+            if roof.get("bound") == "mfma" and mode_ == "bf16":
+                roof["frac_of_library_gemm"] = round(roof["achieved"] / ceil["library_bf16_gemm_tflops"], 4)
+            elif roof.get("bound") == "hbm":
+                roof["frac_of_copy"] = round(roof["achieved"] / ceil["copy_gbs"], 4)
+        vs_ceiling(out["roofline"], mode)
+        for name, x in extras.items():
+            vs_ceiling(x["roofline"], workloads.WORKLOADS[name].mode)
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, args.cpu_budget_fp32)
     print(json.dumps(out), flush=True)
