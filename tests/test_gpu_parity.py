@@ -462,11 +462,12 @@ def test_zero_gradient_slices(mode):
 
 
 @pytest.mark.parametrize("shape,mode", [((96, 160), "fp32"), ((96, 160), "bf16"), ((600, 700), "bf16"),
-                                        ((700, 600), "bf16")])
+                                        ((700, 600), "bf16"), ((600, 700), "fp32")])
 def test_nonfinite_gradient_streamed_paths(shape, mode):
     """An infinite gradient entry in a slice of the streamed paths (the
-    128-tile products, and the large products in bf16 mode) sets bit 0 of
-    the device error word, like the skinny path."""
+    32-tile products, the tiled products of float32 mode and the large
+    products of bf16 mode) sets bit 0 of the device error word, like the
+    skinny path."""
     import torch
 
     from muon_newton_schulz_05_amd import MuonPlan
