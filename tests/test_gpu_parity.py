@@ -115,6 +115,22 @@ def test_nonzero_state_and_bf16_params(mode):
         assert err <= bound, (i, err, bound)
 
 
+def test_tiled_products_bf16_weights():
+    """float32 mode, slices on the tiled products (padded m > 256), stored
+    both ways, with bf16 weights and nonzero state: the last round's
+    epilogue reads and writes W in bf16 (rounded to nearest even)."""
+    import oracle
+    shapes = [(600, 700), (700, 600), (2, 300, 520)]
+    params, grads, moms = make_inputs(shapes, "bf16", 19, param_dtypes="bf16", w_std=0.02, m_std=1e-3)
+    w_gpu, _ = gpu_step(params, grads, moms, mode="fp32", lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    w_ref, _, o_ref = oracle_step(params, grads, moms, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q)
+    for i in range(len(shapes)):
+        err = np.linalg.norm(oracle.decode(w_gpu[i]) - w_ref[i])
+        bound = 2.0 ** -8 * np.linalg.norm(w_ref[i]) + 0.02 * TOL["fp32"] * np.linalg.norm(o_ref[i])
+        print(f"{shapes[i]} bf16 W fp32 mode: {err:.3e} (bound {bound:.3e})")
+        assert err <= bound, (i, err, bound)
+
+
 @pytest.mark.parametrize("mode", ["bf16", "fp32"])
 def test_three_steps(mode):
     check([(24, 1500), (130, 260)], mode, steps=3, lr=0.02, w_std=0.02, tol=TOL[mode])
