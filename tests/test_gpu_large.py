@@ -22,10 +22,10 @@ Q = (3.4445, -4.7750, 2.0315)
 BAR = TOL["bf16"]
 
 
-def _check(shapes, *, ns=5, steps=1, param_dtypes=None, w_std=0.0, m_std=0.0, seed=3, lr=1.0):
+def _check(shapes, *, ns=5, steps=1, param_dtypes=None, w_std=0.0, m_std=0.0, seed=3, lr=1.0, plan_kw=None):
     params, grads, moms = make_inputs(shapes, "bf16", seed, 1e-3, param_dtypes, w_std, m_std)
     w_gpu, m_gpu = gpu_step(params, grads, moms, mode="bf16", lr=lr, beta=0.95, ns_steps=ns, coeffs=Q,
-                            steps=steps)
+                            steps=steps, plan_kw=plan_kw)
     w_ref, m_ref, o_ref = oracle_step(params, grads, moms, lr=lr, beta=0.95, ns_steps=ns, coeffs=Q,
                                       steps=steps)
     worst = 0.0
@@ -57,6 +57,14 @@ def test_mid_shapes(shape):
     rows, so every tile of the symmetric phases sits on the diagonal, and
     m = 129 leaves all but one row of its tile row as padding."""
     _check([shape])
+
+
+@pytest.mark.parametrize("shape", [(33, 500), (40, 400), (64, 1024), (1024, 64), (100, 300), (2, 120, 777)])
+def test_large_tiles_down_to_m_33(shape):
+    """large_min_m = 33 puts every streamed bf16 slice on the large tiles:
+    one tile row holding 33 to 128 rows of the slice, so the waves of rows
+    128 .. 255 of every symmetric tile skip their products."""
+    _check([shape], plan_kw=dict(large_min_m=33))
 
 
 def test_large_fusion_is_bitexact():
