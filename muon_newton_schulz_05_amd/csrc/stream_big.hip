@@ -42,9 +42,11 @@
 // (the 32 workgroups an XCD runs at once share 4 row and 8 column panels in
 // its L2), longest contraction first, with the work balanced over the XCDs.
 // Symmetric products (X X^T, E E) list only tiles on or above the diagonal
-// (on slices with a padded last tile row they compute the mirrors below it,
-// and waves whose rows all lie past m skip their products); the bf16 result
-// of an off-diagonal tile is also written to its mirror position.  The
+// (on slices with a padded last tile row they compute the mirrors below it);
+// the bf16 result of an off-diagonal tile is also written to its mirror
+// position.  A tile of a last tile row with at most 128 rows inside m is a
+// half tile: it computes those 128 rows only, the eight waves taking 64 x 64
+// each.  The
 // epilogue turns the accumulators around in LDS and writes
 // whole rows of 16-byte pieces.  Where a transposed copy holds the same values
 // (the mirror tiles, and X'^T next to X'), it is read out of LDS after the
@@ -67,10 +69,14 @@ constexpr int kWavesBig = 8;                 // waves per workgroup: 2 along i, 
 constexpr int kThreadsBig = 64 * kWavesBig;
 constexpr int kLI = kBigTile / kRPI / kWavesBig;  // load instructions per wave, operand and slice
 constexpr int kStage = 2 * kBigTile * kRB;   // bytes per stage (A and B tiles)
+constexpr int kNSHalf = 3;                   // LDS stages of a half tile's loop
+constexpr int kStageHalf = (128 + kBigTile) * kRB;  // its stage: 128 rows of A, 256 of B
 constexpr int kStageBytes = 128 * 256 * 4;   // epilogue staging: 128 rows of 256 floats
-constexpr int kLds = kNS * kStage > kStageBytes ? kNS * kStage : kStageBytes;
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int kLds = cmax(cmax(kNS * kStage, kNSHalf * kStageHalf), kStageBytes);
 constexpr int kViewRow = 1, kViewCol = 2;
-static_assert(kBK % 16 == 0 && kCPR <= 8 && kNS >= 2 && kLds <= 160 * 1024, "tile geometry");
+static_assert(kBK % 16 == 0 && kCPR <= 8 && kNS >= 2 && kNSHalf >= 2 && kLds <= 160 * 1024 && kLI % 2 == 0,
+              "tile geometry");
 
 #define LDS_PTR __attribute__((address_space(3)))
 
@@ -86,14 +92,16 @@ __device__ __forceinline__ int swz(int r) { return (r / kRW) & (kCPR - 1); }
 // the transposed readout gathers at once sit in distinct slots.
 __device__ __forceinline__ int stage_swz(int r) { return ((r >> 3) & 15) ^ (((r >> 2) & 1) << 3); }
 
-// Wait until at most `slices` k-slices of this wave's operand loads are in flight.
+// Wait until at most `slices` k-slices of this wave's operand loads (L load
+// instructions per slice) are in flight.
+template <int L>
 __device__ __forceinline__ void wait_loads(int slices) {
-  static_assert(kNS - 2 <= 3, "extend the cases");
+  static_assert(kNS - 2 <= 3 && kNSHalf - 2 <= 3 && 3 * L < 64, "extend the cases");
   switch (slices) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLI) : "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kLI) : "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * kLI) : "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * L) : "memory"); break;
   }
 }
 
@@ -146,15 +154,25 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   // The wave index is uniform over the wave; saying so keeps branches on it scalar.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;  // 128 rows x 64 columns per wave
-  // The symmetric products X X^T and E E are zero in their rows past m,
-  // where X and E are zero.  In those phases a wave whose 128 rows all lie
-  // past m skips its products, and its accumulators keep the zero they
-  // would give.  Those waves (4..7) sit one on each SIMD, so every matrix
-  // core of a half-padded tile runs half loaded.  (The apply's padded tile
-  // row gained nothing from the same skip, and the branch slowed its
-  // loop, so it has none.)
-  const bool idle = Epi::kLower && wm == 1 && bb.m - (int64_t)tm * kBigTile <= 128;
+  const int wm = wave >> 2, wn = wave & 3;
+  // Half tiles (the symmetric products).  X and E are zero in their rows
+  // past m, and so are X X^T and E E.  In the last tile row of a slice with
+  // at most 128 real rows there (the phases' padded row, Epi::kLower), the
+  // tile's rows 128..255 are therefore zero, which the workspace already
+  // holds (it is cleared once, and nothing writes anything else there).
+  // Such a tile computes its first 128 rows only: the eight waves take
+  // 64 x 64 each (2 x 2 blocks) instead of 128 x 64 (4 x 2), only those 128
+  // rows of the first operand are loaded, and the epilogue writes one half.
+  // It takes about half a tile's time, in the same launch as the full
+  // tiles, which fills the last wave of tiles better.  (The apply and final
+  // phases have none: on launches that fill the chip their half tiles were
+  // no faster, and their presence made the compiler's code for the full
+  // tiles' X term below 1% slower.)
+  const bool half = Epi::kLower && bb.m - (int64_t)tm * kBigTile <= 128;
+  // The symmetric products are zero in their columns past m as well: on a
+  // half tile on the diagonal, a wave whose 64 columns all lie past m skips
+  // its products, and its accumulators keep the zero they would give.
+  const bool idle = Epi::kLower && half && (int64_t)tn * kBigTile + wn * 64 >= bb.m;
   const char* A = op.a + (int64_t)tm * kBigTile * op.lda * 2;
   const char* B = op.b + (int64_t)tn * kBigTile * op.ldb * 2;
   const int nk = (int)(op.K / kBK);
@@ -170,16 +188,25 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
     oa[u] = (uint32_t)(row * op.lda * 2 + chunk * 16);
     ob[u] = (uint32_t)(row * op.ldb * 2 + chunk * 16);
   }
-  auto issue = [&](int kt, int stage) {
-    char LDS_PTR* base = (char LDS_PTR*)(lds + stage * kStage);
+  // A half tile loads rows 0..127 of the first operand only (u < kLI / 2),
+  // into stages of its own size (B at stage row 128), kNSHalf deep: with
+  // half the products per slice, one slice in flight left its loop waiting
+  // on the loads.  The swizzle of B-stage row 128 + r (or 256 + r) equals
+  // that of operand row r.
+  auto issue = [&](int kt, int stage, auto half_tag) {
+    constexpr bool H = decltype(half_tag)::value;
+    constexpr int kLA = H ? kLI / 2 : kLI;
+    constexpr int kStg = H ? kStageHalf : kStage;
+    constexpr int kOffB = (H ? 128 : kBigTile) * kRB;
+    char LDS_PTR* base = (char LDS_PTR*)(lds + stage * kStg);
 #pragma unroll
-    for (int u = 0; u < kLI; ++u)
+    for (int u = 0; u < kLA; ++u)
       __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(A + (int64_t)kt * kRB + oa[u]),
                                        (void LDS_PTR*)(base + (wave + kWavesBig * u) * 1024), 16, 0, 0);
 #pragma unroll
     for (int u = 0; u < kLI; ++u)
       __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(B + (int64_t)kt * kRB + ob[u]),
-                                       (void LDS_PTR*)(base + kBigTile * kRB + (wave + kWavesBig * u) * 1024), 16, 0, 0);
+                                       (void LDS_PTR*)(base + kOffB + (wave + kWavesBig * u) * 1024), 16, 0, 0);
   };
 
   f32x16_t acc[FM][FN];
@@ -188,18 +215,23 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
-  const int ra = wm * 128 + (lane & 31), rb = kBigTile + wn * 64 + (lane & 31);
   // Multiply one resident slice.  The fragments of k-substep s + 1 are read
-  // from LDS while the 16 products of substep s run (two fragment sets), and
-  // the scheduling hints interleave one fragment read with every two
-  // products, so the matrix cores are not left waiting on LDS.
+  // from LDS while the products of substep s run (two fragment sets), and
+  // the scheduling hints interleave one fragment read with every product
+  // or two, so the matrix cores are not left waiting on LDS.  A half tile's
+  // wave takes the first FM / 2 blocks of its accumulators, rows 64 wm ..
+  // + 63 of the tile.
   constexpr int kSub = kBK / 16;
-  auto multiply = [&](const char* st) {
-    bf16x8_t af[2][FM], bfr[2][FN];
+  auto multiply = [&](const char* st, auto half_tag) {
+    constexpr bool H = decltype(half_tag)::value;
+    constexpr int F = H ? FM / 2 : FM;
+    const int ra = (H ? wm * 64 : wm * 128) + (lane & 31);
+    const int rb = (H ? 128 : kBigTile) + wn * 64 + (lane & 31);
+    bf16x8_t af[2][F], bfr[2][FN];
     auto fragments = [&](int s, int buf) {
       const int ck = 2 * s + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < F; ++i) {
         const int r = ra + 32 * i;
         af[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + r * kRB + ((ck ^ swz(r)) << 4));
       }
@@ -214,24 +246,24 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
     for (int s = 0; s < kSub; ++s) {
       if (s + 1 < kSub) fragments(s + 1, (s + 1) & 1);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < F; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(af[s & 1][i], bfr[s & 1][j], acc[i][j]);
     }
-    // Order: the first substep's 6 reads, then (1 product, 1 read) x 6 and
-    // 2 more products per following substep, then the last substep's 8
-    // products.
-    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+    // Order: the first substep's F + FN reads, then (1 product, 1 read)
+    // F + FN times and the remaining products per following substep, then
+    // the last substep's F FN products.
+    __builtin_amdgcn_sched_group_barrier(0x100, F + FN, 0);
 #pragma unroll
     for (int s = 0; s + 1 < kSub; ++s) {
 #pragma unroll
-      for (int q = 0; q < FM + FN; ++q) {
+      for (int q = 0; q < F + FN; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      if constexpr (F * FN > F + FN) __builtin_amdgcn_sched_group_barrier(0x008, F * FN - (F + FN), 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, F * FN, 0);
   };
 
   // Epi::kAddX (X + R X, second operand X^T): the k-slices whose k range is
@@ -244,7 +276,7 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   // 32 ii + 8 q + 4 (l / 32) + e of the slice, column l mod 32: four
   // consecutive k of B-stage row rb + 32 j, one 8-byte read.  (I0 is a
   // constant, so the accumulators stay in registers.)
-  auto add_x = [&](const char* st, auto i0_tag) {
+  auto add_x = [&](const char* st, int rb, auto i0_tag) {
     constexpr int I0 = decltype(i0_tag)::value;
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
@@ -261,31 +293,42 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
         }
   };
 
-  // kNS - 1 slices in flight.  Iteration kt: wait for this wave's loads of
-  // slice kt; one barrier then says that every wave's part of slice kt is in
-  // LDS and that every wave has finished reading slice kt - 1, whose stage is
-  // refilled with slice kt + kNS - 1 before slice kt is multiplied.  (One
+  // NS - 1 slices in flight (NS = kNS, or kNSHalf on a half tile).
+  // Iteration kt: wait for this wave's loads of slice kt; one barrier then
+  // says that every wave's part of slice kt is in LDS and that every wave
+  // has finished reading slice kt - 1, whose stage is refilled with slice
+  // kt + NS - 1 before slice kt is multiplied.  (One
   // loop: peeling the last slices off made the compiler spill the
   // accumulators around the epilogue.)
+  // The symmetric products run this loop, one copy for full and one for
+  // half tiles, chosen once per workgroup.  The apply phases run the same
+  // loop with the X term, written out in the kernel body below: inside a
+  // lambda, which is optimized before it is inlined, the X term's two calls
+  // were merged into one through a pointer, and the accumulators stayed on
+  // the stack.
+  auto main_loop = [&](auto half_tag) {
+    constexpr bool H = decltype(half_tag)::value;
+    constexpr int NS = H ? kNSHalf : kNS;
+    constexpr int kStg = H ? kStageHalf : kStage;
+    constexpr int L = (H ? kLI / 2 : kLI) + kLI;  // load instructions per slice and wave
+    const int rb = (H ? 128 : kBigTile) + wn * 64 + (lane & 31);
 #pragma unroll
-  for (int p = 0; p < kNS - 1; ++p)
-    if (p < nk) issue(p, p);
-  int stage = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_loads(min(kNS - 2, nk - 1 - kt));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");  // no LDS access moves across the barrier
-    if (kt + kNS - 1 < nk) issue(kt + kNS - 1, stage == 0 ? kNS - 1 : stage - 1);
-    if constexpr (Epi::kAddX) {
-      if ((kt >> 2) == tm && wm == ((kt & 3) >> 1)) {
-        if (kt & 1) add_x(lds + stage * kStage, std::integral_constant<int, 2>{});
-        else add_x(lds + stage * kStage, std::integral_constant<int, 0>{});
+    for (int p = 0; p < NS - 1; ++p)
+      if (p < nk) issue(p, p, half_tag);
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_loads<L>(min(NS - 2, nk - 1 - kt));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");  // no LDS access moves across the barrier
+      if (kt + NS - 1 < nk) issue(kt + NS - 1, stage == 0 ? NS - 1 : stage - 1, half_tag);
+      if constexpr (H) {
+        if (!idle) multiply(lds + stage * kStg, half_tag);
+      } else {
+        multiply(lds + stage * kStg, half_tag);
       }
+      stage = stage == NS - 1 ? 0 : stage + 1;
     }
-    if (!idle) multiply(lds + stage * kStage);
-    stage = stage == kNS - 1 ? 0 : stage + 1;
-  }
-  __syncthreads();  // every wave is done with the stages before they hold the epilogue
+  };
 
   // ---- epilogue.  Accumulator layout of a 32x32 block: lane l, register r ->
   // row 8 (r / 4) + 4 (l / 32) + r mod 4, column l mod 32.  Half of the tile
@@ -303,7 +346,8 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   const bool mirror = Epi::kMirror && (views & kViewCol);
   const float pre = Epi::prescale(cx);
   float* stg = reinterpret_cast<float*>(lds);
-  auto pass = [&](auto view_tag, auto half_tag) {
+  auto pass = [&](auto view_tag, auto half_tag, auto ht_tag) {
+    constexpr bool HT = decltype(ht_tag)::value;  // a half tile
     constexpr int V = decltype(view_tag)::value;
     constexpr int h = decltype(half_tag)::value;
     constexpr int kPieces = 128 * 64 / kThreadsBig;  // 16-byte pieces of a half tile per thread
@@ -345,7 +389,9 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
     if constexpr (!late) first_batch();
     if constexpr (V == kViewRow) {
       // Staged [i][j]; 16-byte slot s of row r sits at s ^ stage_swz(r).
-      if (wm == h) {
+      // A full tile's half h is the rows of the waves with wm = h; a half
+      // tile (h = 0 only) has rows 64 wm + 32 i + .., i < FM / 2, in every wave.
+      if (HT || wm == h) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -354,7 +400,8 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
             for (int q = 0; q < 4; ++q)
 #pragma unroll
               for (int u = 0; u < 4; ++u) {
-                const int r = i * 32 + 8 * q + 4 * (lane >> 5) + u;
+                if (HT && i >= FM / 2) continue;
+                const int r = (HT ? wm * 64 : 0) + i * 32 + 8 * q + 4 * (lane >> 5) + u;
                 const int col = wn * 64 + j * 32 + (lane & 31);
                 const int ps = (col >> 2) ^ stage_swz(r);
                 stg[r * 256 + ps * 4 + (col & 3)] = pre * acc[i][j][4 * q + u];
@@ -362,7 +409,9 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
       }
     } else {
       // Staged [j][i] (four consecutive i per lane are one 16-byte slot);
-      // slot s of row r sits at s ^ (r mod 16).
+      // slot s of row r sits at s ^ (r mod 16).  On a half tile only
+      // i < 128 is staged; the rest of each row is past m, where the
+      // epilogue's guards store nothing (the tile is never on its fast path).
       if ((wn >> 1) == h) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -370,8 +419,9 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
           for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+              if (HT && i >= FM / 2) continue;
               const int rc = (wn & 1) * 64 + j * 32 + (lane & 31);
-              const int ci = wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+              const int ci = (HT ? wm * 64 : wm * 128) + i * 32 + 8 * q + 4 * (lane >> 5);
               const int ps = (ci >> 2) ^ (rc & 15);
               f32x4_t v;
               v.x = pre * acc[i][j][4 * q + 0];
@@ -437,13 +487,48 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   };
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
-  if (views & kViewRow) {
-    pass(std::integral_constant<int, kViewRow>{}, H0{});
-    pass(std::integral_constant<int, kViewRow>{}, H1{});
-  }
-  if ((views & kViewCol) && !mirror) {
-    pass(std::integral_constant<int, kViewCol>{}, H0{});
-    pass(std::integral_constant<int, kViewCol>{}, H1{});
+  using Row = std::integral_constant<int, kViewRow>;
+  using Col = std::integral_constant<int, kViewCol>;
+  auto epilogue = [&](auto ht) {
+    if (views & kViewRow) {
+      pass(Row{}, H0{}, ht);
+      if constexpr (!decltype(ht)::value) pass(Row{}, H1{}, ht);
+    }
+    if ((views & kViewCol) && !mirror) {
+      pass(Col{}, H0{}, ht);
+      pass(Col{}, H1{}, ht);
+    }
+  };
+  using Full = std::false_type;
+  using Half = std::true_type;
+  if constexpr (Epi::kAddX) {
+    const int rb = kBigTile + wn * 64 + (lane & 31);
+#pragma unroll
+    for (int p = 0; p < kNS - 1; ++p)
+      if (p < nk) issue(p, p, Full{});
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_loads<2 * kLI>(min(kNS - 2, nk - 1 - kt));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");  // no LDS access moves across the barrier
+      if (kt + kNS - 1 < nk) issue(kt + kNS - 1, stage == 0 ? kNS - 1 : stage - 1, Full{});
+      if ((kt >> 2) == tm && wm == ((kt & 3) >> 1)) {
+        if (kt & 1) add_x(lds + stage * kStage, rb, std::integral_constant<int, 2>{});
+        else add_x(lds + stage * kStage, rb, std::integral_constant<int, 0>{});
+      }
+      multiply(lds + stage * kStage, Full{});
+      stage = stage == kNS - 1 ? 0 : stage + 1;
+    }
+    __syncthreads();  // every wave is done with the stages before they hold the epilogue
+    epilogue(Full{});
+  } else if (half) {
+    main_loop(Half{});
+    __syncthreads();
+    epilogue(Half{});
+  } else {
+    main_loop(Full{});
+    __syncthreads();
+    epilogue(Full{});
   }
 }
 
