@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
     constexpr bool HT = decltype(ht_tag)::value;  // a half tile
     constexpr int V = decltype(view_tag)::value;
     constexpr int h = decltype(half_tag)::value;
-    constexpr int kPieces = 128 * 64 / kThreadsBig;  // 16-byte pieces of a half tile per thread
+    constexpr int kPieces = 128 * 64 / kThreadsBig;  // 16-byte pieces of one pass (128 rows) per thread
     // In the second half every wave has staged its accumulators before the
     // side inputs are loaded, so their registers can hold a larger batch
     // (Epi::kBatchLast) of those loads; the first half loads its first batch
@@ -360,9 +360,9 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
     constexpr int NB = kB < kPieces ? kB : kPieces;
     const int row0 = (V == kViewRow ? tm : tn) * kBigTile + h * 128;
     const int col0 = (V == kViewRow ? tn : tm) * kBigTile;
-    // Epi::kFastPath: where this half tile lies wholly inside the side
+    // Epi::kFastPath: where this pass's 128 rows lie wholly inside the side
     // input's storage (uniform over the workgroup), the loads and stores run
-    // in a copy of the loop without per-lane guards, chosen once per half:
+    // in a copy of the loop without per-lane guards, chosen once per pass:
     // guards around each load make the compiler wait for it at once, so a
     // batch's loads would not be in flight together.
     using Guarded = std::false_type;
@@ -738,8 +738,8 @@ struct FinalPhase {
   };
   static constexpr int kBatch = 4, kBatchLast = 16;
   // The unguarded path: a float32 W whose rows are whole 16-byte groups, and
-  // a half tile that lies wholly inside the slice (every tile of a slice
-  // whose sides are multiples of 256).
+  // an epilogue pass (128 rows of a tile) that lies wholly inside the slice
+  // (every tile of a slice whose sides are multiples of 256).
   static constexpr bool kFastPath = true;
   static __device__ bool fast(const Ctx& x, int, int row0, int col0) {
     return x.vec && x.pdtype == 0 && row0 + 128 <= x.rows && col0 + kBigTile <= x.len;
