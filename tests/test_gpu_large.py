@@ -62,9 +62,43 @@ def test_mid_shapes(shape):
 @pytest.mark.parametrize("shape", [(33, 500), (40, 400), (64, 1024), (1024, 64), (100, 300), (2, 120, 777)])
 def test_large_tiles_down_to_m_33(shape):
     """large_min_m = 33 puts every streamed bf16 slice on the large tiles:
-    one tile row holding 33 to 128 rows of the slice, so the waves of rows
-    128 .. 255 of every symmetric tile skip their products."""
+    one tile row holding 33 to 128 rows of the slice, so every tile of the
+    Gram and polynomial is a half tile (its first 128 rows only), on the
+    diagonal, where the waves whose columns lie past m skip their products."""
     _check([shape], plan_kw=dict(large_min_m=33))
+
+
+@pytest.mark.parametrize("shape", [(257, 600), (600, 383), (640, 900), (900, 640), (385, 700), (2, 641, 700),
+                                   (511, 1030), (2, 384, 520)])
+def test_half_tile_boundaries(shape):
+    """The symmetric phases' last tile row is a half tile when it holds at
+    most 128 rows inside m (m mod 256 = 1, 127 and 128 here, stored either
+    way round), and a full tile below the diagonal when it holds more
+    (m mod 256 = 129 and 255).  Every 64 x 64 block of the update is
+    checked, so a wrong or missing row of a half tile, or of its mirror
+    writes, fails."""
+    _check([shape])
+
+
+def test_half_tiles_bf16_weights_and_steps():
+    """Half tiles in a mixed plan over three steps, with nonzero W and M and
+    a bf16 W next to float32 ones.  The bf16 W is rounded once per step
+    (unit roundoff 2^-8 each time), the oracle's W not at all."""
+    import oracle
+    shapes = [(384, 700), (700, 384), (300, 520)]
+    params, grads, moms = make_inputs(shapes, "bf16", 57, 1e-3, ["f32", "bf16", "f32"], 0.02, 1e-3)
+    w_gpu, _ = gpu_step(params, grads, moms, mode="bf16", lr=0.02, beta=0.95, ns_steps=5, coeffs=Q, steps=3)
+    w_ref, _, _ = oracle_step(params, grads, moms, lr=0.02, beta=0.95, ns_steps=5, coeffs=Q, steps=3)
+    for i in range(len(shapes)):
+        if i == 1:
+            w0 = oracle.decode(params[i])
+            err = np.linalg.norm(oracle.decode(w_gpu[i]) - w_ref[i])
+            bound = 3 * 2.0 ** -8 * np.linalg.norm(w_ref[i]) + BAR * np.linalg.norm(w_ref[i] - w0)
+            assert err <= bound, (shapes[i], err, bound)
+        else:
+            w0 = params[i].astype(np.float64)
+            errs = slice_rel_errors(w_gpu[i].astype(np.float64) - w0, w_ref[i] - w0, BAR)
+            assert max(errs) <= BAR, (shapes[i], max(errs))
 
 
 def test_large_fusion_is_bitexact():
