@@ -211,6 +211,23 @@ def test_resume_from_host_copies_is_bitexact(mode):
         assert np.array_equal(w3[i], w3b[i]) and np.array_equal(m3[i], m3b[i]), f"parameter {i}"
 
 
+def test_skinny_long_rows():
+    """Skinny slices of about 2M columns (8192 chunks of 256 per slice, one
+    stored transposed): the polynomial kernel sums 8192 Gram partials per
+    slice over many batches of loads, and the launches index tens of
+    thousands of chunks.  Both modes against one oracle run."""
+    shapes = [(24, (1 << 21) + 5), ((1 << 21) + 3, 20)]
+    params, grads, moms = make_inputs(shapes, "bf16", 91, 1e-3, None, 0.0, 1e-3)
+    w_ref, m_ref, o_ref = oracle_step(params, grads, moms, lr=1.0, beta=0.95, ns_steps=5, coeffs=Q)
+    for mode in ("bf16", "fp32"):
+        w_gpu, m_gpu = gpu_step(params, grads, moms, mode=mode, lr=1.0, beta=0.95, ns_steps=5, coeffs=Q)
+        for i in range(len(shapes)):
+            errs = update_errors(w_gpu[i], params[i], 1.0, o_ref[i], TOL[mode])
+            print(f"{shapes[i]} {mode}: worst {max(errs):.3e}", flush=True)
+            assert max(errs) <= TOL[mode], (shapes[i], mode, max(errs))
+            assert max_ulp_diff(m_gpu[i], m_ref[i]) <= 1, (shapes[i], mode)
+
+
 @pytest.mark.parametrize("mode", ["bf16", "fp32"])
 def test_several_skinny_shapes_share_the_launches(mode):
     """Skinny shapes with different m and n (and ragged chunks) run in one
