@@ -166,8 +166,8 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   // It takes about half a tile's time, in the same launch as the full
   // tiles, which fills the last wave of tiles better.  (The apply and final
   // phases have none: on launches that fill the chip their half tiles were
-  // no faster, and their presence made the compiler's code for the full
-  // tiles' X term below 1% slower.)
+  // no faster, and with them in the kernel the compiler's code for the full
+  // tiles' X term, further down, ran up to 1% slower.)
   const bool half = Epi::kLower && bb.m - (int64_t)tm * kBigTile <= 128;
   // The symmetric products are zero in their columns past m as well: on a
   // half tile on the diagonal, a wave whose 64 columns all lie past m skips
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   const char* B = op.b + (int64_t)tn * kBigTile * op.ldb * 2;
   const int nk = (int)(op.K / kBK);
 
-  // Load instruction u of wave w fills rows kRPI (w + 4 u) .. + kRPI - 1 of an
+  // Load instruction u of wave w fills rows kRPI (w + 8 u) .. + kRPI - 1 of an
   // operand tile; lane l lands in slot l mod kCPR of row l / kCPR and fetches
   // the chunk that belongs there.
   uint32_t oa[kLI], ob[kLI];
@@ -297,21 +297,19 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   // Iteration kt: wait for this wave's loads of slice kt; one barrier then
   // says that every wave's part of slice kt is in LDS and that every wave
   // has finished reading slice kt - 1, whose stage is refilled with slice
-  // kt + NS - 1 before slice kt is multiplied.  (One
-  // loop: peeling the last slices off made the compiler spill the
-  // accumulators around the epilogue.)
-  // The symmetric products run this loop, one copy for full and one for
-  // half tiles, chosen once per workgroup.  The apply phases run the same
-  // loop with the X term, written out in the kernel body below: inside a
-  // lambda, which is optimized before it is inlined, the X term's two calls
-  // were merged into one through a pointer, and the accumulators stayed on
-  // the stack.
+  // kt + NS - 1 before slice kt is multiplied.  (One loop: peeling the last
+  // slices off made the compiler spill the accumulators around the
+  // epilogue.)  The symmetric products run this loop, one copy for full and
+  // one for half tiles, chosen once per workgroup.  The apply phases run the
+  // same loop with the X term, written out in the kernel body below: inside
+  // a lambda, which is optimized before it is inlined, the X term's two
+  // calls were merged into one through a pointer, and the accumulators
+  // stayed on the stack.
   auto main_loop = [&](auto half_tag) {
     constexpr bool H = decltype(half_tag)::value;
     constexpr int NS = H ? kNSHalf : kNS;
     constexpr int kStg = H ? kStageHalf : kStage;
     constexpr int L = (H ? kLI / 2 : kLI) + kLI;  // load instructions per slice and wave
-    const int rb = (H ? 128 : kBigTile) + wn * 64 + (lane & 31);
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p)
       if (p < nk) issue(p, p, half_tag);
@@ -331,11 +329,12 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   };
 
   // ---- epilogue.  Accumulator layout of a 32x32 block: lane l, register r ->
-  // row 8 (r / 4) + 4 (l / 32) + r mod 4, column l mod 32.  Half of the tile
-  // (128 x 256 float32 = 128 KB) is staged at a time; each half is then
-  // written as whole rows of 16-byte pieces.  What an epilogue reads besides
-  // the product (old X, W, A, the diagonal) is loaded kBatch pieces at a
-  // time, the first batch before the staging so its latency is hidden.
+  // row 8 (r / 4) + 4 (l / 32) + r mod 4, column l mod 32.  One pass stages
+  // 128 rows of the tile (128 x 256 float32 = 128 KB) and writes them as
+  // whole rows of 16-byte pieces: two passes for a full tile, one for a half
+  // tile.  What an epilogue reads besides the product (W, A, the diagonal)
+  // is loaded kBatch pieces at a time, the first batch before the staging
+  // so its latency is hidden.
   // A phase whose transposed output holds the same values as its own
   // (Epi::kMirror: the symmetric products, and X' next to X'^T) computes
   // them once, in the row view: each thread puts its results back into the
