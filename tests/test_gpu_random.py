@@ -25,7 +25,7 @@ from gpu_helpers import TOL, gpu_step, make_inputs, max_ulp_diff, oracle_step, s
 
 pytestmark = pytest.mark.gpu
 
-CASES = 48
+CASES = 160
 CUBIC = (1.5, -0.5, 0.0)
 
 
