@@ -329,7 +329,10 @@ def test_large_tile_tables_cover_every_tile_once():
     """Each phase's table lists every output tile of every large slice exactly
     once (upper triangle for X X^T and E E), pads only with the empty marker,
     has a length that is a multiple of 8, and its 8 XCD stretches carry work
-    within one block of each other."""
+    within one block of each other.  Work is counted as the kernel spends it:
+    the contraction length per tile, half of it for the symmetric phases'
+    half tiles (the last tile row of a slice with at most 128 rows inside m;
+    on such a slice the kernel takes the table's column index as the row)."""
     shapes = [(4096, 12288, 2), (4096, 4096, 3), (16384, 4096, 1), (1408, 2048, 5), (600, 700, 1)]
     buckets, tables = _tables(shapes)
     assert [b[:2] for b in buckets] == [(4096, 12288), (4096, 4096), (4096, 16384), (1408, 2048), (600, 700)]
@@ -353,16 +356,23 @@ def test_large_tile_tables_cover_every_tile_once():
                         if ph == 2 or j >= i:
                             want.add((bi, z, i, j))
         assert seen == want
-        # work per XCD stretch (contraction length per tile)
+        # work per XCD stretch
+        def half(bucket, j):
+            m, n, mp, np_, cnt = bucket
+            return ph != 2 and j == mp // 256 - 1 and m - (mp - 256) <= 128
         L = len(tab) // 8
         work = []
         for x in range(8):
             w = 0
             for bz, mn in tab[x * L:(x + 1) * L]:
                 if bz != no_tile:
-                    m, n, mp, np_, cnt = buckets[bz >> 24]
-                    w += np_ if ph == 0 else mp
+                    bk = buckets[bz >> 24]
+                    k = bk[3] if ph == 0 else bk[2]
+                    w += k // 2 if half(bk, mn >> 16) else k
             work.append(w)
+        if ph != 2:  # [1408,2048]: the 6 tiles of the last tile row of each of its 5 slices are half tiles
+            n_half = sum(1 for bz, mn in tab if bz != no_tile and half(buckets[bz >> 24], mn >> 16))
+            assert n_half == 5 * 6 + 1 * 3  # and the 3 of [600,700]'s last row
         biggest_block = 32 * max((b[3] if ph == 0 else b[2]) for b in buckets)
         assert max(work) - min(work) <= biggest_block
 
