@@ -329,7 +329,7 @@ std::vector<BigTile> big_table(const Plan& p, int phase) {
   constexpr int kXcd = 8;
   struct Block {
     int64_t k;     // contraction length of every tile in the block
-    int64_t work;  // k per full tile, k / 2 per half tile
+    int64_t work;  // k per full tile, k / 2 per half tile (measured: about 0.6 k)
     std::vector<BigTile> tiles;
   };
   std::vector<Block> blocks;

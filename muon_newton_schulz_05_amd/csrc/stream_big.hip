@@ -163,7 +163,8 @@ __global__ __launch_bounds__(kThreadsBig) void k_gemm_big(BigArgs g) {
   // Such a tile computes its first 128 rows only: the eight waves take
   // 64 x 64 each (2 x 2 blocks) instead of 128 x 64 (4 x 2), only those 128
   // rows of the first operand are loaded, and the epilogue writes one half.
-  // It takes about half a tile's time, in the same launch as the full
+  // It takes about 60% of a full tile's time (fewer products per k-slice
+  // hide less of each slice's fixed cost), in the same launch as the full
   // tiles, which fills the last wave of tiles better.  (The apply and final
   // phases have none: on launches that fill the chip their half tiles were
   // no faster, and with them in the kernel the compiler's code for the full
